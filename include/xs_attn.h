@@ -1,0 +1,78 @@
+/*
+ * xs_attn.h -- C ABI of the fused attention + destination-ordered epilogue
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (X-Stage paper, "X-Stage: An Overlooked Pipeline Stage for
+ * Communication-Computation Overlap in DiT Inference": catalyzex.com abstract;
+ * gist.science explainer, section "Zentrale Beitraege", item
+ * "FlashAttention-A2A (Piggybacking)"): one GPU's share of Ulysses
+ * sequence-parallel attention in a Diffusion Transformer -- the full sequence
+ * S over H_local heads -- computed as a non-causal FlashAttention forward pass
+ * whose output-tile owner writes each finished O tile straight into the buffer
+ * the post-attention All-to-All would deliver, with no dedicated communication
+ * wavefront.  Here that buffer lives in the calling GPU's own HBM.
+ *
+ *   O[b,s,h,:] = softmax_j(scale * q[b,s,h,:] . k[b,j,h,:]) @ v[b,:,h,:]
+ *   out_packed[p][b][s'][h][d] = O[b][p*T + s'][h][d],   T = S / P
+ *   (flat offset (((p*B + b)*T + s')*H_local + h)*D + d)
+ *
+ * Conventions shared by every entry point:
+ *  - q, k, v are device pointers to contiguous [B][S][H_local][D] tensors.
+ *  - out_packed is a device pointer to a contiguous [P][B][S/P][H_local][D]
+ *    bf16 tensor; it must not overlap q, k or v.
+ *  - All device pointers must be 16-byte aligned.
+ *  - The caller owns every buffer.  The library allocates nothing, keeps no
+ *    pointer after returning, holds no global state and is re-entrant.
+ *  - `stream` is a hipStream_t passed as void*; NULL selects the default
+ *    stream.  Calls are asynchronous: they return once the kernel is enqueued
+ *    and do not synchronise; a fault inside the kernel surfaces at the
+ *    caller's next synchronisation on that stream.
+ *  - Arguments are validated before any HIP call, so validation errors are
+ *    reported (and testable) without a GPU.  No entry point prints, throws or
+ *    aborts.
+ */
+#ifndef XS_ATTN_H
+#define XS_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define XS_OK 0
+#define XS_ERR_NULL (-1)        /* a required pointer is NULL */
+#define XS_ERR_SHAPE (-2)       /* B, S, H_local, D or P < 1, or S % P != 0 */
+#define XS_ERR_UNSUPPORTED (-3) /* D not in {64, 128}, scale or a descale not finite, size overflow */
+#define XS_ERR_ALIGN (-4)       /* a pointer is not 16-byte aligned */
+#define XS_ERR_LAUNCH (-5)      /* the HIP launch reported an error */
+#define XS_ERR_OVERLAP (-6)     /* out_packed overlaps q, k or v */
+
+/* Attention forward over bf16 inputs with the destination-ordered epilogue.
+ *   q, k, v     bf16 [B][S][H_local][D], device memory (read only)
+ *   out_packed  bf16 [P][B][S/P][H_local][D], device memory (written fully)
+ *   scale       fp32 softmax scale applied to the fp32 dot products
+ *               (1/sqrt(D) for standard attention); any finite value.
+ * Accumulation is fp32; the probabilities enter the second contraction as
+ * bf16; the output is rounded to bf16 (round to nearest even). */
+int xs_attn_fwd(const void *q, const void *k, const void *v, void *out_packed, int B, int S,
+                int H_local, int D, int P, float scale, void *stream);
+
+/* The same operation over OCP fp8 e4m3 (e4m3fn) inputs with per-tensor fp32
+ * descales: the value of element x is x8 * x_descale.  Accumulation is fp32
+ * and the output is bf16 [P][B][S/P][H_local][D] as above.  Descales must be
+ * finite. */
+int xs_attn_fwd_fp8(const void *q8, const void *k8, const void *v8, float q_descale,
+                    float k_descale, float v_descale, void *out_packed, int B, int S, int H_local,
+                    int D, int P, float scale, void *stream);
+
+/* Static, never-NULL description of a status code. */
+const char *xs_attn_strerror(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int xs_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XS_ATTN_H */

@@ -1,0 +1,245 @@
+/*
+ * xs_oracle.c -- CPU fp64 oracle for the attention forward pass of one GPU's
+ * share of Ulysses sequence-parallel attention, with the output relaid into a
+ * P-way destination-ordered buffer.
+ *
+ * THIS IS TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only the test
+ * suite, the smoke check and the benchmark's CPU-baseline leg may load it.  It
+ * shares no code, header, table or helper with the HIP library: it is written
+ * from the definition of attention and of the all-to-all chunk layout alone.
+ *
+ * What it follows (the X-Stage paper, "X-Stage: An Overlooked Pipeline Stage
+ * for Communication-Computation Overlap in DiT Inference"):
+ *  - catalyzex.com abstract, and the gist.science explainer, section
+ *    "Zentrale Beitraege", item "FlashAttention-A2A (Piggybacking)": Ulysses
+ *    sequence-parallel attention whose post-attention All-to-All is fused into
+ *    FlashAttention at tile granularity; the owner of an output tile stores it
+ *    to its destination.  FlashAttention computes softmax(scale * Q K^T) V
+ *    exactly (up to rounding), so the oracle is that definition written out:
+ *    for every batch b, head h and query row i
+ *        s_j  = scale * sum_d q[b,i,h,d] * k[b,j,h,d]
+ *        m    = max_j s_j                      (exact row max, first pass)
+ *        w_j  = exp(s_j - m),  l = sum_j w_j   (second pass)
+ *        O[b,i,h,:] = (sum_j w_j * v[b,j,h,:]) / l
+ *    There is no online rescaling and no blocking: one query row at a time.
+ *  - The destination-ordered buffer is the layout an All-to-All over P ranks
+ *    delivers when the sequence is cut into P contiguous slices of T = S/P
+ *    rows: out_packed[p][b][s'][h][d] = O[b][p*T + s'][h][d].
+ *
+ * Inputs are stored as fp64, bf16 (bit patterns) or OCP fp8 e4m3fn codes with
+ * a per-tensor fp64 descale; every element is decoded exactly to fp64 before
+ * any arithmetic.  All arithmetic is fp64 with libm exp().  Build without
+ * -ffast-math.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define XSO_F64 0
+#define XSO_BF16 1
+#define XSO_E4M3 2
+
+/* bf16 is the top half of an IEEE binary32: widen the 16 bits into the high
+ * half of a float, which is exact, then widen to double. */
+double xs_oracle_decode_bf16(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* OCP 8-bit float E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with bias 7,
+ * 3 mantissa bits; exponent field 0 encodes subnormals m/8 * 2^-6; there are no
+ * infinities and the codes S.1111.111 are NaN; the largest finite is 448. */
+double xs_oracle_decode_e4m3(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int e = (code >> 3) & 0xF;
+  int m = code & 0x7;
+  double mag;
+  if (e == 0xF && m == 0x7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m / 8.0, -6);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+typedef struct {
+  int dtype;
+  const void *q, *k, *v;
+  double q_descale, k_descale, v_descale;
+  int64_t B, S, H, D;
+  double scale;
+} xso_problem;
+
+/* Element x[b][s][h][d] of a [B][S][H][D] contiguous tensor, decoded to fp64. */
+static double load(const xso_problem *pr, const void *base, double descale, int64_t b, int64_t s,
+                   int64_t h, int64_t d) {
+  int64_t idx = ((b * pr->S + s) * pr->H + h) * pr->D + d;
+  switch (pr->dtype) {
+    case XSO_BF16:
+      return xs_oracle_decode_bf16(((const uint16_t *)base)[idx]);
+    case XSO_E4M3:
+      return xs_oracle_decode_e4m3(((const uint8_t *)base)[idx]) * descale;
+    default:
+      return ((const double *)base)[idx];
+  }
+}
+
+/* One output row O[b,i,h,:] by the two-pass definition above.  `s` is a
+ * scratch row of S doubles and `acc` one of D doubles. */
+static void attention_row(const xso_problem *pr, int64_t b, int64_t i, int64_t h, double *s,
+                          double *acc, double *out_row) {
+  const int64_t S = pr->S, D = pr->D;
+  double m = -INFINITY;
+  for (int64_t j = 0; j < S; ++j) {
+    double dot = 0.0;
+    for (int64_t d = 0; d < D; ++d)
+      dot += load(pr, pr->q, pr->q_descale, b, i, h, d) * load(pr, pr->k, pr->k_descale, b, j, h, d);
+    s[j] = pr->scale * dot;
+    if (s[j] > m) m = s[j];
+  }
+  double l = 0.0;
+  for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+  for (int64_t j = 0; j < S; ++j) {
+    double w = exp(s[j] - m);
+    l += w;
+    for (int64_t d = 0; d < D; ++d) acc[d] += w * load(pr, pr->v, pr->v_descale, b, j, h, d);
+  }
+  for (int64_t d = 0; d < D; ++d) out_row[d] = acc[d] / l;
+}
+
+/* Flat offset of element (b, s, h, d) of O inside the destination-ordered
+ * buffer [P][B][T][H][D], T = S/P, slice p = floor(s/T) holding rows
+ * p*T .. p*T+T-1 of every batch. */
+int64_t xs_oracle_packed_offset(int64_t B, int64_t S, int64_t H, int64_t D, int64_t P, int64_t b,
+                                int64_t s, int64_t h, int64_t d) {
+  int64_t T = S / P;
+  int64_t p = s / T;
+  int64_t sp = s - p * T;
+  return (((p * B + b) * T + sp) * H + h) * D + d;
+}
+
+/* Relayout of a [B][S][H][D] fp64 tensor into [P][B][S/P][H][D].
+ * Returns 0, or -2 when a size is < 1 or S is not a multiple of P. */
+int xs_oracle_pack(const double *o, int64_t B, int64_t S, int64_t H, int64_t D, int64_t P,
+                   double *out_packed) {
+  if (B < 1 || S < 1 || H < 1 || D < 1 || P < 1 || S % P != 0) return -2;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t s = 0; s < S; ++s)
+      for (int64_t h = 0; h < H; ++h)
+        for (int64_t d = 0; d < D; ++d)
+          out_packed[xs_oracle_packed_offset(B, S, H, D, P, b, s, h, d)] =
+              o[((b * S + s) * H + h) * D + d];
+  return 0;
+}
+
+typedef struct {
+  const xso_problem *pr;
+  const int64_t *rows; /* nrows triples (b, s, h) */
+  int64_t nrows;
+  double *out;         /* row r -> out + r*D, unless packed */
+  int64_t P;           /* > 0: write into the packed buffer instead */
+  int tid, nthreads;
+  int status;
+} xso_job;
+
+static void *worker(void *arg) {
+  xso_job *job = (xso_job *)arg;
+  const xso_problem *pr = job->pr;
+  double *s = (double *)malloc((size_t)pr->S * sizeof(double));
+  double *acc = (double *)malloc((size_t)pr->D * sizeof(double));
+  double *row = (double *)malloc((size_t)pr->D * sizeof(double));
+  if (!s || !acc || !row) {
+    job->status = -1;
+    free(s), free(acc), free(row);
+    return NULL;
+  }
+  for (int64_t r = job->tid; r < job->nrows; r += job->nthreads) {
+    int64_t b = job->rows[3 * r], i = job->rows[3 * r + 1], h = job->rows[3 * r + 2];
+    attention_row(pr, b, i, h, s, acc, row);
+    for (int64_t d = 0; d < pr->D; ++d) {
+      if (job->P > 0)
+        job->out[xs_oracle_packed_offset(pr->B, pr->S, pr->H, pr->D, job->P, b, i, h, d)] = row[d];
+      else
+        job->out[r * pr->D + d] = row[d];
+    }
+  }
+  free(s), free(acc), free(row);
+  job->status = 0;
+  return NULL;
+}
+
+static int run_rows(const xso_problem *pr, const int64_t *rows, int64_t nrows, double *out,
+                    int64_t P, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  pthread_t th[256];
+  int created[256];
+  xso_job jobs[256];
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t] = (xso_job){pr, rows, nrows, out, P, t, nthreads, -1};
+    created[t] = pthread_create(&th[t], NULL, worker, &jobs[t]) == 0;
+    if (!created[t]) worker(&jobs[t]); /* run this share on the calling thread */
+  }
+  int status = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    if (created[t]) pthread_join(th[t], NULL);
+    if (jobs[t].status != 0) status = -1;
+  }
+  return status;
+}
+
+static int check(int dtype, const void *q, const void *k, const void *v, int64_t B, int64_t S,
+                 int64_t H, int64_t D) {
+  if (!q || !k || !v) return -1;
+  if (B < 1 || S < 1 || H < 1 || D < 1) return -2;
+  if (dtype < XSO_F64 || dtype > XSO_E4M3) return -3;
+  return 0;
+}
+
+/* Attention rows O[b,s,h,:] for nrows (b, s, h) triples; out is nrows x D.
+ * Returns 0, -1 (null pointer / allocation), -2 (shape), -3 (dtype). */
+int xs_oracle_attention_rows(int dtype, const void *q, const void *k, const void *v,
+                             double q_descale, double k_descale, double v_descale, int64_t B,
+                             int64_t S, int64_t H, int64_t D, double scale, const int64_t *rows,
+                             int64_t nrows, double *out, int nthreads) {
+  int rc = check(dtype, q, k, v, B, S, H, D);
+  if (rc) return rc;
+  if (!rows || !out) return -1;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows[3 * r] < 0 || rows[3 * r] >= B || rows[3 * r + 1] < 0 || rows[3 * r + 1] >= S ||
+        rows[3 * r + 2] < 0 || rows[3 * r + 2] >= H)
+      return -2;
+  xso_problem pr = {dtype, q, k, v, q_descale, k_descale, v_descale, B, S, H, D, scale};
+  return run_rows(&pr, rows, nrows, out, 0, nthreads);
+}
+
+/* The whole hot path: attention over every (b, s, h) row, written straight
+ * into the destination-ordered buffer [P][B][S/P][H][D] (fp64).
+ * Returns 0, -1, -2 (also S % P != 0), -3. */
+int xs_oracle_attention_packed(int dtype, const void *q, const void *k, const void *v,
+                               double q_descale, double k_descale, double v_descale, int64_t B,
+                               int64_t S, int64_t H, int64_t D, int64_t P, double scale,
+                               double *out_packed, int nthreads) {
+  int rc = check(dtype, q, k, v, B, S, H, D);
+  if (rc) return rc;
+  if (!out_packed) return -1;
+  if (P < 1 || S % P != 0) return -2;
+  int64_t nrows = B * S * H;
+  int64_t *rows = (int64_t *)malloc((size_t)nrows * 3 * sizeof(int64_t));
+  if (!rows) return -1;
+  int64_t r = 0;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t s = 0; s < S; ++s)
+      for (int64_t h = 0; h < H; ++h) {
+        rows[3 * r] = b, rows[3 * r + 1] = s, rows[3 * r + 2] = h;
+        ++r;
+      }
+  xso_problem pr = {dtype, q, k, v, q_descale, k_descale, v_descale, B, S, H, D, scale};
+  rc = run_rows(&pr, rows, nrows, out_packed, P, nthreads);
+  free(rows);
+  return rc;
+}
