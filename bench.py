@@ -1,0 +1,162 @@
+"""Benchmark: fused Ulysses-share attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload video|image|long|fp8|tiny]
+
+One step is one call of the whole path -- attention over the full sequence for
+every head of the share plus the destination-ordered epilogue -- on inputs
+already resident in HBM.  Prints one JSON line.  The default workload is the
+S=32768, D=128 video share (B=1, H_local=5, P=8), bf16.
+
+The line carries the roofline of the (single) kernel -- algorithmic flops per
+launch over the mean launch time measured with HIP events on the launch stream
+-- and a CPU baseline: the fp64 oracle timed on a bounded sample of query rows
+of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "attention TFLOP/s (4·B·H·S²·D) + % MFMA peak, S=32768 D=128 bf16"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X published dense MFMA peaks
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="video", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, inp, target_s):
+    """Time the fp64 oracle on a deterministic sample of rows; scale to TFLOP/s."""
+    from oracle import oracle
+
+    threads = oracle.default_threads()
+    per_row = 4.0 * w.S * w.D  # algorithmic flops of one query row
+    n = max(threads, 8)
+    rows = workloads.sample_rows(w, n, seed=11)
+    t0 = time.perf_counter()
+    oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, inp["scale"], inp["descales"], threads)
+    dt = time.perf_counter() - t0
+    n = int(min(max(n, n * target_s / max(dt, 1e-6)), w.B * w.S * w.H))
+    n = max(threads, (n // threads) * threads)
+    rows = workloads.sample_rows(w, n, seed=12)
+    t0 = time.perf_counter()
+    oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, inp["scale"], inp["descales"], threads)
+    dt = time.perf_counter() - t0
+    return {
+        "value": per_row * len(rows) / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(rows)} of {w.B * w.S * w.H} query rows of the {w.name} workload "
+                  f"(all {w.S} keys each), {dt:.1f} s wall, fp64",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no cross-GPU step in this build).", file=sys.stderr)
+        sys.exit(2)
+    import sequence_attention_amd as xs
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = workloads.make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in "qkv")
+    out = torch.empty((w.P, w.B, w.S // w.P, w.H, w.D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        if w.dtype == "fp8":
+            xs.fwd_fp8(q, k, v, inp["descales"], w.P, inp["scale"], out=out, stream=stream)
+        else:
+            xs.fwd(q, k, v, w.P, inp["scale"], out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back launches, each bracketed by events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    ms_per_step = total_ms / args.steps
+
+    flops = w.flops
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = flops / (float(launch_ms.mean()) * 1e-3) / 1e12
+
+    check = None
+    if not args.no_check:
+        from oracle import oracle
+        rows = workloads.sample_rows(w, 32)
+        ref = oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, inp["scale"], inp["descales"])
+        idx = torch.as_tensor(rows, device=dev)
+        got = xs.unpack(out, w.S)[idx[:, 0], idx[:, 1], idx[:, 2]].double().cpu().numpy()
+        check = {"rows": len(rows), "max_abs": float(np.abs(got - ref).max()),
+                 "rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref))}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0, sigma^2) inputs, shapes of the workload)",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "H_local": w.H, "D": w.D, "P": w.P,
+                   "causal": False},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "launch_ms": {"mean": round(float(launch_ms.mean()), 4), "min": round(float(launch_ms.min()), 4),
+                      "median": round(float(np.median(launch_ms)), 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_fp8_kernel",
+                     "flops_per_launch": flops},
+        "check": check,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,111 @@
+"""Fused Ulysses-share attention forward for MI355X (gfx950).
+
+Thin Python binding over libxs_attn.so (include/xs_attn.h).  Every step of the
+computation runs in the library's HIP kernels; this module only checks tensor
+metadata, allocates the output with torch and passes pointers and the current
+HIP stream.  There is no CPU or PyTorch fallback: if the library is missing,
+the calls raise.
+
+    out_packed = fwd(q, k, v, P)            # bf16 q/k/v [B][S][H][D] on the GPU
+    out_packed = fwd_fp8(q8, k8, v8, descales, P)
+    o = unpack(out_packed, S)               # back to [B][S][H][D] (a torch view)
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from ._lib import XsAttnError, check, declared_functions, lib, strerror
+
+__all__ = ["fwd", "fwd_fp8", "unpack", "xs_attn_fwd", "xs_attn_fwd_fp8", "xs_attn_strerror",
+           "xs_attn_version", "XsAttnError", "default_scale"]
+
+
+def default_scale(D: int) -> float:
+    """float32(1/sqrt(D))."""
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+def _stream_ptr(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_inputs(q, k, v, dtype):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a GPU tensor")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B][S][H][D] tensor")
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError("q, k, v must share shape and device")
+
+
+def _out(q, P, out):
+    B, S, H, D = q.shape
+    if S % P:
+        raise ValueError(f"S={S} is not a multiple of P={P}")
+    shape = (P, B, S // P, H, D)
+    if out is None:
+        return torch.empty(shape, dtype=torch.bfloat16, device=q.device)
+    if out.shape != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bf16 tensor of shape {shape}")
+    return out
+
+
+def xs_attn_fwd(q, k, v, out_packed, B, S, H_local, D, P, scale, stream) -> int:
+    """Raw C-ABI call: pointers (ints or tensors), sizes, scale, stream handle. Returns the status."""
+    ptr = lambda x: x.data_ptr() if isinstance(x, torch.Tensor) else x
+    return lib().xs_attn_fwd(ptr(q), ptr(k), ptr(v), ptr(out_packed), B, S, H_local, D, P,
+                             float(scale), stream)
+
+
+def xs_attn_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, out_packed, B, S, H_local, D, P,
+                    scale, stream) -> int:
+    ptr = lambda x: x.data_ptr() if isinstance(x, torch.Tensor) else x
+    return lib().xs_attn_fwd_fp8(ptr(q8), ptr(k8), ptr(v8), float(q_descale), float(k_descale),
+                                 float(v_descale), ptr(out_packed), B, S, H_local, D, P,
+                                 float(scale), stream)
+
+
+def xs_attn_strerror(status: int) -> str:
+    return strerror(status)
+
+
+def xs_attn_version() -> int:
+    return int(lib().xs_attn_version())
+
+
+def fwd(q, k, v, P: int, scale: float | None = None, out=None, stream=None) -> torch.Tensor:
+    """Attention over bf16 [B][S][H][D] inputs; returns bf16 out_packed [P][B][S/P][H][D]."""
+    _check_inputs(q, k, v, torch.bfloat16)
+    B, S, H, D = q.shape
+    out = _out(q, P, out)
+    scale = default_scale(D) if scale is None else float(scale)
+    check(xs_attn_fwd(q, k, v, out, B, S, H, D, P, scale, _stream_ptr(q, stream)))
+    return out
+
+
+def fwd_fp8(q8, k8, v8, descales, P: int, scale: float | None = None, out=None,
+            stream=None) -> torch.Tensor:
+    """Attention over e4m3 [B][S][H][D] inputs with per-tensor descales (x = x8 * d)."""
+    _check_inputs(q8, k8, v8, torch.float8_e4m3fn)
+    B, S, H, D = q8.shape
+    out = _out(q8, P, out)
+    scale = default_scale(D) if scale is None else float(scale)
+    dq, dk, dv = (float(d) for d in descales)
+    check(xs_attn_fwd_fp8(q8, k8, v8, dq, dk, dv, out, B, S, H, D, P, scale,
+                          _stream_ptr(q8, stream)))
+    return out
+
+
+def unpack(out_packed: torch.Tensor, S: int) -> torch.Tensor:
+    """View a [P][B][S/P][H][D] buffer as [B][S][H][D] (torch permute/reshape)."""
+    P, B, T, H, D = out_packed.shape
+    assert P * T == S
+    return out_packed.permute(1, 0, 2, 3, 4).reshape(B, S, H, D)

@@ -1,0 +1,24 @@
+// attn_launch.h -- host-side launchers of the attention kernels (internal to
+// the library; the public interface is include/xs_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xs {
+
+struct AttnArgs {
+  const void* q;  // [B][S][H][D], bf16 or e4m3
+  const void* k;
+  const void* v;
+  void* out;      // bf16 [P][B][T][H][D]
+  int B, S, H, D, P, T;
+  float c;        // |scale| * log2(e), times q_descale * k_descale for fp8
+  int neg;        // nonzero when scale < 0: queries are negated as they are loaded
+  float o_scale;  // factor applied with 1/l in the epilogue (v_descale for fp8)
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace xs

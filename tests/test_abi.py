@@ -1,0 +1,104 @@
+"""The C-ABI library without a GPU: it loads, exports every function the header
+declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import math
+import subprocess
+
+import pytest
+
+import sequence_attention_amd as xs
+from sequence_attention_amd import _lib
+
+XS_OK, XS_ERR_NULL, XS_ERR_SHAPE, XS_ERR_UNSUPPORTED, XS_ERR_ALIGN, XS_ERR_LAUNCH, XS_ERR_OVERLAP = (
+    0, -1, -2, -3, -4, -5, -6)
+
+# distinct, 16-byte aligned, far-apart fake device addresses (never dereferenced)
+Q, K, V, O = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def test_library_exports_every_declared_function():
+    names = _lib.declared_functions()
+    assert set(names) == {"xs_attn_fwd", "xs_attn_fwd_fp8", "xs_attn_strerror", "xs_attn_version"}
+    L = _lib.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_version_and_strerror():
+    assert xs.xs_attn_version() == 10000
+    for code in (XS_OK, XS_ERR_NULL, XS_ERR_SHAPE, XS_ERR_UNSUPPORTED, XS_ERR_ALIGN, XS_ERR_LAUNCH,
+                 XS_ERR_OVERLAP, 12345):
+        s = xs.xs_attn_strerror(code)
+        assert isinstance(s, str) and s
+    assert xs.xs_attn_strerror(12345) == "unknown status code"
+
+
+def _fwd(**kw):
+    a = dict(q=Q, k=K, v=V, out=O, B=1, S=256, H=2, D=64, P=2, scale=0.125)
+    a.update(kw)
+    return xs.xs_attn_fwd(a["q"], a["k"], a["v"], a["out"], a["B"], a["S"], a["H"], a["D"], a["P"],
+                          a["scale"], None)
+
+
+def _fwd8(**kw):
+    a = dict(q=Q, k=K, v=V, out=O, B=1, S=256, H=2, D=64, P=2, scale=0.125, dq=0.01, dk=0.01,
+             dv=0.01)
+    a.update(kw)
+    return xs.xs_attn_fwd_fp8(a["q"], a["k"], a["v"], a["dq"], a["dk"], a["dv"], a["out"], a["B"],
+                              a["S"], a["H"], a["D"], a["P"], a["scale"], None)
+
+
+@pytest.mark.parametrize("call", [_fwd, _fwd8])
+def test_null_pointers(call):
+    for name in ("q", "k", "v", "out"):
+        assert call(**{name: 0}) == XS_ERR_NULL
+
+
+@pytest.mark.parametrize("call", [_fwd, _fwd8])
+def test_bad_shapes(call):
+    for kw in (dict(B=0), dict(S=0), dict(H=0), dict(D=0), dict(P=0), dict(B=-1),
+               dict(S=250, P=8), dict(S=7, P=2)):
+        assert call(**kw) == XS_ERR_SHAPE, kw
+
+
+@pytest.mark.parametrize("call", [_fwd, _fwd8])
+def test_unsupported(call):
+    for kw in (dict(D=32), dict(D=96), dict(D=256), dict(scale=math.inf), dict(scale=math.nan)):
+        assert call(**kw) == XS_ERR_UNSUPPORTED, kw
+
+
+def test_unsupported_fp8_descales():
+    for kw in (dict(dq=math.inf), dict(dk=math.nan), dict(dv=-math.inf)):
+        assert _fwd8(**kw) == XS_ERR_UNSUPPORTED, kw
+
+
+@pytest.mark.parametrize("call", [_fwd, _fwd8])
+def test_misaligned(call):
+    for name, base in (("q", Q), ("k", K), ("v", V), ("out", O)):
+        assert call(**{name: base + 8}) == XS_ERR_ALIGN, name
+
+
+@pytest.mark.parametrize("call", [_fwd, _fwd8])
+def test_output_overlapping_an_input(call):
+    assert call(out=Q) == XS_ERR_OVERLAP
+    assert call(out=K + 4096) == XS_ERR_OVERLAP
+    assert call(v=O + 16) == XS_ERR_OVERLAP
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+    t = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        xs.fwd(t, t, t, 2)
+
+
+def test_strerror_returns_static_c_strings():
+    L = _lib.lib()
+    a = L.xs_attn_strerror(XS_ERR_SHAPE)
+    b = L.xs_attn_strerror(XS_ERR_SHAPE)
+    assert a == b and isinstance(a, bytes)
+    assert isinstance(ctypes.c_char_p(a).value, bytes)

