@@ -8,36 +8,52 @@
 // the post-attention All-to-All delivers, then moves on -- there is no separate
 // communication wave and no separate relayout pass.
 //
-// Design (one workgroup = NW waves = BM = NW*32*QT query rows of one (b, h)):
+// Design (one workgroup = 4 waves, one per SIMD; a wave owns QW = 64 query
+// rows as two 32-row sub-tiles; BM = 256 rows of one (b, h) per workgroup):
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    each lane then owns one query column and 16 keys of every 32x32 score
 //    tile, so the row max and row sum are lane-local except for one
-//    permlane32 swap between the two half-waves.
+//    permlane32 swap between the two half-waves.  Each K fragment read from
+//    LDS feeds both sub-tiles, which halves LDS traffic against 32-row waves.
 //  * The transposed probabilities P^T leave the accumulator already in the
 //    B-operand layout of O^T += V^T P^T (the key order inside a k-step is
 //    permuted identically on both operands), so P never goes through LDS.
 //  * K/V tiles of BN = 64 keys are double buffered in LDS and filled with
-//    direct-to-LDS 16-byte loads (no VGPR round trip).  K rows are XOR
+//    direct-to-LDS 16-byte buffer loads (no VGPR round trip).  K rows are XOR
 //    swizzled for conflict-free ds_read_b128 of the A operand; V rows are
 //    swizzled for ds_read_b64_tr_b16, which delivers V^T fragments directly.
-//  * Online softmax in base 2: p = 2^(s*c - m) with c = scale*log2(e) folded
-//    into one FMA per score.  The running max m is only moved (and O, l
-//    rescaled) when a block's max exceeds it by more than 2^8, so p <= 256
-//    and the rescale is a rare wave-uniform branch.
+//  * Software pipeline inside the wave, one barrier per block:
+//      step 1: QK^T of block j+1 (MFMA)  ||  exp/sum/convert of block j (VALU)
+//      step 2: P V of block j (MFMA)     ||  row max of block j+1 (VALU)
+//    so the matrix core and the vector ALU work on different blocks at once.
+//  * Online softmax in base 2: p = 2^(s*c - m), c = scale*log2(e) folded into
+//    one FMA per score.  The running max is moved only when a block's max
+//    exceeds it by more than 2^TAU (p <= 2^TAU), so rescaling O is a rare
+//    wave-uniform branch.  The row sum adds the bf16-rounded p that enter P V.
 //  * Epilogue: O/l rounded to bf16 and stored per query row at its
 //    destination-slice offset (p = s / T, s' = s - p*T).  Tile shapes and the
 //    reduction order never depend on P; only the store address does.
 #include "attn_launch.h"
 #include "device_common.h"
 
+#ifndef XS_QT
+#define XS_QT 1
+#endif
+#ifndef XS_NW
+#define XS_NW 8
+#endif
+#ifndef XS_BN
+#define XS_BN 64
+#endif
+
 namespace xs {
 
-template <int D_, int QT_, int NW_>
+template <int D_, int QT_, int NW_, int BN_>
 struct Bf16Cfg {
   static constexpr int D = D_;
   static constexpr int QT = QT_;         // 32-query sub-tiles per wave
   static constexpr int NW = NW_;         // waves per workgroup
-  static constexpr int BN = 64;          // keys per K/V block
+  static constexpr int BN = BN_;         // keys per K/V block
   static constexpr int QW = 32 * QT;     // queries per wave
   static constexpr int BM = QW * NW;     // queries per workgroup
   static constexpr int CH = D / 8;       // 16-byte chunks per K/V row
@@ -49,8 +65,8 @@ struct Bf16Cfg {
   static constexpr int DT = D / 32;      // 32-row d tiles of O^T
   static constexpr int NT = BN / 32;     // 32-key tiles per block
   static constexpr int THREADS = 64 * NW;
-  static_assert(LOADS % NW == 0 && LOADS >= NW, "tile loads must split evenly over waves");
   static constexpr float TAU = 8.0f;     // lazy-rescale threshold (log2 units)
+  static_assert(LOADS % NW == 0 && LOADS >= NW, "tile loads must split evenly over waves");
 };
 
 // Per-lane byte offsets (relative to the block's first key row) of the
@@ -84,111 +100,57 @@ __device__ __forceinline__ void load_tile(const uint8_t* head_base, uint32_t row
 }
 
 template <class C>
-struct Bf16State {
-  f32x16 o[C::QT][C::DT];
-  float m[C::QT];
-  float l[C::QT];
-  u32x4 qf[C::QT][C::KS];
+struct Scores {
+  f32x16 s[C::NT][C::QT];  // S^T tiles: [32-key tile][query sub-tile]
 };
 
-// One K/V block: scores, online softmax, P V.
-template <class C, bool MASK>
-__device__ __forceinline__ void block_step(Bf16State<C>& st, const uint8_t XS_LDS* sK,
-                                           const uint8_t XS_LDS* sV, int kv0, int S, float c,
-                                           int lane) {
-  constexpr int QT = C::QT, NT = C::NT, KS = C::KS, DT = C::DT, CH = C::CH, ROWB = C::ROWB;
-  const int hi = lane >> 5;
+template <class C>
+struct Bf16State {
+  f32x16 o[C::QT][C::DT];     // O^T accumulators: lane owns query lane%32 of each sub-tile
+  u32x4 qf[C::QT][C::KS];     // Q^T B-operand fragments
+  u32x4 pb[C::QT][C::NT][2];  // bf16 probabilities (P^T B-operand fragments)
+  float m[C::QT];             // running max of s*c (log2 units), shared by both half-waves
+  float l[C::QT];             // lane-local part of the running sum of p
+  float alpha[C::QT];         // pending rescale of O (applied before the next P V)
+  bool rescale;               // wave-uniform: alpha differs from 1 somewhere
+};
 
-  // ---- S^T = K Q^T
-  f32x16 s[NT][QT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) s[nt][qt] = f32x16{};
-  const uint8_t XS_LDS* krow = sK + (lane & 31) * ROWB;
-  const int ksw = lane & (CH - 1);
+// ---- step-1 MFMA work: S^T = K_j Q^T
+template <class C>
+__device__ __forceinline__ void qk_block(Scores<C>& sc, const Bf16State<C>& st,
+                                         const uint8_t XS_LDS* sK, int lane) {
+  constexpr int QT = C::QT, NT = C::NT, KS = C::KS, CH = C::CH, ROWB = C::ROWB;
+  const int ln = opaque(lane);
+  const int hi = ln >> 5;
+  const uint8_t XS_LDS* krow = sK + (ln & 31) * ROWB;
+  const int ksw = ln & (CH - 1);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const u32x4 kf = lds_read_b128(krow + nt * 32 * ROWB + (((2 * ks + hi) ^ ksw) << 4));
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) s[nt][qt] = mfma_bf16(kf, st.qf[qt][ks], s[nt][qt]);
+      for (int qt = 0; qt < QT; ++qt)
+        sc.s[nt][qt] = mfma_bf16(kf, st.qf[qt][ks], ks == 0 ? f32x16{} : sc.s[nt][qt]);
     }
   }
+}
 
-  // keep the phases apart so the V fragments are not all hoisted into registers
-  // next to the live scores
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- online softmax (lane owns query column lane%32 of every tile)
-  if (MASK) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + nt * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-        if (key >= S)
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) s[nt][qt][r] = -INFINITY;
-      }
-  }
-  float mnew[QT];
-  bool need_any = false;
-  bool need[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    float mx = s[0][qt][0];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nt][qt][r]);
-    mx = max_halves(mx) * c;
-    mnew[qt] = fmaxf(st.m[qt], mx);
-    need[qt] = mnew[qt] > st.m[qt] + C::TAU;
-    need_any |= need[qt];
-  }
-  if (__builtin_amdgcn_ballot_w64(need_any)) {
+// ---- step-2 MFMA work: O^T = alpha O^T + V_j^T P^T
+template <class C>
+__device__ __forceinline__ void pv_block(Bf16State<C>& st, const uint8_t XS_LDS* sV, int lane) {
+  constexpr int QT = C::QT, NT = C::NT, DT = C::DT, CH = C::CH, ROWB = C::ROWB;
+  if (st.rescale) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const float alpha = need[qt] ? fast_exp2(st.m[qt] - mnew[qt]) : 1.0f;
-      st.m[qt] = need[qt] ? mnew[qt] : st.m[qt];
-      st.l[qt] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st.o[qt][dt][r] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) st.o[qt][dt] *= st.alpha[qt];
+      st.alpha[qt] = 1.0f;
     }
+    st.rescale = false;
   }
-  u32x4 pb[QT][NT][2];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const float neg_m = -st.m[qt];
-    float lsum = 0.0f;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = fast_exp2(__builtin_fmaf(s[nt][qt][r], c, neg_m));
-        if (MASK) {
-          const int key = kv0 + nt * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-          p[r] = key < S ? p[r] : 0.0f;
-        }
-        lsum += p[r];
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        pb[qt][nt][h] = u32x4{pack_bf16(p[8 * h + 0], p[8 * h + 1]), pack_bf16(p[8 * h + 2], p[8 * h + 3]),
-                              pack_bf16(p[8 * h + 4], p[8 * h + 5]), pack_bf16(p[8 * h + 6], p[8 * h + 7])};
-    }
-    st.l[qt] += lsum;
-  }
-
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- O^T += V^T P^T   (V^T fragments via LDS transpose reads)
-  const int g = lane >> 4, L = lane & 15;
+  const int ln = opaque(lane);
+  const int g = ln >> 4, L = ln & 15;
   const int vrow = 4 * (g >> 1) + (L >> 2);  // row within an 8-row group
   const int vsw = (2 * vrow) & (CH - 1);
   const uint8_t XS_LDS* vbase = sV + vrow * ROWB + 8 * (L & 1);
@@ -204,16 +166,101 @@ __device__ __forceinline__ void block_step(Bf16State<C>& st, const uint8_t XS_LD
         const u32x2 up = lds_read_tr16(p0 + 8 * ROWB);
         const u32x4 vf = u32x4{lo[0], lo[1], up[0], up[1]};
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma_bf16(vf, pb[qt][nt][h], st.o[qt][dt]);
+        for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma_bf16(vf, st.pb[qt][nt][h], st.o[qt][dt]);
       }
+}
+
+// Keys at or past S (only in the last, partial block) get score -inf.
+template <class C>
+__device__ __forceinline__ void mask_tail(Scores<C>& sc, int kv0, int S, int lane) {
+  const int hi = lane >> 5;
+#pragma unroll
+  for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kv0 + nt * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+      if (key >= S)
+#pragma unroll
+        for (int qt = 0; qt < C::QT; ++qt) sc.s[nt][qt][r] = -INFINITY;
+    }
+}
+
+// ---- step-2 VALU work: row max of a scored block, lazy move of the running max
+template <class C>
+__device__ __forceinline__ void softmax_max(Bf16State<C>& st, const Scores<C>& sc, float c) {
+  constexpr int QT = C::QT, NT = C::NT;
+  bool need[QT], any = false;
+  float mnew[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float mx = sc.s[0][qt][0];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc.s[nt][qt][r]);
+    mnew[qt] = max_halves(mx) * c;  // finite: every block holds a valid key
+    need[qt] = mnew[qt] > st.m[qt] + C::TAU;
+    any |= need[qt];
+  }
+  if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float a = need[qt] ? fast_exp2(st.m[qt] - mnew[qt]) : 1.0f;  // 0 when m = -inf
+      st.m[qt] = need[qt] ? mnew[qt] : st.m[qt];
+      st.l[qt] *= a;
+      st.alpha[qt] *= a;
+    }
+    st.rescale = true;
+  }
+}
+
+// ---- step-1 VALU work: p = 2^(s c - m) -> bf16 P^T fragments, row sums
+template <class C>
+__device__ __forceinline__ void softmax_exp(Bf16State<C>& st, const Scores<C>& sc, float c) {
+  constexpr int QT = C::QT, NT = C::NT;
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float neg_m = -st.m[qt];
+    float lsum = st.l[qt];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = fast_exp2(__builtin_fmaf(sc.s[nt][qt][8 * h + 2 * i], c, neg_m));
+          const float p1 = fast_exp2(__builtin_fmaf(sc.s[nt][qt][8 * h + 2 * i + 1], c, neg_m));
+          w[i] = pack_bf16(p0, p1);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]), ones, lsum, false);
+        }
+        st.pb[qt][nt][h] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    st.l[qt] = lsum;
+  }
+}
+
+// Scheduling pattern for one step: N groups of one MFMA, DS LDS reads and V
+// VALU instructions, so the wave issues vector work between matrix ops.
+template <int N, int V, int DS>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
+    if (DS) __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);      // DS read
+    if (V) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);        // VALU
+  }
 }
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int QT = C::QT, KS = C::KS, DT = C::DT, BM = C::BM, BN = C::BN;
-  // [stage][K tile | V tile], two stages
+  // K stage 0 | K stage 1 | V stage 0 | V stage 1
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];
   uint8_t XS_LDS* const lds = (uint8_t XS_LDS*)smem;
+  auto kbuf = [&](int i) { return lds + (i & 1) * C::TILE; };
+  auto vbuf = [&](int i) { return lds + (2 + (i & 1)) * C::TILE; };
 
   const int S = a.S, H = a.H;
   const int mtiles = (S + BM - 1) / BM;
@@ -234,9 +281,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a
   tile_offsets<C, false>(row_stride, wave, lane, koff);
   tile_offsets<C, true>(row_stride, wave, lane, voff);
 
-  // first K/V block in flight while the queries load
-  load_tile<C>(kbase, row_stride, 0, S, lds, koff, wave);
-  load_tile<C>(vbase, row_stride, 0, S, lds + C::TILE, voff, wave);
+  const int nblk = (S + BN - 1) / BN;
+  const int nfull = S / BN;  // blocks with no key past the end of the sequence
+  load_tile<C>(kbase, row_stride, 0, S, kbuf(0), koff, wave);
+  load_tile<C>(vbase, row_stride, 0, S, vbuf(0), voff, wave);
+  if (nblk > 1) load_tile<C>(kbase, row_stride, BN, S, kbuf(1), koff, wave);
 
   Bf16State<C> st;
   const uint32_t qflip = a.neg ? 0x80008000u : 0u;
@@ -252,28 +301,75 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a
     }
     st.m[qt] = -INFINITY;
     st.l[qt] = 0.0f;
+    st.alpha[qt] = 1.0f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.o[qt][dt] = f32x16{};
   }
-
+  st.rescale = false;
   const float c = a.c;
-  const int nblk = (S + BN - 1) / BN;
-  const int nfull = S / BN;  // blocks with no key past the end of the sequence
-  for (int j = 0; j < nblk; ++j) {
-    // block j's tiles (issued one block earlier) are complete in every wave, and
-    // every wave is done reading the stage block j+1 is about to overwrite
+
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // prologue: score block 0 and take its max
+  Scores<C> sa, sb;
+  qk_block<C>(sa, st, kbuf(0), lane);
+  if (nfull == 0) mask_tail<C>(sa, 0, S, lane);
+  softmax_max<C>(st, sa, c);
+
+  // Steady state, two blocks per trip so the score buffers swap statically.
+  // Entering a step for block i: scores of block i are in one buffer with
+  // their max taken; K_{i+1} and V_i are loaded (or in flight).
+  int j = 0;
+  for (; j + 2 < nblk; j += 2) {
+    // ---- block j (scores in sa), next block's scores into sb
     wait_vmcnt<0>();
     __syncthreads();
-    uint8_t XS_LDS* const cur = lds + (j & 1) * 2 * C::TILE;
-    if (j + 1 < nblk) {
-      uint8_t XS_LDS* const nxt = lds + ((j + 1) & 1) * 2 * C::TILE;
-      load_tile<C>(kbase, row_stride, (j + 1) * BN, S, nxt, koff, wave);
-      load_tile<C>(vbase, row_stride, (j + 1) * BN, S, nxt + C::TILE, voff, wave);
-    }
-    if (j < nfull)
-      block_step<C, false>(st, cur, cur + C::TILE, j * BN, S, c, lane);
-    else
-      block_step<C, true>(st, cur, cur + C::TILE, j * BN, S, c, lane);
+    load_tile<C>(kbase, row_stride, (j + 2) * BN, S, kbuf(j), koff, wave);
+    load_tile<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(j + 1), voff, wave);
+    qk_block<C>(sb, st, kbuf(j + 1), lane);
+    softmax_exp<C>(st, sa, c);
+    interleave<C::NT * 16, 6, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
+    pv_block<C>(st, vbuf(j), lane);
+    softmax_max<C>(st, sb, c);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- block j+1 (scores in sb), next block's scores into sa
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (j + 3 < nblk) load_tile<C>(kbase, row_stride, (j + 3) * BN, S, kbuf(j + 1), koff, wave);
+    load_tile<C>(vbase, row_stride, (j + 2) * BN, S, vbuf(j + 2), voff, wave);
+    qk_block<C>(sa, st, kbuf(j + 2), lane);
+    softmax_exp<C>(st, sb, c);
+    interleave<C::NT * 16, 6, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
+    pv_block<C>(st, vbuf(j + 1), lane);
+    softmax_max<C>(st, sa, c);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the last one or two blocks (scores of block j in sa)
+  if (j + 1 < nblk) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    load_tile<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(j + 1), voff, wave);
+    qk_block<C>(sb, st, kbuf(j + 1), lane);
+    softmax_exp<C>(st, sa, c);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
+    pv_block<C>(st, vbuf(j), lane);
+    softmax_max<C>(st, sb, c);
+    wait_vmcnt<0>();
+    __syncthreads();
+    softmax_exp<C>(st, sb, c);
+    pv_block<C>(st, vbuf(j + 1), lane);
+  } else {
+    wait_vmcnt<0>();  // V_j may have been issued by the last loop step
+    __syncthreads();
+    softmax_exp<C>(st, sa, c);
+    pv_block<C>(st, vbuf(j), lane);
   }
 
   // ---- epilogue: normalise, round to bf16, store into the destination slice
@@ -302,7 +398,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a
 
 template <int D>
 static hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
-  using C = Bf16Cfg<D, 1, 8>;
+  using C = Bf16Cfg<D, XS_QT, XS_NW, XS_BN>;
   const int mtiles = (a.S + C::BM - 1) / C::BM;
   const long long ntiles = (long long)a.B * a.H * mtiles;
   if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;

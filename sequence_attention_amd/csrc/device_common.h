@@ -103,6 +103,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Returns x unchanged but opaque to the optimiser, so address arithmetic that
+// depends on it is recomputed where it is used instead of being hoisted out of
+// the loop and kept live (or spilled) across the whole kernel.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (block i -> XCD i%8).
 // Give XCD x a contiguous range of tiles so that the workgroups resident on one
 // XCD at the same time work on neighbouring tiles of the same (batch, head) and

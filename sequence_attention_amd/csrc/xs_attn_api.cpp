@@ -11,6 +11,15 @@ namespace {
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// |scale| * log2(e): the kernels compute p = 2^(s*c - m).  A zero scale is
+// replaced by a factor so small that s*c rounds every exponent to 0 (p = 1,
+// the uniform softmax) while masked scores (-inf) still give p = 0 instead of
+// the NaN of -inf * 0.
+float scores_factor(float scale) {
+  const float c = fabsf(scale) * kLog2e;
+  return c > 1e-30f ? c : 1e-30f;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -46,7 +55,7 @@ int validate(const void* q, const void* k, const void* v, void* out, int B, int 
   args->P = P;
   args->T = S / P;
   args->neg = scale < 0.0f;
-  args->c = fabsf(scale) * kLog2e;
+  args->c = scores_factor(scale);
   args->o_scale = 1.0f;
   return XS_OK;
 }
@@ -77,7 +86,7 @@ int xs_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_desc
   const float qk = scale * q_descale * k_descale;
   if (!isfinite(qk)) return XS_ERR_UNSUPPORTED;
   a.neg = qk < 0.0f;
-  a.c = fabsf(qk) * kLog2e;
+  a.c = scores_factor(qk);
   a.o_scale = v_descale;
   if (xs::launch_attn_fp8(a, (hipStream_t)stream) != hipSuccess) return XS_ERR_LAUNCH;
   return XS_OK;
