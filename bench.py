@@ -42,7 +42,37 @@ def parse():
                     help="target wall time of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run a plain device copy of MIB MiB (the "
+                         "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib, steps):
+    """A plain device-to-device copy of a known size, for counter calibration."""
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n * 4, "bytes_written": n * 4,
+                                           "launches": steps}}), flush=True)
+
+
+def recorded_traffic(kernel_tag, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or
+    None when there is none for this workload or the kernel sources changed since it was taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256(b"".join(open(os.path.join(ROOT, s), "rb").read() for s in rec["sources"]))
+    if h.hexdigest() != rec["kernel_sources_sha256"]:
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def cpu_baseline(w, inp, target_s):
@@ -78,6 +108,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no cross-GPU step in this build).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
     import sequence_attention_amd as xs
 
     w = workloads.WORKLOADS[args.workload]
@@ -148,7 +181,9 @@ def main():
         "launch_ms": {"mean": round(float(launch_ms.mean()), 4), "min": round(float(launch_ms.min()), 4),
                       "median": round(float(np.median(launch_ms)), 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": recorded_traffic(
+                         "attn_fwd_bf16" if w.dtype == "bf16" else "attn_fwd_fp8", w.name),
                      "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_fp8_kernel",
                      "flops_per_launch": flops},
         "check": check,
