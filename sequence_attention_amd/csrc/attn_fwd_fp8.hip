@@ -1,6 +1,351 @@
-// attn_fwd_fp8.hip -- placeholder until the e4m3 kernel lands.
+// attn_fwd_fp8.hip -- the attention forward pass over OCP e4m3 (e4m3fn) Q/K/V
+// with per-tensor descales, fp32 accumulation and bf16 output, fused with the
+// destination-ordered epilogue; gfx950.
+//
+// Same operation and schedule as the bf16 kernel (X-Stage paper, catalyzex.com
+// abstract; gist.science explainer, "Zentrale Beitraege", "FlashAttention-A2A
+// (Piggybacking)"): per workgroup 8 waves x 32 query rows of one (b, h), K/V
+// blocks of 64 keys double buffered in LDS via direct-to-LDS loads, QK^T of
+// block j+1 overlapped with the softmax of block j inside each wave.  What
+// differs for 8-bit operands:
+//  * Both contractions use v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3 -> fp32):
+//    S^T = K Q^T takes D/64 k-steps; O^T += V^T P^T takes one k-step of all 64
+//    keys of the block per 32-row d tile.
+//  * The descales fold into the exponent factor (c = scale*dq*dk*log2 e) and
+//    the epilogue (O * dv / l); the MFMAs see the raw e4m3 codes.
+//  * P is quantised to e4m3 (p <= 2^TAU = 256 < 448, so nothing saturates).
+//    Its accumulator registers already hold, per half-wave, the 32 keys
+//    {8g + 4h + i}; the V tile is stored in LDS with its rows permuted so that
+//    those keys are 32 consecutive rows, which ds_read_b64_tr_b8 turns into
+//    the V^T operand in the same order.
+//  * Row sums add the fp32 probabilities before quantisation.
 #include "attn_launch.h"
+#include "device_common.h"
 
 namespace xs {
-hipError_t launch_attn_fp8(const AttnArgs&, hipStream_t) { return hipErrorNotSupported; }
+
+template <int D_>
+struct Fp8Cfg {
+  static constexpr int D = D_;
+  static constexpr int NW = 8;            // waves per workgroup, 32 query rows each
+  static constexpr int BN = 64;           // keys per K/V block
+  static constexpr int QW = 32;
+  static constexpr int BM = QW * NW;
+  static constexpr int ROWB = D;          // bytes per K/V row
+  static constexpr int CH = D / 16;       // 16-byte chunks per row
+  static constexpr int RPB = 256 / D;     // rows per 256 bytes (one pass over the LDS banks)
+  static constexpr int TILE = BN * ROWB;  // bytes per K or V tile
+  static constexpr int LOADS = TILE / 1024;
+  static constexpr int KS = D / 64;       // k-steps of QK^T
+  static constexpr int DT = D / 32;       // 32-row d tiles of O^T
+  static constexpr int NT = BN / 32;      // 32-key score tiles per block
+  static constexpr int THREADS = 64 * NW;
+  static constexpr float TAU = 8.0f;      // lazy-rescale threshold (log2 units)
+  static_assert(LOADS <= NW, "one direct load per wave at most");
+  static_assert(NT == 2, "the P^T operand layout assumes 64-key blocks");
+};
+
+// LDS row R of a V tile holds key 8*((R%32)/4) + 4*(R/32) + R%4: rows
+// 32h..32h+31 are the keys whose scores half-wave h holds, in register order.
+__device__ __forceinline__ int vrow_key(int R) { return 8 * ((R & 31) >> 2) + 4 * (R >> 5) + (R & 3); }
+
+// XOR swizzles of the 16-byte chunk index, chosen so that a ds_read_b128 of
+// 16 consecutive K rows, and a ds_read_b64_tr_b8 of 8 V rows x 2 chunks, touch
+// every LDS bank once.
+template <class C>
+__device__ __forceinline__ int kswz(int R) { return (R / C::RPB) & (C::CH - 1); }
+template <class C>
+__device__ __forceinline__ int vswz(int R) { return 2 * ((R / C::RPB) & (C::CH / 2 - 1)); }
+
+template <class C>
+__device__ __forceinline__ void load_tile8(const uint8_t* head_base, uint32_t row_stride, int kv0,
+                                           int S, const uint8_t XS_LDS* dst, uint32_t voff, int wave) {
+  if (wave < C::LOADS) {
+    const u32x4 rsrc = make_rsrc(head_base + (size_t)kv0 * row_stride,
+                                 (uint32_t)(S - kv0 - 1) * row_stride + (uint32_t)C::ROWB);
+    load_lds_b128(rsrc, voff, lds_addr(dst) + (uint32_t)wave * 1024u);
+  }
+}
+
+template <class C>
+struct Scores8 {
+  f32x16 s[C::NT];
+};
+
+template <class C>
+struct Fp8State {
+  f32x16 o[C::DT];
+  i32x8 qf[C::KS];
+  i32x8 pf;          // P^T operand: e4m3 probabilities of the 64 keys
+  float m, l, alpha;
+  bool rescale;
+};
+
+template <class C>
+__device__ __forceinline__ void qk_block8(Scores8<C>& sc, const Fp8State<C>& st,
+                                          const uint8_t XS_LDS* sK, int lane) {
+  const int ln = opaque(lane);
+  const int hi = ln >> 5;
+  const int R = ln & 31;
+  const uint8_t XS_LDS* krow = sK + R * C::ROWB;
+  const int sw = kswz<C>(R);
+#pragma unroll
+  for (int t = 0; t < C::KS; ++t) {
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      const int c0 = 4 * t + 2 * hi;
+      const u32x4 a0 = lds_read_b128(krow + nt * 32 * C::ROWB + ((c0 ^ sw) << 4));
+      const u32x4 a1 = lds_read_b128(krow + nt * 32 * C::ROWB + (((c0 + 1) ^ sw) << 4));
+      const i32x8 kf = __builtin_bit_cast(i32x8, (u32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}));
+      sc.s[nt] = mfma_fp8(kf, st.qf[t], t == 0 ? f32x16{} : sc.s[nt]);
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void pv_block8(Fp8State<C>& st, const uint8_t XS_LDS* sV, int lane) {
+  if (st.rescale) {
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) st.o[dt] *= st.alpha;
+    st.alpha = 1.0f;
+    st.rescale = false;
+  }
+  const int ln = opaque(lane);
+  const int g = ln >> 4, L = ln & 15, h = g >> 1;
+  const int R0 = 32 * h + (L >> 1);          // + 8t
+  const int sw = vswz<C>(R0);                // the same for R0 + 8t
+  const uint8_t XS_LDS* vbase = sV + R0 * C::ROWB + 8 * (L & 1);
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+    const int chunk = (dt * 2 + (g & 1)) ^ sw;
+    u32x2 r[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) r[t] = lds_read_tr8(vbase + 8 * t * C::ROWB + (chunk << 4));
+    const i32x8 vf = __builtin_bit_cast(
+        i32x8, (u32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]}));
+    st.o[dt] = mfma_fp8(vf, st.pf, st.o[dt]);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void mask_tail8(Scores8<C>& sc, int kv0, int S, int lane) {
+  const int hi = lane >> 5;
+#pragma unroll
+  for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kv0 + nt * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+      if (key >= S) sc.s[nt][r] = -INFINITY;
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void softmax_max8(Fp8State<C>& st, const Scores8<C>& sc, float c) {
+  float mx = sc.s[0][0];
+#pragma unroll
+  for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc.s[nt][r]);
+  const float mnew = max_halves(mx) * c;
+  const bool need = mnew > st.m + C::TAU;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float a = need ? fast_exp2(st.m - mnew) : 1.0f;
+    st.m = need ? mnew : st.m;
+    st.l *= a;
+    st.alpha *= a;
+    st.rescale = true;
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void softmax_exp8(Fp8State<C>& st, const Scores8<C>& sc, float c) {
+  const float neg_m = -st.m;
+  float lsum = st.l;
+  uint32_t w[8];
+#pragma unroll
+  for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(__builtin_fmaf(sc.s[nt][4 * q + i], c, neg_m));
+        lsum += p[i];
+      }
+      w[nt * 4 + q] = pack_fp8x4(p[0], p[1], p[2], p[3]);
+    }
+  st.pf = __builtin_bit_cast(i32x8, (u32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]}));
+  st.l = lsum;
+}
+
+template <int N, int V, int DS>
+__device__ __forceinline__ void interleave8() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (DS) __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+    if (V) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a) {
+  constexpr int BM = C::BM, BN = C::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];
+  uint8_t XS_LDS* const lds = (uint8_t XS_LDS*)smem;
+  auto kbuf = [&](int i) { return lds + (i & 1) * C::TILE; };
+  auto vbuf = [&](int i) { return lds + (2 + (i & 1)) * C::TILE; };
+
+  const int S = a.S, H = a.H;
+  const int mtiles = (S + BM - 1) / BM;
+  const int ntiles = a.B * H * mtiles;
+  const int tile = xcd_tile(blockIdx.x, ntiles);
+  const int mt = tile % mtiles;
+  const int bh = tile / mtiles;
+  const int h = bh % H, b = bh / H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int m0 = mt * BM;
+
+  const uint32_t row_stride = (uint32_t)H * C::ROWB;
+  const size_t head_off = ((size_t)b * S * H + h) * C::ROWB;
+  const uint8_t* kbase = (const uint8_t*)a.k + head_off;
+  const uint8_t* vbase = (const uint8_t*)a.v + head_off;
+  // this lane's 16-byte chunk of the wave's 1 KiB direct load, for K and V
+  uint32_t koff, voff;
+  {
+    const int pos = wave * 64 + lane;
+    const int R = pos / C::CH, cp = pos % C::CH;
+    koff = (uint32_t)R * row_stride + (uint32_t)((cp ^ kswz<C>(R)) * 16);
+    voff = (uint32_t)vrow_key(R) * row_stride + (uint32_t)((cp ^ vswz<C>(R)) * 16);
+  }
+
+  const int nblk = (S + BN - 1) / BN;
+  const int nfull = S / BN;
+  load_tile8<C>(kbase, row_stride, 0, S, kbuf(0), koff, wave);
+  load_tile8<C>(vbase, row_stride, 0, S, vbuf(0), voff, wave);
+  if (nblk > 1) load_tile8<C>(kbase, row_stride, BN, S, kbuf(1), koff, wave);
+
+  Fp8State<C> st;
+  {
+    const uint32_t qflip = a.neg ? 0x80808080u : 0u;
+    int qrow = m0 + wave * C::QW + (lane & 31);
+    qrow = qrow < S ? qrow : S - 1;
+    const uint8_t* qp = (const uint8_t*)a.q + head_off + (size_t)qrow * row_stride + (lane >> 5) * 32;
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t) {
+      const u32x4 x0 = *(const u32x4*)(qp + t * 64) ^ qflip;
+      const u32x4 x1 = *(const u32x4*)(qp + t * 64 + 16) ^ qflip;
+      st.qf[t] = __builtin_bit_cast(i32x8, (u32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}));
+    }
+  }
+  st.m = -INFINITY;
+  st.l = 0.0f;
+  st.alpha = 1.0f;
+  st.rescale = false;
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) st.o[dt] = f32x16{};
+  const float c = a.c;
+
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  Scores8<C> sa, sb;
+  qk_block8<C>(sa, st, kbuf(0), lane);
+  if (nfull == 0) mask_tail8<C>(sa, 0, S, lane);
+  softmax_max8<C>(st, sa, c);
+
+  int j = 0;
+  for (; j + 2 < nblk; j += 2) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    load_tile8<C>(kbase, row_stride, (j + 2) * BN, S, kbuf(j), koff, wave);
+    load_tile8<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(j + 1), voff, wave);
+    qk_block8<C>(sb, st, kbuf(j + 1), lane);
+    softmax_exp8<C>(st, sa, c);
+    interleave8<C::NT * C::KS, 10, 2>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
+    pv_block8<C>(st, vbuf(j), lane);
+    softmax_max8<C>(st, sb, c);
+    __builtin_amdgcn_sched_barrier(0);
+
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (j + 3 < nblk) load_tile8<C>(kbase, row_stride, (j + 3) * BN, S, kbuf(j + 1), koff, wave);
+    load_tile8<C>(vbase, row_stride, (j + 2) * BN, S, vbuf(j + 2), voff, wave);
+    qk_block8<C>(sa, st, kbuf(j + 2), lane);
+    softmax_exp8<C>(st, sb, c);
+    interleave8<C::NT * C::KS, 10, 2>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 2 >= nfull) mask_tail8<C>(sa, (j + 2) * BN, S, lane);
+    pv_block8<C>(st, vbuf(j + 1), lane);
+    softmax_max8<C>(st, sa, c);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (j + 1 < nblk) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    load_tile8<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(j + 1), voff, wave);
+    qk_block8<C>(sb, st, kbuf(j + 1), lane);
+    softmax_exp8<C>(st, sa, c);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
+    pv_block8<C>(st, vbuf(j), lane);
+    softmax_max8<C>(st, sb, c);
+    wait_vmcnt<0>();
+    __syncthreads();
+    softmax_exp8<C>(st, sb, c);
+    pv_block8<C>(st, vbuf(j + 1), lane);
+  } else {
+    wait_vmcnt<0>();
+    __syncthreads();
+    softmax_exp8<C>(st, sa, c);
+    pv_block8<C>(st, vbuf(j), lane);
+  }
+
+  // ---- epilogue: O * dv / l, rounded to bf16, stored into the destination slice
+  const int T = a.T, B = a.B;
+  const float inv = a.o_scale / sum_halves(st.l);
+  const int srow = m0 + wave * C::QW + (lane & 31);
+  if (srow < S) {
+    const int p = srow / T;
+    const int sp = srow - p * T;
+    uint16_t* orow = (uint16_t*)a.out + ((((size_t)p * B + b) * T + sp) * H + h) * C::D;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = dt * 32 + r4 * 8 + 4 * (lane >> 5);
+        const f32x16& o = st.o[dt];
+        u32x2 w = {pack_bf16(o[4 * r4 + 0] * inv, o[4 * r4 + 1] * inv),
+                   pack_bf16(o[4 * r4 + 2] * inv, o[4 * r4 + 3] * inv)};
+        *(u32x2*)(orow + d0) = w;
+      }
+  }
+}
+
+template <int D>
+static hipError_t launch_d8(const AttnArgs& a, hipStream_t stream) {
+  using C = Fp8Cfg<D>;
+  const int mtiles = (a.S + C::BM - 1) / C::BM;
+  const long long ntiles = (long long)a.B * a.H * mtiles;
+  if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  AttnArgs args = a;
+  void* kargs[] = {&args};
+  return hipLaunchKernel((const void*)attn_fwd_fp8_kernel<C>, dim3((unsigned)ntiles), dim3(C::THREADS),
+                         kargs, 0, stream);
+}
+
+hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream) {
+  switch (a.D) {
+    case 64:
+      return launch_d8<64>(a, stream);
+    case 128:
+      return launch_d8<128>(a, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace xs

@@ -15,6 +15,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define XS_LDS __attribute__((address_space(3)))
@@ -42,6 +43,16 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 // row-major 16-bit matrix, lane j receives rows r0..r0+3 of column c0 + j.
 __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t XS_LDS* p) {
   i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 XS_LDS*)p);
+  return __builtin_bit_cast(u32x2, t);
+}
+
+// ds_read_b64_tr_b8: within each group of 16 lanes, lane j receives byte j%8
+// of the 64-bit words addressed by lanes 2e + j/8, e = 0..7.  When lane L of
+// the group addresses row r0 + L/2, columns c0 + 8*(L%2) .. +7 of a row-major
+// byte matrix, lane j receives rows r0..r0+7 of column c0 + j.
+__device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t XS_LDS* p) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 XS_LDS*)p);
   return __builtin_bit_cast(u32x2, t);
 }
 
@@ -99,6 +110,14 @@ __device__ __forceinline__ float sum_halves(float x) {
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   f32x2 v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Four fp32 values -> four OCP e4m3 bytes (round to nearest even), first value
+// in the low byte.  Inputs must stay below 464 (larger values become NaN).
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
