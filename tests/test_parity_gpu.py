@@ -278,3 +278,84 @@ def test_negative_controls_fail_the_gate(gpu):
     assert not gate(pick(swapped), ref, "bf16")[2], "slices"
     wrong_head = (q, torch.roll(k, 1, dims=2).contiguous(), torch.roll(v, 1, dims=2).contiguous())
     assert not gate(pick(run(inp, w.P, gpu, tensors=wrong_head)), ref, "bf16")[2], "head"
+
+
+# ------------------------------------------------------------------ fp8 path: exactness properties
+def test_fp8_relayout_is_bit_exact_and_deterministic(gpu):
+    w = workloads.custom(2, 1000, 3, 128, 8, dtype="fp8", index=4000)
+    inp = workloads.make_inputs(w)
+    q, k, v = to_gpu(inp, gpu)
+    base = xs.unpack(run(inp, 1, gpu, tensors=(q, k, v)), w.S)
+    for P in (2, 8, 1000):
+        out = run(inp, P, gpu, tensors=(q, k, v))
+        want = torch.stack(torch.split(base, w.S // P, dim=1)).contiguous()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"P={P}"
+    again = xs.unpack(run(inp, 1, gpu, tensors=(q, k, v)), w.S)
+    assert torch.equal(again.view(torch.int16), base.view(torch.int16))
+
+
+def test_fp8_descale_metamorphic(gpu):
+    # (2 dq) * (scale / 2) = dq * scale exactly in fp32, so the exponent factor is
+    # unchanged; doubling dv doubles every output exactly.
+    w = workloads.custom(1, 700, 2, 128, 7, dtype="fp8", index=4100)
+    inp = workloads.make_inputs(w)
+    q, k, v = to_gpu(inp, gpu)
+    dq, dk, dv = inp["descales"]
+    _say("fp8 descale metamorphic")
+    a = xs.fwd_fp8(q, k, v, (dq, dk, dv), 7, inp["scale"])
+    b = xs.fwd_fp8(q, k, v, (2 * dq, dk, 2 * dv), 7, inp["scale"] / 2)
+    torch.cuda.synchronize()
+    assert torch.equal((a * 2).view(torch.int16), b.view(torch.int16))
+
+
+def test_fp8_negative_scale(gpu):
+    w = workloads.custom(2, 333, 2, 64, 3, dtype="fp8", index=4200)
+    inp = workloads.make_inputs(w)
+    scale = -0.0883883461356163
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], 3, scale, inp["descales"])
+    out = run(inp, 3, gpu, scale=scale)
+    assert_gate(f64(out), ref, "fp8", f"fp8 scale={scale}")
+
+
+def test_fp8_peaked_softmax_within_rounding_bound(gpu):
+    # At scale 0.25, D=64 a few keys dominate each row and the e4m3 rounding of P
+    # (unit roundoff 2^-4 for normal values, absolute 2^-10 below 2^-6) no longer
+    # averages out.  Bound per element: 2^-4 (1 + 2^-8) sum_j w_ij |v_j| for P,
+    # 2^-8 |O_i| for the bf16 output, and 2^-9 max|v| for weights in the
+    # subnormal range; the relative-L2 gate of the fp8 workloads still applies.
+    w = workloads.custom(2, 333, 2, 64, 3, dtype="fp8", index=4200)
+    inp = workloads.make_inputs(w)
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], 3, 0.25, inp["descales"])
+    vabs = inp["v"].to(torch.float64).abs().to(torch.float64)
+    # sum_j w_ij |v_j| from the oracle on |V| (same weights, dequantised |v|)
+    dq, dk, dv = inp["descales"]
+    qf = inp["q"].to(torch.float64) * dq
+    kf = inp["k"].to(torch.float64) * dk
+    ref_abs = oracle.attention_packed(qf, kf, vabs * dv, 3, 0.25)
+    got = f64(run(inp, 3, gpu, scale=0.25))
+    vmax = float(vabs.max()) * dv
+    bound = 2.0 ** -4 * (1 + 2.0 ** -8) * ref_abs + 2.0 ** -8 * np.abs(ref) + 2.0 ** -9 * vmax
+    worst = float((np.abs(got - ref) / bound).max())
+    print(f"  fp8 scale=0.25 worst error / bound = {worst:.3f}", flush=True)
+    assert worst <= 1.0
+    assert gate(got, ref, "fp8")[1] <= TOL["fp8"][1]
+
+
+def test_fp8_canaries_and_full_write(gpu):
+    B, S, H, D, P = 2, 130, 2, 64, 2
+    w = workloads.custom(B, S, H, D, P, dtype="fp8", index=4300)
+    inp = workloads.make_inputs(w)
+    q, k, v = to_gpu(inp, gpu)
+    n = P * B * (S // P) * H * D
+    pad = 2048
+    big = torch.full((n + 2 * pad,), float("nan"), dtype=torch.bfloat16, device=gpu)
+    big[:pad] = 5.0
+    big[pad + n:] = -9.0
+    out = big[pad:pad + n].view(P, B, S // P, H, D)
+    _say("fp8 canary", B, S, H, D, P)
+    xs.fwd_fp8(q, k, v, inp["descales"], P, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any()
+    assert torch.all(big[:pad] == 5.0) and torch.all(big[pad + n:] == -9.0)
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, inp["scale"], inp["descales"])
+    assert_gate(f64(out), ref, "fp8", "fp8 canary case")
