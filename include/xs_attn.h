@@ -34,6 +34,8 @@
 #ifndef XS_ATTN_H
 #define XS_ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -42,10 +44,12 @@ extern "C" {
 #define XS_OK 0
 #define XS_ERR_NULL (-1)        /* a required pointer is NULL */
 #define XS_ERR_SHAPE (-2)       /* B, S, H_local, D or P < 1, or S % P != 0 */
-#define XS_ERR_UNSUPPORTED (-3) /* D not in {64, 128}, scale or a descale not finite, size overflow */
+#define XS_ERR_UNSUPPORTED (-3) /* D not in {64, 128}, scale or a descale not finite, or
+                                   S*H_local*D*elem_bytes >= 4 GiB (one batch's rows) */
 #define XS_ERR_ALIGN (-4)       /* a pointer is not 16-byte aligned */
 #define XS_ERR_LAUNCH (-5)      /* the HIP launch reported an error */
 #define XS_ERR_OVERLAP (-6)     /* out_packed overlaps q, k or v */
+#define XS_ERR_WORKSPACE (-7)   /* workspace smaller than xs_attn_workspace_size() */
 
 /* Attention forward over bf16 inputs with the destination-ordered epilogue.
  *   q, k, v     bf16 [B][S][H_local][D], device memory (read only)
@@ -64,6 +68,40 @@ int xs_attn_fwd(const void *q, const void *k, const void *v, void *out_packed, i
 int xs_attn_fwd_fp8(const void *q8, const void *k8, const void *v8, float q_descale,
                     float k_descale, float v_descale, void *out_packed, int B, int S, int H_local,
                     int D, int P, float scale, void *stream);
+
+/* Split-key variants.  When the grid of 256-row query tiles would leave compute
+ * units idle (few heads, or a last partial round of tiles), the key range of
+ * every tile is cut into nsplit chunks processed by separate workgroups; each
+ * writes unnormalised fp32 partials (O and, per row, the running max and row
+ * sum) into `workspace`, and a second kernel on the same stream merges them
+ * with the online-softmax rule into out_packed.  This is the merge of partial
+ * attention by online softmax of "Move the Query, Not the Cache" (gist.science
+ * explainer, Methodik: the Route primitive), applied inside one GPU.
+ *   workspace        device memory, 16-byte aligned, at least
+ *                    xs_attn_workspace_size(B, S, H_local, D) bytes; owned by the
+ *                    caller, not retained after the call; its contents are
+ *                    scratch (overwritten).  Calls that overlap in time must not
+ *                    share a workspace.
+ *   workspace NULL   run without splitting (identical to xs_attn_fwd).
+ * Results differ from the unsplit call only by rounding (the splits are merged
+ * in a fixed order, so they are deterministic); they do not depend on P.
+ * Returns XS_ERR_WORKSPACE if workspace is non-NULL but too small. */
+int xs_attn_fwd_ws(const void *q, const void *k, const void *v, void *out_packed, int B, int S,
+                   int H_local, int D, int P, float scale, void *workspace,
+                   size_t workspace_bytes, void *stream);
+int xs_attn_fwd_fp8_ws(const void *q8, const void *k8, const void *v8, float q_descale,
+                       float k_descale, float v_descale, void *out_packed, int B, int S,
+                       int H_local, int D, int P, float scale, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace the split-key variants need on the current device for this
+ * shape (0: the shape is run unsplit).  Depends on the device's compute-unit
+ * count; returns 0 for invalid sizes.  No allocation, no kernel launch. */
+size_t xs_attn_workspace_size(int B, int S, int H_local, int D);
+
+/* The number of key-range splits the split-key variants use for this shape on
+ * the current device (1 = unsplit); 0 for invalid sizes. */
+int xs_attn_split_count(int B, int S, int H_local, int D);
 
 /* Static, never-NULL description of a status code. */
 const char *xs_attn_strerror(int status);

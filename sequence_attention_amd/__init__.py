@@ -9,6 +9,11 @@ the calls raise.
     out_packed = fwd(q, k, v, P)            # bf16 q/k/v [B][S][H][D] on the GPU
     out_packed = fwd_fp8(q8, k8, v8, descales, P)
     o = unpack(out_packed, S)               # back to [B][S][H][D] (a torch view)
+
+By default the calls use the split-key schedule when it fills the GPU better,
+with a workspace allocated from torch's caching allocator (pass a tensor of
+at least workspace_size(...) bytes to reuse one, or workspace=None to run
+unsplit).
 """
 from __future__ import annotations
 
@@ -19,8 +24,10 @@ import torch
 
 from ._lib import XsAttnError, check, declared_functions, lib, strerror
 
-__all__ = ["fwd", "fwd_fp8", "unpack", "xs_attn_fwd", "xs_attn_fwd_fp8", "xs_attn_strerror",
-           "xs_attn_version", "XsAttnError", "default_scale"]
+__all__ = ["fwd", "fwd_fp8", "unpack", "workspace_size", "split_count", "xs_attn_fwd",
+           "xs_attn_fwd_fp8", "xs_attn_fwd_ws", "xs_attn_fwd_fp8_ws", "xs_attn_workspace_size",
+           "xs_attn_split_count", "xs_attn_strerror", "xs_attn_version", "XsAttnError",
+           "default_scale"]
 
 
 def default_scale(D: int) -> float:
@@ -73,6 +80,50 @@ def xs_attn_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, out_packed, B, 
                                  float(scale), stream)
 
 
+def xs_attn_fwd_ws(q, k, v, out_packed, B, S, H_local, D, P, scale, workspace, workspace_bytes,
+                   stream) -> int:
+    ptr = lambda x: x.data_ptr() if isinstance(x, torch.Tensor) else x
+    return lib().xs_attn_fwd_ws(ptr(q), ptr(k), ptr(v), ptr(out_packed), B, S, H_local, D, P,
+                                float(scale), ptr(workspace), int(workspace_bytes), stream)
+
+
+def xs_attn_fwd_fp8_ws(q8, k8, v8, q_descale, k_descale, v_descale, out_packed, B, S, H_local, D,
+                       P, scale, workspace, workspace_bytes, stream) -> int:
+    ptr = lambda x: x.data_ptr() if isinstance(x, torch.Tensor) else x
+    return lib().xs_attn_fwd_fp8_ws(ptr(q8), ptr(k8), ptr(v8), float(q_descale), float(k_descale),
+                                    float(v_descale), ptr(out_packed), B, S, H_local, D, P,
+                                    float(scale), ptr(workspace), int(workspace_bytes), stream)
+
+
+def xs_attn_workspace_size(B, S, H_local, D) -> int:
+    return int(lib().xs_attn_workspace_size(B, S, H_local, D))
+
+
+def xs_attn_split_count(B, S, H_local, D) -> int:
+    return int(lib().xs_attn_split_count(B, S, H_local, D))
+
+
+workspace_size = xs_attn_workspace_size
+split_count = xs_attn_split_count
+
+
+def _workspace(q, workspace):
+    """Resolve the workspace argument to (pointer-or-tensor, bytes)."""
+    if workspace is None:
+        return None, 0
+    B, S, H, D = q.shape
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be a tensor, None or 'auto'")
+        n = xs_attn_workspace_size(B, S, H, D)
+        if n == 0:
+            return None, 0
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise TypeError("workspace must be a GPU tensor")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def xs_attn_strerror(status: int) -> str:
     return strerror(status)
 
@@ -81,26 +132,29 @@ def xs_attn_version() -> int:
     return int(lib().xs_attn_version())
 
 
-def fwd(q, k, v, P: int, scale: float | None = None, out=None, stream=None) -> torch.Tensor:
+def fwd(q, k, v, P: int, scale: float | None = None, out=None, stream=None,
+        workspace="auto") -> torch.Tensor:
     """Attention over bf16 [B][S][H][D] inputs; returns bf16 out_packed [P][B][S/P][H][D]."""
     _check_inputs(q, k, v, torch.bfloat16)
     B, S, H, D = q.shape
     out = _out(q, P, out)
     scale = default_scale(D) if scale is None else float(scale)
-    check(xs_attn_fwd(q, k, v, out, B, S, H, D, P, scale, _stream_ptr(q, stream)))
+    ws, nbytes = _workspace(q, workspace)
+    check(xs_attn_fwd_ws(q, k, v, out, B, S, H, D, P, scale, ws, nbytes, _stream_ptr(q, stream)))
     return out
 
 
 def fwd_fp8(q8, k8, v8, descales, P: int, scale: float | None = None, out=None,
-            stream=None) -> torch.Tensor:
+            stream=None, workspace="auto") -> torch.Tensor:
     """Attention over e4m3 [B][S][H][D] inputs with per-tensor descales (x = x8 * d)."""
     _check_inputs(q8, k8, v8, torch.float8_e4m3fn)
     B, S, H, D = q8.shape
     out = _out(q8, P, out)
     scale = default_scale(D) if scale is None else float(scale)
     dq, dk, dv = (float(d) for d in descales)
-    check(xs_attn_fwd_fp8(q8, k8, v8, dq, dk, dv, out, B, S, H, D, P, scale,
-                          _stream_ptr(q8, stream)))
+    ws, nbytes = _workspace(q8, workspace)
+    check(xs_attn_fwd_fp8_ws(q8, k8, v8, dq, dk, dv, out, B, S, H, D, P, scale, ws, nbytes,
+                             _stream_ptr(q8, stream)))
     return out
 
 

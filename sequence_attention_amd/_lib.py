@@ -31,6 +31,15 @@ def lib() -> ctypes.CDLL:
         L.xs_attn_fwd.restype = ci
         L.xs_attn_fwd_fp8.argtypes = [vp, vp, vp, cf, cf, cf, vp, ci, ci, ci, ci, ci, cf, vp]
         L.xs_attn_fwd_fp8.restype = ci
+        sz = ctypes.c_size_t
+        L.xs_attn_fwd_ws.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp, sz, vp]
+        L.xs_attn_fwd_ws.restype = ci
+        L.xs_attn_fwd_fp8_ws.argtypes = [vp, vp, vp, cf, cf, cf, vp, ci, ci, ci, ci, ci, cf, vp, sz, vp]
+        L.xs_attn_fwd_fp8_ws.restype = ci
+        L.xs_attn_workspace_size.argtypes = [ci, ci, ci, ci]
+        L.xs_attn_workspace_size.restype = sz
+        L.xs_attn_split_count.argtypes = [ci, ci, ci, ci]
+        L.xs_attn_split_count.restype = ci
         L.xs_attn_strerror.argtypes = [ci]
         L.xs_attn_strerror.restype = ctypes.c_char_p
         L.xs_attn_version.argtypes = []

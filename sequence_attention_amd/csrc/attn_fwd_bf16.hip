@@ -264,10 +264,13 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a
 
   const int S = a.S, H = a.H;
   const int mtiles = (S + BM - 1) / BM;
-  const int ntiles = a.B * H * mtiles;
-  const int tile = xcd_tile(blockIdx.x, ntiles);
-  const int mt = tile % mtiles;
-  const int bh = tile / mtiles;
+  const int nsplit = a.nsplit;
+  // work item = ((b*H + h)*nsplit + split)*mtiles + m-tile, XCD-aware order: the
+  // items resident on one XCD at once share a head and a key range
+  const int item = xcd_tile(blockIdx.x, a.B * H * nsplit * mtiles);
+  const int mt = item % mtiles;
+  const int split = (item / mtiles) % nsplit;
+  const int bh = item / (mtiles * nsplit);
   const int h = bh % H, b = bh / H;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -283,9 +286,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a
 
   const int nblk = (S + BN - 1) / BN;
   const int nfull = S / BN;  // blocks with no key past the end of the sequence
-  load_tile<C>(kbase, row_stride, 0, S, kbuf(0), koff, wave);
-  load_tile<C>(vbase, row_stride, 0, S, vbuf(0), voff, wave);
-  if (nblk > 1) load_tile<C>(kbase, row_stride, BN, S, kbuf(1), koff, wave);
+  const int jb = split * a.nb_per;                                // this item's key blocks
+  const int je = jb + a.nb_per < nblk ? jb + a.nb_per : nblk;    // [jb, je)
+  load_tile<C>(kbase, row_stride, jb * BN, S, kbuf(jb), koff, wave);
+  load_tile<C>(vbase, row_stride, jb * BN, S, vbuf(jb), voff, wave);
+  if (jb + 1 < je) load_tile<C>(kbase, row_stride, (jb + 1) * BN, S, kbuf(jb + 1), koff, wave);
 
   Bf16State<C> st;
   const uint32_t qflip = a.neg ? 0x80008000u : 0u;
@@ -313,15 +318,15 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a
 
   // prologue: score block 0 and take its max
   Scores<C> sa, sb;
-  qk_block<C>(sa, st, kbuf(0), lane);
-  if (nfull == 0) mask_tail<C>(sa, 0, S, lane);
+  qk_block<C>(sa, st, kbuf(jb), lane);
+  if (jb >= nfull) mask_tail<C>(sa, jb * BN, S, lane);
   softmax_max<C>(st, sa, c);
 
   // Steady state, two blocks per trip so the score buffers swap statically.
   // Entering a step for block i: scores of block i are in one buffer with
   // their max taken; K_{i+1} and V_i are loaded (or in flight).
-  int j = 0;
-  for (; j + 2 < nblk; j += 2) {
+  int j = jb;
+  for (; j + 2 < je; j += 2) {
     // ---- block j (scores in sa), next block's scores into sb
     wait_vmcnt<0>();
     __syncthreads();
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a
     // ---- block j+1 (scores in sb), next block's scores into sa
     wait_vmcnt<0>();
     __syncthreads();
-    if (j + 3 < nblk) load_tile<C>(kbase, row_stride, (j + 3) * BN, S, kbuf(j + 1), koff, wave);
+    if (j + 3 < je) load_tile<C>(kbase, row_stride, (j + 3) * BN, S, kbuf(j + 1), koff, wave);
     load_tile<C>(vbase, row_stride, (j + 2) * BN, S, vbuf(j + 2), voff, wave);
     qk_block<C>(sa, st, kbuf(j + 2), lane);
     softmax_exp<C>(st, sb, c);
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a
     __builtin_amdgcn_sched_barrier(0);
   }
   // the last one or two blocks (scores of block j in sa)
-  if (j + 1 < nblk) {
+  if (j + 1 < je) {
     wait_vmcnt<0>();
     __syncthreads();
     load_tile<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(j + 1), voff, wave);
@@ -372,26 +377,50 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a
     pv_block<C>(st, vbuf(j), lane);
   }
 
-  // ---- epilogue: normalise, round to bf16, store into the destination slice
+  // ---- epilogue
   const int T = a.T, B = a.B;
+  if (nsplit == 1) {
+    // normalise, round to bf16, store into the destination slice
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const float inv = a.o_scale / sum_halves(st.l[qt]);
-    const int srow = m0 + wave * C::QW + qt * 32 + (lane & 31);
-    if (srow < S) {
-      const int p = srow / T;
-      const int sp = srow - p * T;
-      uint16_t* orow = (uint16_t*)a.out + ((((size_t)p * B + b) * T + sp) * H + h) * C::D;
+    for (int qt = 0; qt < QT; ++qt) {
+      const float inv = a.o_scale / sum_halves(st.l[qt]);
+      const int srow = m0 + wave * C::QW + qt * 32 + (lane & 31);
+      if (srow < S) {
+        const int p = srow / T;
+        const int sp = srow - p * T;
+        uint16_t* orow = (uint16_t*)a.out + ((((size_t)p * B + b) * T + sp) * H + h) * C::D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = dt * 32 + r4 * 8 + 4 * (lane >> 5);
-          const f32x16& o = st.o[qt][dt];
-          u32x2 w = {pack_bf16(o[4 * r4 + 0] * inv, o[4 * r4 + 1] * inv),
-                     pack_bf16(o[4 * r4 + 2] * inv, o[4 * r4 + 3] * inv)};
-          *(u32x2*)(orow + d0) = w;
-        }
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int d0 = dt * 32 + r4 * 8 + 4 * (lane >> 5);
+            const f32x16& o = st.o[qt][dt];
+            u32x2 w = {pack_bf16(o[4 * r4 + 0] * inv, o[4 * r4 + 1] * inv),
+                       pack_bf16(o[4 * r4 + 2] * inv, o[4 * r4 + 3] * inv)};
+            *(u32x2*)(orow + d0) = w;
+          }
+      }
+    }
+  } else {
+    // unnormalised fp32 partials of this key range, merged by attn_combine
+    const size_t rows = (size_t)B * H * S;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float lsum = sum_halves(st.l[qt]);
+      const int srow = m0 + wave * C::QW + qt * 32 + (lane & 31);
+      if (srow < S) {
+        const size_t r = (size_t)split * rows + (size_t)bh * S + srow;
+        float* orow = a.ws_o + r * C::D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x16& o = st.o[qt][dt];
+            *(f32x4*)(orow + dt * 32 + r4 * 8 + 4 * (lane >> 5)) =
+                f32x4{o[4 * r4 + 0], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]};
+          }
+        if (lane < 32) *(f32x2*)(a.ws_ml + 2 * r) = f32x2{st.m[qt], lsum};
+      }
     }
   }
 }
@@ -399,12 +428,13 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a
 template <int D>
 static hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   using C = Bf16Cfg<D, XS_QT, XS_NW, XS_BN>;
+  static_assert(C::BM == kBlockM && C::BN == kBlockN, "tile geometry");
   const int mtiles = (a.S + C::BM - 1) / C::BM;
-  const long long ntiles = (long long)a.B * a.H * mtiles;
-  if (ntiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  const long long items = (long long)a.B * a.H * a.nsplit * mtiles;
+  if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   AttnArgs args = a;
   void* kargs[] = {&args};
-  return hipLaunchKernel((const void*)attn_fwd_bf16_kernel<C>, dim3((unsigned)ntiles), dim3(C::THREADS),
+  return hipLaunchKernel((const void*)attn_fwd_bf16_kernel<C>, dim3((unsigned)items), dim3(C::THREADS),
                          kargs, 0, stream);
 }
 

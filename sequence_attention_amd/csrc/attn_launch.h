@@ -16,7 +16,21 @@ struct AttnArgs {
   float c;        // |scale| * log2(e), times q_descale * k_descale for fp8
   int neg;        // nonzero when scale < 0: queries are negated as they are loaded
   float o_scale;  // factor applied with 1/l in the epilogue (v_descale for fp8)
+  // Split of the key range: work item (b, h, split, m-tile) covers key blocks
+  // [split*nb_per, min(nblk, (split+1)*nb_per)).  With nsplit > 1 the items
+  // write unnormalised fp32 partials (O, and m, l per row) to the workspace
+  // and attn_combine merges them into out.
+  int nsplit;
+  int nb_per;
+  float* ws_o;    // [nsplit][B*H*S][D] fp32
+  float* ws_ml;   // [nsplit][B*H*S][2] fp32: running max (log2 units), row sum
 };
+
+// Tile geometry shared by the bf16 and fp8 kernels and the host-side plan.
+constexpr int kBlockM = 256;  // query rows per workgroup
+constexpr int kBlockN = 64;   // keys per K/V block
+
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream);

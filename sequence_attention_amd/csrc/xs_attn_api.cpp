@@ -1,6 +1,8 @@
 // xs_attn_api.cpp -- the C ABI declared in include/xs_attn.h: argument
 // validation (before any HIP call), dispatch to the kernel launchers.
+#include <hip/hip_runtime.h>
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "attn_launch.h"
@@ -8,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // |scale| * log2(e): the kernels compute p = 2^(s*c - m).  A zero scale is
@@ -38,6 +40,8 @@ int validate(const void* q, const void* k, const void* v, void* out, int B, int 
   // element counts must fit comfortably in 64-bit byte offsets
   const double elems = (double)B * (double)S * (double)H * (double)D;
   if (elems * 2.0 > 9.0e18) return XS_ERR_UNSUPPORTED;
+  // K/V rows of one (batch, head) are addressed with 32-bit buffer offsets
+  if ((double)S * H * D * (double)in_elem_bytes >= 4294967296.0) return XS_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return XS_ERR_ALIGN;
   const size_t n = (size_t)B * S * H * D;
   const size_t in_bytes = n * in_elem_bytes, out_bytes = n * 2;
@@ -57,6 +61,84 @@ int validate(const void* q, const void* k, const void* v, void* out, int B, int 
   args->neg = scale < 0.0f;
   args->c = scores_factor(scale);
   args->o_scale = 1.0f;
+  args->nsplit = 1;
+  args->nb_per = (S + xs::kBlockN - 1) / xs::kBlockN;
+  args->ws_o = nullptr;
+  args->ws_ml = nullptr;
+  return XS_OK;
+}
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
+// Split of the key range.  Model of the run time on `cus` compute units with
+// one workgroup resident per CU: ceil(items / cus) rounds, each as long as one
+// item (its key blocks plus about two blocks of prologue/epilogue work), plus,
+// when split, the extra HBM traffic of the fp32 partials (written once, read
+// once by the merge) and the merge launch.  Picks the cheapest nsplit <= 16.
+struct Plan {
+  int nsplit, nb_per;
+};
+Plan plan_split(long long ntiles, int nblk, long long rows, int D, int cus) {
+  const double t_block = D == 128 ? 1.9e-6 : 1.0e-6;  // s per 64-key block per workgroup
+  const double hbm = 4.0e12, t_launch = 5.0e-6;
+  auto cost = [&](int ns, int nbp) {
+    const double rounds = (double)((ntiles * ns + cus - 1) / cus);
+    double t = rounds * (nbp + 2) * t_block;
+    if (ns > 1) t += 2.0 * ns * (double)rows * (4.0 * D + 8.0) / hbm + t_launch;
+    return t;
+  };
+  Plan best{1, nblk};
+  double best_cost = cost(1, nblk);
+  for (int ns = 2; ns <= 16 && ns <= nblk; ++ns) {
+    const int nbp = (nblk + ns - 1) / ns;
+    if ((nblk + nbp - 1) / nbp != ns) continue;  // fewer splits would do: skip
+    const double c = cost(ns, nbp);
+    if (c < 0.97 * best_cost) {
+      best_cost = c;
+      best = Plan{ns, nbp};
+    }
+  }
+  return best;
+}
+
+Plan plan_for(int B, int S, int H, int D) {
+  const long long ntiles = (long long)B * H * ((S + xs::kBlockM - 1) / xs::kBlockM);
+  const int nblk = (S + xs::kBlockN - 1) / xs::kBlockN;
+  return plan_split(ntiles, nblk, (long long)B * H * S, D, device_cus());
+}
+
+size_t workspace_bytes(const Plan& pl, int B, int S, int H, int D) {
+  if (pl.nsplit <= 1) return 0;
+  const size_t rows = (size_t)B * S * H;
+  return (size_t)pl.nsplit * rows * ((size_t)D * 4 + 8);
+}
+
+// Attaches the split plan and workspace to validated arguments.
+int attach_workspace(xs::AttnArgs* a, void* ws, size_t ws_bytes) {
+  if (ws == nullptr) return XS_OK;  // no workspace: one item per tile
+  if (((uintptr_t)ws & 15u) != 0) return XS_ERR_ALIGN;
+  const Plan pl = plan_for(a->B, a->S, a->H, a->D);
+  const size_t need = workspace_bytes(pl, a->B, a->S, a->H, a->D);
+  if (need == 0) return XS_OK;
+  if (ws_bytes < need) return XS_ERR_WORKSPACE;
+  const size_t rows = (size_t)a->B * a->S * a->H;
+  a->nsplit = pl.nsplit;
+  a->nb_per = pl.nb_per;
+  a->ws_o = (float*)ws;
+  a->ws_ml = (float*)((char*)ws + (size_t)pl.nsplit * rows * a->D * 4);
+  return XS_OK;
+}
+
+int launch(const xs::AttnArgs& a, bool fp8, hipStream_t stream) {
+  const hipError_t e = fp8 ? xs::launch_attn_fp8(a, stream) : xs::launch_attn_bf16(a, stream);
+  if (e != hipSuccess) return XS_ERR_LAUNCH;
+  if (a.nsplit > 1 && xs::launch_attn_combine(a, stream) != hipSuccess) return XS_ERR_LAUNCH;
   return XS_OK;
 }
 
@@ -64,18 +146,26 @@ int validate(const void* q, const void* k, const void* v, void* out, int B, int 
 
 extern "C" {
 
-int xs_attn_fwd(const void* q, const void* k, const void* v, void* out_packed, int B, int S,
-                int H_local, int D, int P, float scale, void* stream) {
+int xs_attn_fwd_ws(const void* q, const void* k, const void* v, void* out_packed, int B, int S,
+                   int H_local, int D, int P, float scale, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   xs::AttnArgs a;
   int rc = validate(q, k, v, out_packed, B, S, H_local, D, P, scale, 2, &a);
   if (rc != XS_OK) return rc;
-  if (xs::launch_attn_bf16(a, (hipStream_t)stream) != hipSuccess) return XS_ERR_LAUNCH;
-  return XS_OK;
+  rc = attach_workspace(&a, workspace, workspace_bytes);
+  if (rc != XS_OK) return rc;
+  return launch(a, false, (hipStream_t)stream);
 }
 
-int xs_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale,
-                    float k_descale, float v_descale, void* out_packed, int B, int S, int H_local,
-                    int D, int P, float scale, void* stream) {
+int xs_attn_fwd(const void* q, const void* k, const void* v, void* out_packed, int B, int S,
+                int H_local, int D, int P, float scale, void* stream) {
+  return xs_attn_fwd_ws(q, k, v, out_packed, B, S, H_local, D, P, scale, nullptr, 0, stream);
+}
+
+int xs_attn_fwd_fp8_ws(const void* q8, const void* k8, const void* v8, float q_descale,
+                       float k_descale, float v_descale, void* out_packed, int B, int S,
+                       int H_local, int D, int P, float scale, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   xs::AttnArgs a;
   int rc = validate(q8, k8, v8, out_packed, B, S, H_local, D, P, scale, 1, &a);
   if (rc != XS_OK) return rc;
@@ -88,8 +178,26 @@ int xs_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_desc
   a.neg = qk < 0.0f;
   a.c = scores_factor(qk);
   a.o_scale = v_descale;
-  if (xs::launch_attn_fp8(a, (hipStream_t)stream) != hipSuccess) return XS_ERR_LAUNCH;
-  return XS_OK;
+  rc = attach_workspace(&a, workspace, workspace_bytes);
+  if (rc != XS_OK) return rc;
+  return launch(a, true, (hipStream_t)stream);
+}
+
+int xs_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale,
+                    float k_descale, float v_descale, void* out_packed, int B, int S, int H_local,
+                    int D, int P, float scale, void* stream) {
+  return xs_attn_fwd_fp8_ws(q8, k8, v8, q_descale, k_descale, v_descale, out_packed, B, S,
+                            H_local, D, P, scale, nullptr, 0, stream);
+}
+
+size_t xs_attn_workspace_size(int B, int S, int H_local, int D) {
+  if (B < 1 || S < 1 || H_local < 1 || (D != 64 && D != 128)) return 0;
+  return workspace_bytes(plan_for(B, S, H_local, D), B, S, H_local, D);
+}
+
+int xs_attn_split_count(int B, int S, int H_local, int D) {
+  if (B < 1 || S < 1 || H_local < 1 || (D != 64 && D != 128)) return 0;
+  return plan_for(B, S, H_local, D).nsplit;
 }
 
 const char* xs_attn_strerror(int status) {
@@ -108,6 +216,8 @@ const char* xs_attn_strerror(int status) {
       return "the HIP kernel launch failed";
     case XS_ERR_OVERLAP:
       return "out_packed overlaps q, k or v";
+    case XS_ERR_WORKSPACE:
+      return "workspace smaller than xs_attn_workspace_size()";
     default:
       return "unknown status code";
   }

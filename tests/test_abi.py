@@ -11,6 +11,7 @@ from sequence_attention_amd import _lib
 
 XS_OK, XS_ERR_NULL, XS_ERR_SHAPE, XS_ERR_UNSUPPORTED, XS_ERR_ALIGN, XS_ERR_LAUNCH, XS_ERR_OVERLAP = (
     0, -1, -2, -3, -4, -5, -6)
+XS_ERR_WORKSPACE = -7
 
 # distinct, 16-byte aligned, far-apart fake device addresses (never dereferenced)
 Q, K, V, O = 0x10000000, 0x20000000, 0x30000000, 0x40000000
@@ -18,7 +19,9 @@ Q, K, V, O = 0x10000000, 0x20000000, 0x30000000, 0x40000000
 
 def test_library_exports_every_declared_function():
     names = _lib.declared_functions()
-    assert set(names) == {"xs_attn_fwd", "xs_attn_fwd_fp8", "xs_attn_strerror", "xs_attn_version"}
+    assert set(names) == {"xs_attn_fwd", "xs_attn_fwd_fp8", "xs_attn_fwd_ws", "xs_attn_fwd_fp8_ws",
+                          "xs_attn_workspace_size", "xs_attn_split_count", "xs_attn_strerror",
+                          "xs_attn_version"}
     L = _lib.lib()
     for n in names:
         assert getattr(L, n) is not None
@@ -29,9 +32,9 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert xs.xs_attn_version() == 10000
+    assert xs.xs_attn_version() == 10100
     for code in (XS_OK, XS_ERR_NULL, XS_ERR_SHAPE, XS_ERR_UNSUPPORTED, XS_ERR_ALIGN, XS_ERR_LAUNCH,
-                 XS_ERR_OVERLAP, 12345):
+                 XS_ERR_OVERLAP, XS_ERR_WORKSPACE, 12345):
         s = xs.xs_attn_strerror(code)
         assert isinstance(s, str) and s
     assert xs.xs_attn_strerror(12345) == "unknown status code"
@@ -102,3 +105,38 @@ def test_strerror_returns_static_c_strings():
     b = L.xs_attn_strerror(XS_ERR_SHAPE)
     assert a == b and isinstance(a, bytes)
     assert isinstance(ctypes.c_char_p(a).value, bytes)
+
+
+def test_rows_of_one_batch_beyond_4gib_are_unsupported():
+    # S * H * D * 2 bytes >= 4 GiB cannot be addressed with 32-bit buffer offsets
+    assert _fwd(S=2 ** 24, H=1024, D=128, P=1) == XS_ERR_UNSUPPORTED
+
+
+def _fwd_ws(ws, nbytes, **kw):
+    a = dict(q=Q, k=K, v=V, out=O, B=1, S=4608, H=3, D=128, P=8, scale=0.088)
+    a.update(kw)
+    return xs.xs_attn_fwd_ws(a["q"], a["k"], a["v"], a["out"], a["B"], a["S"], a["H"], a["D"],
+                             a["P"], a["scale"], ws, nbytes, None)
+
+
+def test_split_plan_fills_the_grid():
+    # 256 compute units (what the plan assumes when no GPU is visible), 256-row
+    # tiles, 64-key blocks: cost = ceil(items / 256) rounds x blocks per item
+    assert xs.split_count(1, 32768, 5, 128) == 2    # 640 tiles: 2.5 rounds -> 5 exact rounds
+    assert xs.split_count(1, 131072, 3, 128) == 1   # 1536 tiles: 6 exact rounds
+    assert xs.split_count(2, 32768, 4, 128) == 1    # 1024 tiles: 4 exact rounds
+    assert xs.split_count(1, 4608, 3, 128) == 4     # 54 tiles: one round of 216 items
+    assert xs.split_count(0, 4608, 3, 128) == 0
+    n = xs.workspace_size(1, 32768, 5, 128)
+    assert n == 2 * 32768 * 5 * (128 * 4 + 8)
+    assert xs.workspace_size(1, 131072, 3, 128) == 0
+    assert xs.workspace_size(1, 4608, 3, 96) == 0
+
+
+def test_workspace_errors_before_any_launch():
+    need = xs.workspace_size(1, 4608, 3, 128)
+    assert need > 0
+    W = 0x50000000
+    assert _fwd_ws(W + 8, need) == XS_ERR_ALIGN
+    assert _fwd_ws(W, need - 16) == XS_ERR_WORKSPACE
+    assert _fwd_ws(W, need, D=96) == XS_ERR_UNSUPPORTED

@@ -359,3 +359,48 @@ def test_fp8_canaries_and_full_write(gpu):
     assert torch.all(big[:pad] == 5.0) and torch.all(big[pad + n:] == -9.0)
     ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, inp["scale"], inp["descales"])
     assert_gate(f64(out), ref, "fp8", "fp8 canary case")
+
+
+# ------------------------------------------------------------------ split-key schedule
+def test_split_and_unsplit_agree_with_the_oracle(gpu):
+    # the image share: 54 tiles of 256 rows on a 256-CU GPU -> the key range is split
+    w = workloads.WORKLOADS["image"]
+    inp = workloads.make_inputs(w)
+    assert xs.split_count(w.B, w.S, w.H, w.D) > 1
+    q, k, v = to_gpu(inp, gpu)
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], w.P, inp["scale"])
+    _say("image split vs unsplit")
+    split = xs.fwd(q, k, v, w.P, inp["scale"])
+    whole = xs.fwd(q, k, v, w.P, inp["scale"], workspace=None)
+    torch.cuda.synchronize()
+    assert_gate(f64(split), ref, "bf16", "image split")
+    assert_gate(f64(whole), ref, "bf16", "image unsplit")
+    assert float((split.float() - whole.float()).abs().max()) <= 2e-3
+
+
+def test_split_fp8_agrees_with_the_oracle(gpu):
+    w = workloads.custom(1, 4608, 3, 128, 8, dtype="fp8", index=4400)
+    inp = workloads.make_inputs(w)
+    assert xs.split_count(w.B, w.S, w.H, w.D) > 1
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], w.P, inp["scale"], inp["descales"])
+    out = run(inp, w.P, gpu)
+    assert_gate(f64(out), ref, "fp8", "fp8 split")
+
+
+def test_explicit_workspace_reused_twice(gpu):
+    w = workloads.custom(2, 1000, 3, 64, 8, index=4500)
+    inp = workloads.make_inputs(w)
+    q, k, v = to_gpu(inp, gpu)
+    n = xs.workspace_size(2, 1000, 3, 64)
+    assert n > 0
+    ws = torch.full((n,), 255, dtype=torch.uint8, device=gpu)  # stale contents must not matter
+    _say("explicit workspace")
+    a = xs.fwd(q, k, v, 8, workspace=ws)
+    b = xs.fwd(q, k, v, 8, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], 8, inp["scale"])
+    assert_gate(f64(a), ref, "bf16", "explicit workspace")
+    small = torch.empty(n - 16, dtype=torch.uint8, device=gpu)
+    with pytest.raises(xs.XsAttnError):
+        xs.fwd(q, k, v, 8, workspace=small)
