@@ -69,6 +69,25 @@ struct Bf16Cfg {
   static_assert(LOADS % NW == 0 && LOADS >= NW, "tile loads must split evenly over waves");
 };
 
+#ifndef XS_VSWZ
+#define XS_VSWZ 1
+#endif
+
+// XOR swizzle of the 16-byte chunk index of V row `row`.  A ds_read_b64_tr_b16
+// of a V^T fragment touches 8 rows x 4 chunks and is served one half-wave at a
+// time (4 rows x 4 chunks = 256 bytes): XOR-ing the chunk with 4*(row%4) (D=128,
+// one row per 256-byte bank line) or 4*((row/2)%2) (D=64, two rows per line)
+// puts the 16 chunks of each half-wave on 16 different bank groups.
+template <class C>
+__device__ __forceinline__ int vswz(int row) {
+#if XS_VSWZ == 0
+  return (2 * row) & (C::CH - 1);
+#else
+  constexpr int RPL = 256 / C::ROWB;  // rows per 256-byte bank line
+  return 4 * ((row / RPL) & (C::CH / 4 - 1));
+#endif
+}
+
 // Per-lane byte offsets (relative to the block's first key row) of the
 // 16-byte chunks this lane moves for one K (SWZ_V = false) or V (SWZ_V = true)
 // tile: LDS chunk position pos holds global chunk (pos % CH) ^ swizzle(row).
@@ -79,7 +98,7 @@ __device__ __forceinline__ void tile_offsets(uint32_t row_stride, int wave, int 
   for (int i = 0; i < C::LPW; ++i) {
     const int pos = (wave * C::LPW + i) * 64 + lane;
     const int row = pos / C::CH;
-    const int swz = SWZ_V ? ((2 * row) & (C::CH - 1)) : (row & (C::CH - 1));
+    const int swz = SWZ_V ? vswz<C>(row) : (row & (C::CH - 1));
     const int chunk = (pos % C::CH) ^ swz;
     voff[i] = (uint32_t)row * row_stride + (uint32_t)chunk * 16u;
   }
@@ -152,7 +171,7 @@ __device__ __forceinline__ void pv_block(Bf16State<C>& st, const uint8_t XS_LDS*
   const int ln = opaque(lane);
   const int g = ln >> 4, L = ln & 15;
   const int vrow = 4 * (g >> 1) + (L >> 2);  // row within an 8-row group
-  const int vsw = (2 * vrow) & (CH - 1);
+  const int vsw = vswz<C>(vrow);  // rows of a fragment differ from vrow by multiples of 8
   const uint8_t XS_LDS* vbase = sV + vrow * ROWB + 8 * (L & 1);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
@@ -216,6 +235,17 @@ __device__ __forceinline__ void softmax_max(Bf16State<C>& st, const Scores<C>& s
 
 // ---- step-1 VALU work: p = 2^(s c - m) -> bf16 P^T fragments, row sums
 template <class C>
+__device__ __forceinline__ void keep_probs(const Bf16State<C>& st) {
+#pragma unroll
+  for (int qt = 0; qt < C::QT; ++qt)
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      keep(st.pb[qt][nt][0]);
+      keep(st.pb[qt][nt][1]);
+    }
+}
+
+template <class C>
 __device__ __forceinline__ void softmax_exp(Bf16State<C>& st, const Scores<C>& sc, float c) {
   constexpr int QT = C::QT, NT = C::NT;
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
@@ -241,15 +271,168 @@ __device__ __forceinline__ void softmax_exp(Bf16State<C>& st, const Scores<C>& s
   }
 }
 
-// Scheduling pattern for one step: N groups of one MFMA, DS LDS reads and V
-// VALU instructions, so the wave issues vector work between matrix ops.
-template <int N, int V, int DS>
-__device__ __forceinline__ void interleave() {
+#ifndef XS_LEAD
+#define XS_LEAD 3
+#endif
+
+// ---- The two steps of the software pipeline, written as fixed sequences of
+// micro-steps separated by scheduling barriers: each micro-step reads the LDS
+// fragment LEAD positions ahead, issues the MFMA that uses the fragment read
+// LEAD micro-steps earlier, and does a slice of the softmax work, so LDS
+// latency and vector work hide under the matrix core.  The exponentials of a
+// block are split between the two steps (keys 0-31 under the next block's
+// QK^T, keys 32-63 under the first half of this block's P V) so that neither
+// step is bound by the vector ALU.  LDS addresses are per-lane offsets
+// computed once plus immediates (the double-buffer stage is a template
+// argument: splits start on even blocks).
+
+// Per-lane LDS byte offsets of the fragments, relative to a tile's start.
+template <class C>
+struct LdsOffs {
+  uint32_t k[C::KS];  // K fragment of k-step ks (row lane%32, chunk 2ks + lane/32)
+  uint32_t v[C::DT];  // first V^T transpose read of d-tile dt (rows 0..7 group)
+};
+
+template <class C>
+__device__ __forceinline__ LdsOffs<C> lds_offsets(int lane) {
+  LdsOffs<C> o;
+  const int hi = lane >> 5, ksw = lane & (C::CH - 1);
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
-    if (DS) __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);      // DS read
-    if (V) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);        // VALU
+  for (int ks = 0; ks < C::KS; ++ks)
+    o.k[ks] = (uint32_t)((lane & 31) * C::ROWB + (((2 * ks + hi) ^ ksw) << 4));
+  const int g = lane >> 4, L = lane & 15;
+  const int vrow = 4 * (g >> 1) + (L >> 2);
+  const int vsw = vswz<C>(vrow);  // rows of a fragment differ from vrow by multiples of 8
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+    const int chunk = (dt * 4 + 2 * (g & 1) + ((L & 3) >> 1)) ^ vsw;
+    o.v[dt] = (uint32_t)(vrow * C::ROWB + 8 * (L & 1) + (chunk << 4));
+  }
+  return o;
+}
+
+// exp2(s c - m) of score pair e (0..15) of 32-key tile nt, packed to bf16,
+// added to the row sum; pinned to the current micro-step.
+template <class C>
+__device__ __forceinline__ void exp_pair(Bf16State<C>& st, const Scores<C>& cur, int nt, int e,
+                                         float c, float neg_m, float& lsum, uint32_t (&w)[8]) {
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  const float p0 = fast_exp2(__builtin_fmaf(cur.s[nt][0][2 * e], c, neg_m));
+  const float p1 = fast_exp2(__builtin_fmaf(cur.s[nt][0][2 * e + 1], c, neg_m));
+  uint32_t pk = pack_bf16(p0, p1);
+  lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, lsum, false);
+  pin(pk);
+  pin(lsum);
+  w[e] = pk;
+}
+
+// Step 1: S^T of the next block from K stage KST || probabilities of keys 0..31
+// of the current block.
+template <class C, int KST>
+__device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16State<C>& st,
+                                      const uint8_t XS_LDS* lds, const LdsOffs<C>& off, float c) {
+  static_assert(C::QT == 1 && C::NT == 2, "pipeline written for 32-row waves, 64-key blocks");
+  constexpr int NT = C::NT, KS = C::KS, ROWB = C::ROWB;
+  constexpr int NF = KS * NT;
+  constexpr int LEAD = XS_LEAD < NF ? XS_LEAD : NF;
+  constexpr int R = LEAD + 1;
+  const uint8_t XS_LDS* kb = lds + KST * C::TILE;
+  auto kread = [&](int f) { return lds_read_b128(kb + off.k[f / NT] + (f % NT) * 32 * ROWB); };
+  const float neg_m = -st.m[0];
+  float lsum = st.l[0];
+  uint32_t w[8];
+  u32x4 kf[R];
+#pragma unroll
+  for (int f = 0; f < LEAD; ++f) kf[f] = kread(f);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + LEAD < NF) kf[(f + LEAD) % R] = kread(f + LEAD);
+    const int ks = f / NT, nt = f % NT;
+    nxt.s[nt][0] = mfma_bf16(kf[f % R], st.qf[0][ks], ks == 0 ? f32x16{} : nxt.s[nt][0]);
+    // the 8 pairs of tile 0, spread evenly over the NF micro-steps
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e * NF / 8 == f) exp_pair<C>(st, cur, 0, e, c, neg_m, lsum, w);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l[0] = lsum;
+  st.pb[0][0][0] = u32x4{w[0], w[1], w[2], w[3]};
+  st.pb[0][0][1] = u32x4{w[4], w[5], w[6], w[7]};
+  keep(st.pb[0][0][0]);
+  keep(st.pb[0][0][1]);
+}
+
+// Step 2: O^T = alpha O^T + V^T P^T from V stage VST; under the first half
+// (keys 0..31) the probabilities of keys 32..63, under the second half the row
+// max of the next block (lazy move of the running max; the O rescale it may
+// ask for is applied at the start of the next step 2).
+template <class C, int VST>
+__device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, const Scores<C>& cur,
+                                      const uint8_t XS_LDS* lds, const LdsOffs<C>& off, float c) {
+  constexpr int NT = C::NT, DT = C::DT, ROWB = C::ROWB;
+  constexpr int NF = NT * 2 * DT;          // V fragments, keys 0..31 first
+  constexpr int HALF = NF / 2;
+  constexpr int LEAD = XS_LEAD < NF ? XS_LEAD : NF;
+  constexpr int R = LEAD + 1;
+  if (st.rescale) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.o[0][dt] *= st.alpha[0];
+    st.alpha[0] = 1.0f;
+    st.rescale = false;
+  }
+  const uint8_t XS_LDS* vb = lds + (2 + VST) * C::TILE;
+  auto vaddr = [&](int f) {
+    const int nt = f / (2 * DT), h = (f / DT) % 2, dt = f % DT;
+    return vb + off.v[dt] + (nt * 32 + 16 * h) * ROWB;
+  };
+  const float neg_m = -st.m[0];
+  float lsum = st.l[0];
+  uint32_t w[8];
+  float mx = nxt.s[0][0][0];
+  u32x2 vlo[R], vhi[R];
+#pragma unroll
+  for (int f = 0; f < LEAD; ++f) {
+    vlo[f] = lds_read_tr16(vaddr(f));
+    vhi[f] = lds_read_tr16(vaddr(f) + 8 * ROWB);
+  }
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + LEAD < NF) {
+      vlo[(f + LEAD) % R] = lds_read_tr16(vaddr(f + LEAD));
+      vhi[(f + LEAD) % R] = lds_read_tr16(vaddr(f + LEAD) + 8 * ROWB);
+    }
+    if (f == HALF) {
+      // probabilities of keys 32..63 complete: assemble their operands
+      st.pb[0][1][0] = u32x4{w[0], w[1], w[2], w[3]};
+      st.pb[0][1][1] = u32x4{w[4], w[5], w[6], w[7]};
+    }
+    const int nt = f / (2 * DT), h = (f / DT) % 2, dt = f % DT;
+    const u32x4 vf = u32x4{vlo[f % R][0], vlo[f % R][1], vhi[f % R][0], vhi[f % R][1]};
+    st.o[0][dt] = mfma_bf16(vf, st.pb[0][nt][h], st.o[0][dt]);
+    if (f < HALF) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e * HALF / 8 == f) exp_pair<C>(st, cur, 1, e, c, neg_m, lsum, w);
+    } else {
+      constexpr int EPS = 32 / HALF;  // max over the 32 scores of the next block
+#pragma unroll
+      for (int ee = 0; ee < EPS; ++ee) {
+        const int e = (f - HALF) * EPS + ee;
+        mx = fmaxf(mx, nxt.s[e / 16][0][e % 16]);
+      }
+      pin(mx);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l[0] = lsum;
+  const float mnew = max_halves(mx) * c;
+  const bool need = mnew > st.m[0] + C::TAU;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float a = need ? fast_exp2(st.m[0] - mnew) : 1.0f;
+    st.m[0] = need ? mnew : st.m[0];
+    st.l[0] *= a;
+    st.alpha[0] *= a;
+    st.rescale = true;
   }
 }
 
@@ -325,35 +508,27 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a
   // Steady state, two blocks per trip so the score buffers swap statically.
   // Entering a step for block i: scores of block i are in one buffer with
   // their max taken; K_{i+1} and V_i are loaded (or in flight).
+  // (jb is even: K_i and V_i live in stage i % 2)
+  const LdsOffs<C> off = lds_offsets<C>(lane);
   int j = jb;
   for (; j + 2 < je; j += 2) {
     // ---- block j (scores in sa), next block's scores into sb
     wait_vmcnt<0>();
     __syncthreads();
-    load_tile<C>(kbase, row_stride, (j + 2) * BN, S, kbuf(j), koff, wave);
-    load_tile<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(j + 1), voff, wave);
-    qk_block<C>(sb, st, kbuf(j + 1), lane);
-    softmax_exp<C>(st, sa, c);
-    interleave<C::NT * 16, 6, 1>();
-    __builtin_amdgcn_sched_barrier(0);
+    load_tile<C>(kbase, row_stride, (j + 2) * BN, S, kbuf(0), koff, wave);
+    load_tile<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(1), voff, wave);
+    step1<C, 1>(sb, sa, st, lds, off, c);
     if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
-    pv_block<C>(st, vbuf(j), lane);
-    softmax_max<C>(st, sb, c);
-    __builtin_amdgcn_sched_barrier(0);
+    step2<C, 0>(st, sb, sa, lds, off, c);
 
     // ---- block j+1 (scores in sb), next block's scores into sa
     wait_vmcnt<0>();
     __syncthreads();
-    if (j + 3 < je) load_tile<C>(kbase, row_stride, (j + 3) * BN, S, kbuf(j + 1), koff, wave);
-    load_tile<C>(vbase, row_stride, (j + 2) * BN, S, vbuf(j + 2), voff, wave);
-    qk_block<C>(sa, st, kbuf(j + 2), lane);
-    softmax_exp<C>(st, sb, c);
-    interleave<C::NT * 16, 6, 1>();
-    __builtin_amdgcn_sched_barrier(0);
+    if (j + 3 < je) load_tile<C>(kbase, row_stride, (j + 3) * BN, S, kbuf(1), koff, wave);
+    load_tile<C>(vbase, row_stride, (j + 2) * BN, S, vbuf(0), voff, wave);
+    step1<C, 0>(sa, sb, st, lds, off, c);
     if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
-    pv_block<C>(st, vbuf(j + 1), lane);
-    softmax_max<C>(st, sa, c);
-    __builtin_amdgcn_sched_barrier(0);
+    step2<C, 1>(st, sa, sb, lds, off, c);
   }
   // the last one or two blocks (scores of block j in sa)
   if (j + 1 < je) {

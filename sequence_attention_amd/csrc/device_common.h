@@ -123,6 +123,19 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Marks x as used here: keeps the optimiser from sinking the instructions that
+// compute x past this point (into a later block of the software pipeline).
+template <class T>
+__device__ __forceinline__ void keep(const T& x) {
+  asm volatile("" : : "v"(x));
+}
+
+// Pins the computation of x to this point of the instruction stream: x must be
+// complete here and is opaque afterwards.  Used to place slices of the vector
+// work between the matrix instructions of a software-pipelined step.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
 // Returns x unchanged but opaque to the optimiser, so address arithmetic that
 // depends on it is recomputed where it is used instead of being hoisted out of
 // the loop and kept live (or spilled) across the whole kernel.

@@ -96,7 +96,9 @@ Plan plan_split(long long ntiles, int nblk, long long rows, int D, int cus) {
   Plan best{1, nblk};
   double best_cost = cost(1, nblk);
   for (int ns = 2; ns <= 16 && ns <= nblk; ++ns) {
-    const int nbp = (nblk + ns - 1) / ns;
+    // an even number of blocks per split, so every split starts on an even
+    // block and the kernels' double-buffer stages have fixed parity
+    const int nbp = ((nblk + ns - 1) / ns + 1) & ~1;
     if ((nblk + nbp - 1) / nbp != ns) continue;  // fewer splits would do: skip
     const double c = cost(ns, nbp);
     if (c < 0.97 * best_cost) {
