@@ -189,7 +189,8 @@ def main():
                      "frac": round(achieved / peak, 4),
                      "traffic": recorded_traffic(
                          "attn_fwd_bf16" if w.dtype == "bf16" else "attn_fwd_fp8", w.name),
-                     "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_fp8_kernel",
+                     "kernel": ("attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_fp8_kernel")
+                               + (" + attn_combine_kernel" if nsplit > 1 else ""),
                      "flops_per_launch": flops},
         "check": check,
     }

@@ -8,13 +8,12 @@
 // the post-attention All-to-All delivers, then moves on -- there is no separate
 // communication wave and no separate relayout pass.
 //
-// Design (one workgroup = 4 waves, one per SIMD; a wave owns QW = 64 query
-// rows as two 32-row sub-tiles; BM = 256 rows of one (b, h) per workgroup):
+// Design (one workgroup = 8 waves, two per SIMD; a wave owns 32 query rows;
+// BM = 256 rows of one (b, h) per workgroup, one workgroup per CU):
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    each lane then owns one query column and 16 keys of every 32x32 score
 //    tile, so the row max and row sum are lane-local except for one
-//    permlane32 swap between the two half-waves.  Each K fragment read from
-//    LDS feeds both sub-tiles, which halves LDS traffic against 32-row waves.
+//    permlane32 swap between the two half-waves.
 //  * The transposed probabilities P^T leave the accumulator already in the
 //    B-operand layout of O^T += V^T P^T (the key order inside a k-step is
 //    permuted identically on both operands), so P never goes through LDS.
@@ -23,8 +22,9 @@
 //    swizzled for conflict-free ds_read_b128 of the A operand; V rows are
 //    swizzled for ds_read_b64_tr_b16, which delivers V^T fragments directly.
 //  * Software pipeline inside the wave, one barrier per block:
-//      step 1: QK^T of block j+1 (MFMA)  ||  exp/sum/convert of block j (VALU)
-//      step 2: P V of block j (MFMA)     ||  row max of block j+1 (VALU)
+//      step 1: QK^T of block j+1 (MFMA)  ||  exp/sum/convert of keys 0-31 of block j
+//      step 2: P V of block j (MFMA)     ||  exp/sum/convert of keys 32-63 of block j,
+//                                            then the row max of block j+1
 //    so the matrix core and the vector ALU work on different blocks at once.
 //  * Online softmax in base 2: p = 2^(s*c - m), c = scale*log2(e) folded into
 //    one FMA per score.  The running max is moved only when a block's max
@@ -437,7 +437,7 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, co
 }
 
 template <class C>
-__global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(C::THREADS, 8 / C::NW) void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int QT = C::QT, KS = C::KS, DT = C::DT, BM = C::BM, BN = C::BN;
   // K stage 0 | K stage 1 | V stage 0 | V stage 1
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];

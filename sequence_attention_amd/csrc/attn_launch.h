@@ -27,8 +27,15 @@ struct AttnArgs {
 };
 
 // Tile geometry shared by the bf16 and fp8 kernels and the host-side plan.
-constexpr int kBlockM = 256;  // query rows per workgroup
-constexpr int kBlockN = 64;   // keys per K/V block
+#ifndef XS_BM
+#define XS_BM 256
+#endif
+#ifndef XS_WGPC
+#define XS_WGPC 1
+#endif
+constexpr int kBlockM = XS_BM;         // query rows per workgroup
+constexpr int kBlockN = 64;            // keys per K/V block
+constexpr int kGroupsPerCU = XS_WGPC;  // workgroups resident per compute unit
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);
 

@@ -112,7 +112,7 @@ Plan plan_split(long long ntiles, int nblk, long long rows, int D, int cus) {
 Plan plan_for(int B, int S, int H, int D) {
   const long long ntiles = (long long)B * H * ((S + xs::kBlockM - 1) / xs::kBlockM);
   const int nblk = (S + xs::kBlockN - 1) / xs::kBlockN;
-  return plan_split(ntiles, nblk, (long long)B * H * S, D, device_cus());
+  return plan_split(ntiles, nblk, (long long)B * H * S, D, device_cus() * xs::kGroupsPerCU);
 }
 
 size_t workspace_bytes(const Plan& pl, int B, int S, int H, int D) {
