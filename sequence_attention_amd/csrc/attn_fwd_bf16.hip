@@ -311,36 +311,41 @@ __device__ __forceinline__ LdsOffs<C> lds_offsets(int lane) {
   return o;
 }
 
-// exp2(s c - m) of score pair e (0..15) of 32-key tile nt, packed to bf16,
-// added to the row sum; pinned to the current micro-step.
+// exp2(s c - m) of score pair e (0..7) of 32-key tile nt, query sub-tile qt,
+// packed to bf16, added to the row sum; pinned to the current micro-step.
 template <class C>
-__device__ __forceinline__ void exp_pair(Bf16State<C>& st, const Scores<C>& cur, int nt, int e,
-                                         float c, float neg_m, float& lsum, uint32_t (&w)[8]) {
+__device__ __forceinline__ void exp_pair(const Scores<C>& cur, int qt, int nt, int e, float c,
+                                         float neg_m, float& lsum, uint32_t& w) {
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  const float p0 = fast_exp2(__builtin_fmaf(cur.s[nt][0][2 * e], c, neg_m));
-  const float p1 = fast_exp2(__builtin_fmaf(cur.s[nt][0][2 * e + 1], c, neg_m));
+  const float p0 = fast_exp2(__builtin_fmaf(cur.s[nt][qt][2 * e], c, neg_m));
+  const float p1 = fast_exp2(__builtin_fmaf(cur.s[nt][qt][2 * e + 1], c, neg_m));
   uint32_t pk = pack_bf16(p0, p1);
   lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, lsum, false);
   pin(pk);
   pin(lsum);
-  w[e] = pk;
+  w = pk;
 }
 
 // Step 1: S^T of the next block from K stage KST || probabilities of keys 0..31
-// of the current block.
+// of the current block.  Each K fragment feeds the QT query sub-tiles.
 template <class C, int KST>
 __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16State<C>& st,
                                       const uint8_t XS_LDS* lds, const LdsOffs<C>& off, float c) {
-  static_assert(C::QT == 1 && C::NT == 2, "pipeline written for 32-row waves, 64-key blocks");
-  constexpr int NT = C::NT, KS = C::KS, ROWB = C::ROWB;
+  static_assert(C::NT == 2, "pipeline written for 64-key blocks");
+  constexpr int QT = C::QT, NT = C::NT, KS = C::KS, ROWB = C::ROWB;
   constexpr int NF = KS * NT;
   constexpr int LEAD = XS_LEAD < NF ? XS_LEAD : NF;
   constexpr int R = LEAD + 1;
+  constexpr int NE = 8 * QT;  // score pairs of keys 0..31, all sub-tiles
   const uint8_t XS_LDS* kb = lds + KST * C::TILE;
   auto kread = [&](int f) { return lds_read_b128(kb + off.k[f / NT] + (f % NT) * 32 * ROWB); };
-  const float neg_m = -st.m[0];
-  float lsum = st.l[0];
-  uint32_t w[8];
+  float neg_m[QT], lsum[QT];
+  uint32_t w[QT][8];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    neg_m[qt] = -st.m[qt];
+    lsum[qt] = st.l[qt];
+  }
   u32x4 kf[R];
 #pragma unroll
   for (int f = 0; f < LEAD; ++f) kf[f] = kread(f);
@@ -348,18 +353,23 @@ __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16
   for (int f = 0; f < NF; ++f) {
     if (f + LEAD < NF) kf[(f + LEAD) % R] = kread(f + LEAD);
     const int ks = f / NT, nt = f % NT;
-    nxt.s[nt][0] = mfma_bf16(kf[f % R], st.qf[0][ks], ks == 0 ? f32x16{} : nxt.s[nt][0]);
-    // the 8 pairs of tile 0, spread evenly over the NF micro-steps
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (e * NF / 8 == f) exp_pair<C>(st, cur, 0, e, c, neg_m, lsum, w);
+    for (int qt = 0; qt < QT; ++qt)
+      nxt.s[nt][qt] = mfma_bf16(kf[f % R], st.qf[qt][ks], ks == 0 ? f32x16{} : nxt.s[nt][qt]);
+    // the score pairs of tile 0, spread evenly over the NF micro-steps
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      if (e * NF / NE == f) exp_pair<C>(cur, e / 8, 0, e % 8, c, neg_m[e / 8], lsum[e / 8], w[e / 8][e % 8]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  st.l[0] = lsum;
-  st.pb[0][0][0] = u32x4{w[0], w[1], w[2], w[3]};
-  st.pb[0][0][1] = u32x4{w[4], w[5], w[6], w[7]};
-  keep(st.pb[0][0][0]);
-  keep(st.pb[0][0][1]);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    st.l[qt] = lsum[qt];
+    st.pb[qt][0][0] = u32x4{w[qt][0], w[qt][1], w[qt][2], w[qt][3]};
+    st.pb[qt][0][1] = u32x4{w[qt][4], w[qt][5], w[qt][6], w[qt][7]};
+    keep(st.pb[qt][0][0]);
+    keep(st.pb[qt][0][1]);
+  }
 }
 
 // Step 2: O^T = alpha O^T + V^T P^T from V stage VST; under the first half
@@ -369,15 +379,20 @@ __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16
 template <class C, int VST>
 __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, const Scores<C>& cur,
                                       const uint8_t XS_LDS* lds, const LdsOffs<C>& off, float c) {
-  constexpr int NT = C::NT, DT = C::DT, ROWB = C::ROWB;
+  constexpr int QT = C::QT, NT = C::NT, DT = C::DT, ROWB = C::ROWB;
   constexpr int NF = NT * 2 * DT;          // V fragments, keys 0..31 first
   constexpr int HALF = NF / 2;
   constexpr int LEAD = XS_LEAD < NF ? XS_LEAD : NF;
   constexpr int R = LEAD + 1;
+  constexpr int NE = 8 * QT;               // score pairs of keys 32..63
+  constexpr int NM = 32 * QT;              // scores of the next block per lane
   if (st.rescale) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st.o[0][dt] *= st.alpha[0];
-    st.alpha[0] = 1.0f;
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) st.o[qt][dt] *= st.alpha[qt];
+      st.alpha[qt] = 1.0f;
+    }
     st.rescale = false;
   }
   const uint8_t XS_LDS* vb = lds + (2 + VST) * C::TILE;
@@ -385,10 +400,14 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, co
     const int nt = f / (2 * DT), h = (f / DT) % 2, dt = f % DT;
     return vb + off.v[dt] + (nt * 32 + 16 * h) * ROWB;
   };
-  const float neg_m = -st.m[0];
-  float lsum = st.l[0];
-  uint32_t w[8];
-  float mx = nxt.s[0][0][0];
+  float neg_m[QT], lsum[QT], mx[QT];
+  uint32_t w[QT][8];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    neg_m[qt] = -st.m[qt];
+    lsum[qt] = st.l[qt];
+    mx[qt] = nxt.s[0][qt][0];
+  }
   u32x2 vlo[R], vhi[R];
 #pragma unroll
   for (int f = 0; f < LEAD; ++f) {
@@ -403,41 +422,57 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, co
     }
     if (f == HALF) {
       // probabilities of keys 32..63 complete: assemble their operands
-      st.pb[0][1][0] = u32x4{w[0], w[1], w[2], w[3]};
-      st.pb[0][1][1] = u32x4{w[4], w[5], w[6], w[7]};
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        st.pb[qt][1][0] = u32x4{w[qt][0], w[qt][1], w[qt][2], w[qt][3]};
+        st.pb[qt][1][1] = u32x4{w[qt][4], w[qt][5], w[qt][6], w[qt][7]};
+      }
     }
     const int nt = f / (2 * DT), h = (f / DT) % 2, dt = f % DT;
     const u32x4 vf = u32x4{vlo[f % R][0], vlo[f % R][1], vhi[f % R][0], vhi[f % R][1]};
-    st.o[0][dt] = mfma_bf16(vf, st.pb[0][nt][h], st.o[0][dt]);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma_bf16(vf, st.pb[qt][nt][h], st.o[qt][dt]);
     if (f < HALF) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e * HALF / 8 == f) exp_pair<C>(st, cur, 1, e, c, neg_m, lsum, w);
+      for (int e = 0; e < NE; ++e)
+        if (e * HALF / NE == f)
+          exp_pair<C>(cur, e / 8, 1, e % 8, c, neg_m[e / 8], lsum[e / 8], w[e / 8][e % 8]);
     } else {
-      constexpr int EPS = 32 / HALF;  // max over the 32 scores of the next block
+      constexpr int EPS = NM / HALF;  // max over the scores of the next block
 #pragma unroll
       for (int ee = 0; ee < EPS; ++ee) {
-        const int e = (f - HALF) * EPS + ee;
-        mx = fmaxf(mx, nxt.s[e / 16][0][e % 16]);
+        const int e = (f - HALF) * EPS + ee;  // 0 .. NM-1
+        const int qt = e / 32, r = e % 32;
+        mx[qt] = fmaxf(mx[qt], nxt.s[r / 16][qt][r % 16]);
       }
-      pin(mx);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) pin(mx[qt]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  st.l[0] = lsum;
-  const float mnew = max_halves(mx) * c;
-  const bool need = mnew > st.m[0] + C::TAU;
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    const float a = need ? fast_exp2(st.m[0] - mnew) : 1.0f;
-    st.m[0] = need ? mnew : st.m[0];
-    st.l[0] *= a;
-    st.alpha[0] *= a;
+  bool need[QT], any = false;
+  float mnew[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    st.l[qt] = lsum[qt];
+    mnew[qt] = max_halves(mx[qt]) * c;
+    need[qt] = mnew[qt] > st.m[qt] + C::TAU;
+    any |= need[qt];
+  }
+  if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float a = need[qt] ? fast_exp2(st.m[qt] - mnew[qt]) : 1.0f;
+      st.m[qt] = need[qt] ? mnew[qt] : st.m[qt];
+      st.l[qt] *= a;
+      st.alpha[qt] *= a;
+    }
     st.rescale = true;
   }
 }
 
 template <class C>
-__global__ __launch_bounds__(C::THREADS, 8 / C::NW) void attn_fwd_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int QT = C::QT, KS = C::KS, DT = C::DT, BM = C::BM, BN = C::BN;
   // K stage 0 | K stage 1 | V stage 0 | V stage 1
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];

@@ -2,12 +2,12 @@
 // with per-tensor descales, fp32 accumulation and bf16 output, fused with the
 // destination-ordered epilogue; gfx950.
 //
-// Same operation and schedule as the bf16 kernel (X-Stage paper, catalyzex.com
-// abstract; gist.science explainer, "Zentrale Beitraege", "FlashAttention-A2A
+// Same operation as the bf16 kernel (X-Stage paper, catalyzex.com abstract;
+// gist.science explainer, "Zentrale Beitraege", "FlashAttention-A2A
 // (Piggybacking)"): per workgroup 8 waves x 32 query rows of one (b, h), K/V
-// blocks of 64 keys double buffered in LDS via direct-to-LDS loads, QK^T of
-// block j+1 overlapped with the softmax of block j inside each wave.  What
-// differs for 8-bit operands:
+// blocks of 64 keys double buffered in LDS via direct-to-LDS loads, a software
+// pipeline of pinned micro-steps inside each wave.  What differs for 8-bit
+// operands:
 //  * Both contractions use v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3 -> fp32):
 //    S^T = K Q^T takes D/64 k-steps; O^T += V^T P^T takes one k-step of all 64
 //    keys of the block per 32-row d tile.
@@ -76,7 +76,7 @@ template <class C>
 struct Fp8State {
   f32x16 o[C::DT];
   i32x8 qf[C::KS];
-  i32x8 pf;          // P^T operand: e4m3 probabilities of the 64 keys
+  u32x4 p0, p1;      // P^T operand: e4m3 probabilities of keys 0..31 and 32..63
   float m, l, alpha;
   bool rescale;
 };
@@ -99,31 +99,6 @@ __device__ __forceinline__ void qk_block8(Scores8<C>& sc, const Fp8State<C>& st,
       const i32x8 kf = __builtin_bit_cast(i32x8, (u32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}));
       sc.s[nt] = mfma_fp8(kf, st.qf[t], t == 0 ? f32x16{} : sc.s[nt]);
     }
-  }
-}
-
-template <class C>
-__device__ __forceinline__ void pv_block8(Fp8State<C>& st, const uint8_t XS_LDS* sV, int lane) {
-  if (st.rescale) {
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) st.o[dt] *= st.alpha;
-    st.alpha = 1.0f;
-    st.rescale = false;
-  }
-  const int ln = opaque(lane);
-  const int g = ln >> 4, L = ln & 15, h = g >> 1;
-  const int R0 = 32 * h + (L >> 1);          // + 8t
-  const int sw = vswz<C>(R0);                // the same for R0 + 8t
-  const uint8_t XS_LDS* vbase = sV + R0 * C::ROWB + 8 * (L & 1);
-#pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) {
-    const int chunk = (dt * 2 + (g & 1)) ^ sw;
-    u32x2 r[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) r[t] = lds_read_tr8(vbase + 8 * t * C::ROWB + (chunk << 4));
-    const i32x8 vf = __builtin_bit_cast(
-        i32x8, (u32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]}));
-    st.o[dt] = mfma_fp8(vf, st.pf, st.o[dt]);
   }
 }
 
@@ -157,34 +132,206 @@ __device__ __forceinline__ void softmax_max8(Fp8State<C>& st, const Scores8<C>& 
   }
 }
 
+#ifndef XS_LEAD8
+#define XS_LEAD8 1
+#endif
+
+// ---- The software pipeline as fixed sequences of micro-steps (one MFMA each,
+// separated by scheduling barriers, the vector work of each micro-step pinned
+// in place).  One PV MFMA of the fp8 kernel takes all 64 keys of a block, so
+// the probabilities of a block must be complete before its first PV MFMA; the
+// work is therefore split as
+//   step A: QK^T of block j+1 (MFMA)  ||  probabilities of keys 32..63 of block j
+//   step B: P V of block j (MFMA)     ||  row max of block j+1, lazy move of the
+//                                         running max, probabilities of its keys 0..31
+// so that each step carries about half of the vector work.
+
+// Per-lane LDS byte offsets of the fragments, relative to a tile's start.
 template <class C>
-__device__ __forceinline__ void softmax_exp8(Fp8State<C>& st, const Scores8<C>& sc, float c) {
-  const float neg_m = -st.m;
-  float lsum = st.l;
-  uint32_t w[8];
+struct LdsOffs8 {
+  uint32_t k[C::KS][2];  // the two 16-byte K chunks of k-step ks (row lane%32)
+  uint32_t v[C::DT];     // first transpose read of d-tile dt (then + 8 rows each)
+};
+
+template <class C>
+__device__ __forceinline__ LdsOffs8<C> lds_offsets8(int lane) {
+  LdsOffs8<C> o;
+  const int hi = lane >> 5, R = lane & 31, sw = kswz<C>(R);
 #pragma unroll
-  for (int nt = 0; nt < C::NT; ++nt)
+  for (int t = 0; t < C::KS; ++t) {
+    const int c0 = 4 * t + 2 * hi;
+    o.k[t][0] = (uint32_t)(R * C::ROWB + ((c0 ^ sw) << 4));
+    o.k[t][1] = (uint32_t)(R * C::ROWB + (((c0 + 1) ^ sw) << 4));
+  }
+  const int g = lane >> 4, L = lane & 15, h = g >> 1;
+  const int R0 = 32 * h + (L >> 1);
+  const int vs = vswz<C>(R0);  // the same for R0 + 8t
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = fast_exp2(__builtin_fmaf(sc.s[nt][4 * q + i], c, neg_m));
-        lsum += p[i];
-      }
-      w[nt * 4 + q] = pack_fp8x4(p[0], p[1], p[2], p[3]);
-    }
-  st.pf = __builtin_bit_cast(i32x8, (u32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]}));
-  st.l = lsum;
+  for (int dt = 0; dt < C::DT; ++dt) {
+    const int chunk = (dt * 2 + (g & 1)) ^ vs;
+    o.v[dt] = (uint32_t)(R0 * C::ROWB + 8 * (L & 1) + (chunk << 4));
+  }
+  return o;
 }
 
-template <int N, int V, int DS>
-__device__ __forceinline__ void interleave8() {
+// p = 2^(s c - m) of scores 4q..4q+3 of 32-key tile nt, packed to four e4m3
+// bytes, fp32 values added to the row sum; pinned to the current micro-step.
+template <class C>
+__device__ __forceinline__ void exp_quad(const Scores8<C>& sc, int nt, int q, float c, float neg_m,
+                                         float& lsum, uint32_t& w) {
+  float p[4];
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (DS) __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
-    if (V) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+  for (int i = 0; i < 4; ++i) {
+    p[i] = fast_exp2(__builtin_fmaf(sc.s[nt][4 * q + i], c, neg_m));
+    lsum += p[i];
+  }
+  uint32_t pk = pack_fp8x4(p[0], p[1], p[2], p[3]);
+  pin(pk);
+  pin(lsum);
+  w = pk;
+}
+
+// Step A: S^T of the next block from K stage KST || keys 32..63 of the current
+// block (its keys 0..31 were done in the previous step B).
+template <class C, int KST>
+__device__ __forceinline__ void step_a8(Scores8<C>& nxt, const Scores8<C>& cur, Fp8State<C>& st,
+                                        const uint8_t XS_LDS* lds, const LdsOffs8<C>& off, float c) {
+  constexpr int NT = C::NT, KS = C::KS, ROWB = C::ROWB;
+  constexpr int NF = KS * NT;
+  constexpr int LEAD = XS_LEAD8 < NF ? XS_LEAD8 : NF;
+  constexpr int R = LEAD + 1;
+  const uint8_t XS_LDS* kb = lds + KST * C::TILE;
+  auto kread = [&](int f) {
+    const int t = f / NT, nt = f % NT;
+    const u32x4 a0 = lds_read_b128(kb + off.k[t][0] + nt * 32 * ROWB);
+    const u32x4 a1 = lds_read_b128(kb + off.k[t][1] + nt * 32 * ROWB);
+    return __builtin_bit_cast(i32x8, (u32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}));
+  };
+  const float neg_m = -st.m;
+  float lsum = st.l;
+  uint32_t w[4];
+  i32x8 kf[R];
+#pragma unroll
+  for (int f = 0; f < LEAD; ++f) kf[f] = kread(f);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + LEAD < NF) kf[(f + LEAD) % R] = kread(f + LEAD);
+    const int t = f / NT, nt = f % NT;
+    nxt.s[nt] = mfma_fp8(kf[f % R], st.qf[t], t == 0 ? f32x16{} : nxt.s[nt]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q * NF / 4 == f) exp_quad<C>(cur, 1, q, c, neg_m, lsum, w[q]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l = lsum;
+  st.p1 = u32x4{w[0], w[1], w[2], w[3]};
+  keep(st.p1);
+}
+
+// Step B: O^T = alpha O^T + V^T P^T from V stage VST || row max of the next
+// block (first half), then the probabilities of its keys 0..31 (second half).
+template <class C, int VST>
+__device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
+                                        const uint8_t XS_LDS* lds, const LdsOffs8<C>& off, float c) {
+  constexpr int DT = C::DT, ROWB = C::ROWB;
+  constexpr int NF = DT;
+  constexpr int HALF = NF / 2;
+  constexpr int LEAD = XS_LEAD8 < NF ? XS_LEAD8 : NF;
+  constexpr int R = LEAD + 1;
+  if (st.rescale) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.o[dt] *= st.alpha;
+    st.alpha = 1.0f;
+    st.rescale = false;
+  }
+  const i32x8 pf = __builtin_bit_cast(
+      i32x8, (u32x8{st.p0[0], st.p0[1], st.p0[2], st.p0[3], st.p1[0], st.p1[1], st.p1[2], st.p1[3]}));
+  const uint8_t XS_LDS* vb = lds + (2 + VST) * C::TILE;
+  auto vread = [&](int f) {
+    u32x2 r[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) r[t] = lds_read_tr8(vb + off.v[f] + 8 * t * ROWB);
+    return __builtin_bit_cast(
+        i32x8, (u32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]}));
+  };
+  float mx = nxt.s[0][0];
+  float neg_m = 0.0f, lsum = 0.0f;
+  uint32_t w[4];
+  i32x8 vf[R];
+#pragma unroll
+  for (int f = 0; f < LEAD; ++f) vf[f] = vread(f);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + LEAD < NF) vf[(f + LEAD) % R] = vread(f + LEAD);
+    st.o[f] = mfma_fp8(vf[f % R], pf, st.o[f]);
+    if (f < HALF) {
+      constexpr int EPS = 32 / HALF;  // max over the 32 scores of the next block
+#pragma unroll
+      for (int ee = 0; ee < EPS; ++ee) {
+        const int e = f * EPS + ee;
+        mx = fmaxf(mx, nxt.s[e / 16][e % 16]);
+      }
+      pin(mx);
+      if (f == HALF - 1) {
+        // lazy move of the running max (the O rescale waits for the next step B)
+        const float mnew = max_halves(mx) * c;
+        const bool need = mnew > st.m + C::TAU;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          const float a = need ? fast_exp2(st.m - mnew) : 1.0f;
+          st.m = need ? mnew : st.m;
+          st.l *= a;
+          st.alpha *= a;
+          st.rescale = true;
+        }
+        neg_m = -st.m;
+        lsum = st.l;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q * HALF / 4 == f - HALF) exp_quad<C>(nxt, 0, q, c, neg_m, lsum, w[q]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l = lsum;
+  st.p0 = u32x4{w[0], w[1], w[2], w[3]};
+  keep(st.p0);
+}
+
+// Probabilities of all 32 keys of tile nt (prologue and tail, not pipelined).
+template <class C>
+__device__ __forceinline__ void exp_tile8(Fp8State<C>& st, const Scores8<C>& sc, int nt, float c,
+                                          u32x4& out) {
+  const float neg_m = -st.m;
+  float lsum = st.l;
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) exp_quad<C>(sc, nt, q, c, neg_m, lsum, w[q]);
+  st.l = lsum;
+  out = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// O^T = alpha O^T + V^T P^T of one block from V stage VST (tail, not pipelined).
+template <class C, int VST>
+__device__ __forceinline__ void pv_only8(Fp8State<C>& st, const uint8_t XS_LDS* lds,
+                                         const LdsOffs8<C>& off) {
+  if (st.rescale) {
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) st.o[dt] *= st.alpha;
+    st.alpha = 1.0f;
+    st.rescale = false;
+  }
+  const i32x8 pf = __builtin_bit_cast(
+      i32x8, (u32x8{st.p0[0], st.p0[1], st.p0[2], st.p0[3], st.p1[0], st.p1[1], st.p1[2], st.p1[3]}));
+  const uint8_t XS_LDS* vb = lds + (2 + VST) * C::TILE;
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+    u32x2 r[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) r[t] = lds_read_tr8(vb + off.v[dt] + 8 * t * C::ROWB);
+    const i32x8 vf = __builtin_bit_cast(
+        i32x8, (u32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]}));
+    st.o[dt] = mfma_fp8(vf, pf, st.o[dt]);
   }
 }
 
@@ -253,58 +400,53 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
   wait_vmcnt<0>();
   __syncthreads();
 
+  // prologue: score block jb, take its max, probabilities of its keys 0..31
   Scores8<C> sa, sb;
   qk_block8<C>(sa, st, kbuf(jb), lane);
   if (jb >= nfull) mask_tail8<C>(sa, jb * BN, S, lane);
   softmax_max8<C>(st, sa, c);
+  exp_tile8<C>(st, sa, 0, c, st.p0);
 
+  // Steady state, two blocks per trip so the score buffers swap statically.
+  // Entering the trip for block i: its scores are in one buffer with their max
+  // taken and the probabilities of keys 0..31 in st.p0; K_{i+1} and V_i are
+  // loaded or in flight.  (jb is even: K_i and V_i live in stage i % 2.)
+  const LdsOffs8<C> off = lds_offsets8<C>(lane);
   int j = jb;
   for (; j + 2 < je; j += 2) {
     wait_vmcnt<0>();
     __syncthreads();
-    load_tile8<C>(kbase, row_stride, (j + 2) * BN, S, kbuf(j), koff, wave);
-    load_tile8<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(j + 1), voff, wave);
-    qk_block8<C>(sb, st, kbuf(j + 1), lane);
-    softmax_exp8<C>(st, sa, c);
-    interleave8<C::NT * C::KS, 10, 2>();
-    __builtin_amdgcn_sched_barrier(0);
+    load_tile8<C>(kbase, row_stride, (j + 2) * BN, S, kbuf(0), koff, wave);
+    load_tile8<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(1), voff, wave);
+    step_a8<C, 1>(sb, sa, st, lds, off, c);
     if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
-    pv_block8<C>(st, vbuf(j), lane);
-    softmax_max8<C>(st, sb, c);
-    __builtin_amdgcn_sched_barrier(0);
+    step_b8<C, 0>(st, sb, lds, off, c);
 
     wait_vmcnt<0>();
     __syncthreads();
-    if (j + 3 < je) load_tile8<C>(kbase, row_stride, (j + 3) * BN, S, kbuf(j + 1), koff, wave);
-    load_tile8<C>(vbase, row_stride, (j + 2) * BN, S, vbuf(j + 2), voff, wave);
-    qk_block8<C>(sa, st, kbuf(j + 2), lane);
-    softmax_exp8<C>(st, sb, c);
-    interleave8<C::NT * C::KS, 10, 2>();
-    __builtin_amdgcn_sched_barrier(0);
+    if (j + 3 < je) load_tile8<C>(kbase, row_stride, (j + 3) * BN, S, kbuf(1), koff, wave);
+    load_tile8<C>(vbase, row_stride, (j + 2) * BN, S, vbuf(0), voff, wave);
+    step_a8<C, 0>(sa, sb, st, lds, off, c);
     if (j + 2 >= nfull) mask_tail8<C>(sa, (j + 2) * BN, S, lane);
-    pv_block8<C>(st, vbuf(j + 1), lane);
-    softmax_max8<C>(st, sa, c);
-    __builtin_amdgcn_sched_barrier(0);
+    step_b8<C, 1>(st, sa, lds, off, c);
   }
+  // the last one or two blocks (j is even; scores of block j in sa)
   if (j + 1 < je) {
     wait_vmcnt<0>();
     __syncthreads();
-    load_tile8<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(j + 1), voff, wave);
-    qk_block8<C>(sb, st, kbuf(j + 1), lane);
-    softmax_exp8<C>(st, sa, c);
-    __builtin_amdgcn_sched_barrier(0);
+    load_tile8<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(1), voff, wave);
+    step_a8<C, 1>(sb, sa, st, lds, off, c);
     if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
-    pv_block8<C>(st, vbuf(j), lane);
-    softmax_max8<C>(st, sb, c);
+    step_b8<C, 0>(st, sb, lds, off, c);
     wait_vmcnt<0>();
     __syncthreads();
-    softmax_exp8<C>(st, sb, c);
-    pv_block8<C>(st, vbuf(j + 1), lane);
+    exp_tile8<C>(st, sb, 1, c, st.p1);
+    pv_only8<C, 1>(st, lds, off);
   } else {
-    wait_vmcnt<0>();
+    wait_vmcnt<0>();  // V_j may have been issued by the last loop trip
     __syncthreads();
-    softmax_exp8<C>(st, sa, c);
-    pv_block8<C>(st, vbuf(j), lane);
+    exp_tile8<C>(st, sa, 1, c, st.p1);
+    pv_only8<C, 0>(st, lds, off);
   }
 
   // ---- epilogue
