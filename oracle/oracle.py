@@ -10,7 +10,10 @@ definition of attention, softmax(scale * Q K^T) V with a two-pass (exact max,
 then exp/sum) softmax, and writes the result into the destination-ordered
 buffer [P][B][S/P][H][D] an all-to-all over P sequence slices delivers (X-Stage
 paper: catalyzex.com abstract; gist.science explainer, "Zentrale Beitraege",
-"FlashAttention-A2A (Piggybacking)").
+"FlashAttention-A2A (Piggybacking)").  It also returns the rows' log-sum-exp
+(natural log) on request, and reads inputs either as [B][S][H][D] or in the
+same chunk layout [in_P][B][S/in_P][H][D] (what the pre-attention All-to-All
+delivers).
 """
 from __future__ import annotations
 
@@ -62,6 +65,12 @@ def _load():
         lib.xs_oracle_attention_packed.argtypes = [ci, vp, vp, vp, dbl, dbl, dbl, i64, i64, i64,
                                                    i64, i64, dbl, vp, ci]
         lib.xs_oracle_attention_packed.restype = ci
+        lib.xs_oracle_attention_rows_ex.argtypes = [ci, vp, vp, vp, dbl, dbl, dbl, i64, i64, i64,
+                                                    i64, i64, dbl, vp, i64, vp, vp, ci]
+        lib.xs_oracle_attention_rows_ex.restype = ci
+        lib.xs_oracle_attention_packed_ex.argtypes = [ci, vp, vp, vp, dbl, dbl, dbl, i64, i64, i64,
+                                                      i64, i64, i64, dbl, vp, vp, ci]
+        lib.xs_oracle_attention_packed_ex.restype = ci
         _lib = lib
     return _lib
 
@@ -87,45 +96,59 @@ def _as_input(x):
     raise TypeError(f"oracle takes float64, bfloat16 or float8_e4m3fn inputs, got {x.dtype}")
 
 
-def _problem(q, k, v):
+def _problem(q, k, v, in_P: int = 0):
+    """(dtype code, q, k, v, (B, S, H, D)) for [B][S][H][D] inputs (in_P = 0) or
+    inputs in the chunk layout [in_P][B][S/in_P][H][D]."""
     (cq, q), (ck, k), (cv, v) = _as_input(q), _as_input(k), _as_input(v)
     if not (cq == ck == cv):
         raise TypeError("q, k, v must share one dtype")
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must all be [B][S][H][D]")
-    return cq, q, k, v
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one shape")
+    if in_P:
+        if q.dim() != 5 or q.shape[0] != in_P:
+            raise ValueError("chunk-layout inputs must be [in_P][B][S/in_P][H][D]")
+        _, B, T, H, D = q.shape
+        shape = (B, in_P * T, H, D)
+    else:
+        if q.dim() != 4:
+            raise ValueError("q, k, v must all be [B][S][H][D]")
+        shape = tuple(q.shape)
+    return cq, q, k, v, shape
 
 
 def attention_packed(q, k, v, P: int, scale: float, descales=(1.0, 1.0, 1.0),
-                     nthreads: int | None = None) -> np.ndarray:
-    """Full oracle: fp64 out_packed of shape [P][B][S/P][H][D]."""
-    code, q, k, v = _problem(q, k, v)
-    B, S, H, D = q.shape
+                     nthreads: int | None = None, in_P: int = 0, with_lse: bool = False):
+    """Full oracle: fp64 out_packed of shape [P][B][S/P][H][D] (and, with
+    with_lse, the fp64 log-sum-exp [B][H][S])."""
+    code, q, k, v, (B, S, H, D) = _problem(q, k, v, in_P)
     if P < 1 or S % P:
         raise ValueError("S must be a multiple of P")
     out = np.empty((P, B, S // P, H, D), dtype=np.float64)
-    rc = _load().xs_oracle_attention_packed(
-        code, q.data_ptr(), k.data_ptr(), v.data_ptr(), *map(float, descales), B, S, H, D, P,
-        float(scale), out.ctypes.data, nthreads or default_threads())
-    if rc != 0:
-        raise RuntimeError(f"oracle failed with status {rc}")
-    return out
-
-
-def attention_rows(q, k, v, rows, scale: float, descales=(1.0, 1.0, 1.0),
-                   nthreads: int | None = None) -> np.ndarray:
-    """Oracle rows O[b, s, h, :] for an (n, 3) array of (b, s, h); returns (n, D) fp64."""
-    code, q, k, v = _problem(q, k, v)
-    B, S, H, D = q.shape
-    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
-    out = np.empty((rows.shape[0], D), dtype=np.float64)
-    rc = _load().xs_oracle_attention_rows(
-        code, q.data_ptr(), k.data_ptr(), v.data_ptr(), *map(float, descales), B, S, H, D,
-        float(scale), rows.ctypes.data, rows.shape[0], out.ctypes.data,
+    lse = np.empty((B, H, S), dtype=np.float64) if with_lse else None
+    rc = _load().xs_oracle_attention_packed_ex(
+        code, q.data_ptr(), k.data_ptr(), v.data_ptr(), *map(float, descales), in_P, B, S, H, D,
+        P, float(scale), out.ctypes.data, lse.ctypes.data if with_lse else None,
         nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle failed with status {rc}")
-    return out
+    return (out, lse) if with_lse else out
+
+
+def attention_rows(q, k, v, rows, scale: float, descales=(1.0, 1.0, 1.0),
+                   nthreads: int | None = None, in_P: int = 0, with_lse: bool = False):
+    """Oracle rows O[b, s, h, :] for an (n, 3) array of (b, s, h); returns (n, D)
+    fp64 (and, with with_lse, the rows' log-sum-exp, shape (n,))."""
+    code, q, k, v, (B, S, H, D) = _problem(q, k, v, in_P)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+    out = np.empty((rows.shape[0], D), dtype=np.float64)
+    lse = np.empty(rows.shape[0], dtype=np.float64) if with_lse else None
+    rc = _load().xs_oracle_attention_rows_ex(
+        code, q.data_ptr(), k.data_ptr(), v.data_ptr(), *map(float, descales), in_P, B, S, H, D,
+        float(scale), rows.ctypes.data, rows.shape[0], out.ctypes.data,
+        lse.ctypes.data if with_lse else None, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle failed with status {rc}")
+    return (out, lse) if with_lse else out
 
 
 def pack(o, P: int) -> np.ndarray:

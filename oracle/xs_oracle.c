@@ -26,6 +26,13 @@
  *    delivers when the sequence is cut into P contiguous slices of T = S/P
  *    rows: out_packed[p][b][s'][h][d] = O[b][p*T + s'][h][d].
  *
+ *  - The log-sum-exp of a row, lse = log(sum_j exp(s_j)) = m + log(l) in
+ *    natural-log units, the by-product of the same two passes.
+ *  - Inputs may also arrive in the chunk layout the pre-attention All-to-All
+ *    delivers, [P][B][S/P][H][D] (chunk p = rows p*T .. p*T+T-1 of every batch,
+ *    the same relayout as the output): element (b, s, h, d) then sits at
+ *    (((p*B + b)*T + s')*H + h)*D + d with p = floor(s/T), s' = s - p*T.
+ *
  * Inputs are stored as fp64, bf16 (bit patterns) or OCP fp8 e4m3fn codes with
  * a per-tensor fp64 descale; every element is decoded exactly to fp64 before
  * any arithmetic.  All arithmetic is fp64 with libm exp().  Build without
@@ -72,12 +79,20 @@ typedef struct {
   double q_descale, k_descale, v_descale;
   int64_t B, S, H, D;
   double scale;
+  int64_t in_P; /* 0: inputs are [B][S][H][D]; >= 1: [in_P][B][S/in_P][H][D] */
 } xso_problem;
 
-/* Element x[b][s][h][d] of a [B][S][H][D] contiguous tensor, decoded to fp64. */
+/* Element x[b][s][h][d] of an input tensor in the problem's layout, decoded to
+ * fp64. */
 static double load(const xso_problem *pr, const void *base, double descale, int64_t b, int64_t s,
                    int64_t h, int64_t d) {
-  int64_t idx = ((b * pr->S + s) * pr->H + h) * pr->D + d;
+  int64_t idx;
+  if (pr->in_P > 0) {
+    const int64_t T = pr->S / pr->in_P, p = s / T, sp = s - p * T;
+    idx = (((p * pr->B + b) * T + sp) * pr->H + h) * pr->D + d;
+  } else {
+    idx = ((b * pr->S + s) * pr->H + h) * pr->D + d;
+  }
   switch (pr->dtype) {
     case XSO_BF16:
       return xs_oracle_decode_bf16(((const uint16_t *)base)[idx]);
@@ -88,10 +103,10 @@ static double load(const xso_problem *pr, const void *base, double descale, int6
   }
 }
 
-/* One output row O[b,i,h,:] by the two-pass definition above.  `s` is a
- * scratch row of S doubles and `acc` one of D doubles. */
-static void attention_row(const xso_problem *pr, int64_t b, int64_t i, int64_t h, double *s,
-                          double *acc, double *out_row) {
+/* One output row O[b,i,h,:] by the two-pass definition above, and the row's
+ * log-sum-exp.  `s` is a scratch row of S doubles and `acc` one of D doubles. */
+static double attention_row(const xso_problem *pr, int64_t b, int64_t i, int64_t h, double *s,
+                            double *acc, double *out_row) {
   const int64_t S = pr->S, D = pr->D;
   double m = -INFINITY;
   for (int64_t j = 0; j < S; ++j) {
@@ -109,6 +124,7 @@ static void attention_row(const xso_problem *pr, int64_t b, int64_t i, int64_t h
     for (int64_t d = 0; d < D; ++d) acc[d] += w * load(pr, pr->v, pr->v_descale, b, j, h, d);
   }
   for (int64_t d = 0; d < D; ++d) out_row[d] = acc[d] / l;
+  return m + log(l);
 }
 
 /* Flat offset of element (b, s, h, d) of O inside the destination-ordered
@@ -142,6 +158,7 @@ typedef struct {
   int64_t nrows;
   double *out;         /* row r -> out + r*D, unless packed */
   int64_t P;           /* > 0: write into the packed buffer instead */
+  double *lse;         /* NULL, or row r -> lse[r] (rows) / lse[(b*H + h)*S + s] (packed) */
   int tid, nthreads;
   int status;
 } xso_job;
@@ -159,7 +176,8 @@ static void *worker(void *arg) {
   }
   for (int64_t r = job->tid; r < job->nrows; r += job->nthreads) {
     int64_t b = job->rows[3 * r], i = job->rows[3 * r + 1], h = job->rows[3 * r + 2];
-    attention_row(pr, b, i, h, s, acc, row);
+    const double lse = attention_row(pr, b, i, h, s, acc, row);
+    if (job->lse) job->lse[job->P > 0 ? (b * pr->H + h) * pr->S + i : r] = lse;
     for (int64_t d = 0; d < pr->D; ++d) {
       if (job->P > 0)
         job->out[xs_oracle_packed_offset(pr->B, pr->S, pr->H, pr->D, job->P, b, i, h, d)] = row[d];
@@ -173,14 +191,14 @@ static void *worker(void *arg) {
 }
 
 static int run_rows(const xso_problem *pr, const int64_t *rows, int64_t nrows, double *out,
-                    int64_t P, int nthreads) {
+                    int64_t P, double *lse, int nthreads) {
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
   pthread_t th[256];
   int created[256];
   xso_job jobs[256];
   for (int t = 0; t < nthreads; ++t) {
-    jobs[t] = (xso_job){pr, rows, nrows, out, P, t, nthreads, -1};
+    jobs[t] = (xso_job){pr, rows, nrows, out, P, lse, t, nthreads, -1};
     created[t] = pthread_create(&th[t], NULL, worker, &jobs[t]) == 0;
     if (!created[t]) worker(&jobs[t]); /* run this share on the calling thread */
   }
@@ -200,34 +218,49 @@ static int check(int dtype, const void *q, const void *k, const void *v, int64_t
   return 0;
 }
 
-/* Attention rows O[b,s,h,:] for nrows (b, s, h) triples; out is nrows x D.
- * Returns 0, -1 (null pointer / allocation), -2 (shape), -3 (dtype). */
-int xs_oracle_attention_rows(int dtype, const void *q, const void *k, const void *v,
-                             double q_descale, double k_descale, double v_descale, int64_t B,
-                             int64_t S, int64_t H, int64_t D, double scale, const int64_t *rows,
-                             int64_t nrows, double *out, int nthreads) {
+/* Attention rows O[b,s,h,:] for nrows (b, s, h) triples; out is nrows x D;
+ * lse (may be NULL) receives the rows' log-sum-exp.  in_P = 0 for
+ * [B][S][H][D] inputs, >= 1 for inputs in the [in_P][B][S/in_P][H][D] chunk
+ * layout.  Returns 0, -1 (null pointer / allocation), -2 (shape), -3 (dtype). */
+int xs_oracle_attention_rows_ex(int dtype, const void *q, const void *k, const void *v,
+                                double q_descale, double k_descale, double v_descale, int64_t in_P,
+                                int64_t B, int64_t S, int64_t H, int64_t D, double scale,
+                                const int64_t *rows, int64_t nrows, double *out, double *lse,
+                                int nthreads) {
   int rc = check(dtype, q, k, v, B, S, H, D);
   if (rc) return rc;
   if (!rows || !out) return -1;
+  if (in_P < 0 || (in_P > 0 && S % in_P != 0)) return -2;
   for (int64_t r = 0; r < nrows; ++r)
     if (rows[3 * r] < 0 || rows[3 * r] >= B || rows[3 * r + 1] < 0 || rows[3 * r + 1] >= S ||
         rows[3 * r + 2] < 0 || rows[3 * r + 2] >= H)
       return -2;
-  xso_problem pr = {dtype, q, k, v, q_descale, k_descale, v_descale, B, S, H, D, scale};
-  return run_rows(&pr, rows, nrows, out, 0, nthreads);
+  xso_problem pr = {dtype, q, k, v, q_descale, k_descale, v_descale, B, S, H, D, scale, in_P};
+  return run_rows(&pr, rows, nrows, out, 0, lse, nthreads);
+}
+
+int xs_oracle_attention_rows(int dtype, const void *q, const void *k, const void *v,
+                             double q_descale, double k_descale, double v_descale, int64_t B,
+                             int64_t S, int64_t H, int64_t D, double scale, const int64_t *rows,
+                             int64_t nrows, double *out, int nthreads) {
+  return xs_oracle_attention_rows_ex(dtype, q, k, v, q_descale, k_descale, v_descale, 0, B, S, H,
+                                     D, scale, rows, nrows, out, NULL, nthreads);
 }
 
 /* The whole hot path: attention over every (b, s, h) row, written straight
- * into the destination-ordered buffer [P][B][S/P][H][D] (fp64).
+ * into the destination-ordered buffer [P][B][S/P][H][D] (fp64); lse (may be
+ * NULL) receives the log-sum-exp of every row as [B][H][S].  in_P as above.
  * Returns 0, -1, -2 (also S % P != 0), -3. */
-int xs_oracle_attention_packed(int dtype, const void *q, const void *k, const void *v,
-                               double q_descale, double k_descale, double v_descale, int64_t B,
-                               int64_t S, int64_t H, int64_t D, int64_t P, double scale,
-                               double *out_packed, int nthreads) {
+int xs_oracle_attention_packed_ex(int dtype, const void *q, const void *k, const void *v,
+                                  double q_descale, double k_descale, double v_descale,
+                                  int64_t in_P, int64_t B, int64_t S, int64_t H, int64_t D,
+                                  int64_t P, double scale, double *out_packed, double *lse,
+                                  int nthreads) {
   int rc = check(dtype, q, k, v, B, S, H, D);
   if (rc) return rc;
   if (!out_packed) return -1;
   if (P < 1 || S % P != 0) return -2;
+  if (in_P < 0 || (in_P > 0 && S % in_P != 0)) return -2;
   int64_t nrows = B * S * H;
   int64_t *rows = (int64_t *)malloc((size_t)nrows * 3 * sizeof(int64_t));
   if (!rows) return -1;
@@ -238,8 +271,16 @@ int xs_oracle_attention_packed(int dtype, const void *q, const void *k, const vo
         rows[3 * r] = b, rows[3 * r + 1] = s, rows[3 * r + 2] = h;
         ++r;
       }
-  xso_problem pr = {dtype, q, k, v, q_descale, k_descale, v_descale, B, S, H, D, scale};
-  rc = run_rows(&pr, rows, nrows, out_packed, P, nthreads);
+  xso_problem pr = {dtype, q, k, v, q_descale, k_descale, v_descale, B, S, H, D, scale, in_P};
+  rc = run_rows(&pr, rows, nrows, out_packed, P, lse, nthreads);
   free(rows);
   return rc;
+}
+
+int xs_oracle_attention_packed(int dtype, const void *q, const void *k, const void *v,
+                               double q_descale, double k_descale, double v_descale, int64_t B,
+                               int64_t S, int64_t H, int64_t D, int64_t P, double scale,
+                               double *out_packed, int nthreads) {
+  return xs_oracle_attention_packed_ex(dtype, q, k, v, q_descale, k_descale, v_descale, 0, B, S,
+                                       H, D, P, scale, out_packed, NULL, nthreads);
 }

@@ -10,6 +10,8 @@ answers.  Each pin is chosen so a plausible mistake in the oracle fails it:
   head/batch indexing                -> SDPA at B, H > 1; permutation tests per head
   bf16 / e4m3 decode                 -> all codes vs torch's decoders
   pack layout                        -> hand-derived golden layouts, numpy split/stack
+  log-sum-exp: dropped max / log     -> golden values, score-shift invariance, torch.logsumexp
+  chunk-layout inputs (index math)   -> numpy reshape/transpose of [B][S][H][D] inputs
 """
 import json
 import math
@@ -64,7 +66,8 @@ def test_e4m3_decode_matches_torch_for_every_code():
 # ---------------------------------------------------------------- golden closed forms
 def _golden_value(x):
     if isinstance(x, str):
-        return {"ln2": math.log(2.0), "ln3": math.log(3.0)}[x]
+        return {"ln2": math.log(2.0), "ln3": math.log(3.0), "ln4": math.log(4.0),
+                "ln6": math.log(6.0)}[x]
     return float(x)
 
 
@@ -81,6 +84,16 @@ def test_golden_closed_forms():
         got = _unpacked(q, k, v, c["scale"])
         want = _golden_array(c["O"], shape)
         np.testing.assert_allclose(got, want, rtol=0, atol=1e-14, err_msg=c["name"])
+
+
+def test_golden_log_sum_exp():
+    cases = json.load(open(os.path.join(GOLDEN, "attention_closed_form.json")))["cases"]
+    for c in cases:
+        shape = (c["B"], c["S"], c["H"], c["D"])
+        q, k, v = (_f64(_golden_array(c[n], shape)) for n in "qkv")
+        _, lse = oracle.attention_packed(q, k, v, 1, c["scale"], with_lse=True)
+        want = _golden_array(c["lse"], (c["B"], c["H"], c["S"]))
+        np.testing.assert_allclose(lse, want, rtol=0, atol=1e-14, err_msg=c["name"])
 
 
 def test_two_key_logistic_closed_form():
@@ -267,3 +280,88 @@ def test_rejects_s_not_multiple_of_p():
     q = _rand((1, 10, 1, 4), 32)
     with pytest.raises(ValueError):
         oracle.attention_packed(q, q, q, 3, 1.0)
+
+
+# ---------------------------------------------------------------- log-sum-exp
+def test_log_sum_exp_matches_torch_logsumexp_float64():
+    B, S, H, D = 2, 37, 3, 16
+    q, k, v = _rand((B, S, H, D), 40), _rand((B, S, H, D), 41), _rand((B, S, H, D), 42)
+    scale = 0.61
+    _, lse = oracle.attention_packed(q, k, v, 1, scale, with_lse=True)
+    s = torch.matmul(q.permute(0, 2, 1, 3), k.permute(0, 2, 3, 1).contiguous()) * scale
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-13)
+
+
+def test_log_sum_exp_zero_keys_is_log_of_key_count():
+    B, S, H, D = 1, 53, 2, 8
+    q, v = _rand((B, S, H, D), 43, 4.0), _rand((B, S, H, D), 44)
+    k = torch.zeros((B, S, H, D), dtype=torch.float64)
+    _, lse = oracle.attention_packed(q, k, v, 1, 0.8, with_lse=True)
+    np.testing.assert_allclose(lse, math.log(S), rtol=0, atol=1e-14)
+
+
+def test_log_sum_exp_of_one_key_is_its_score():
+    q, k, v = _rand((2, 1, 2, 8), 45), _rand((2, 1, 2, 8), 46), _rand((2, 1, 2, 8), 47)
+    _, lse = oracle.attention_packed(q, k, v, 1, 0.3, with_lse=True)
+    want = 0.3 * (q.numpy() * k.numpy()).sum(-1)          # [B][1][H]
+    np.testing.assert_allclose(lse, want.transpose(0, 2, 1), rtol=0, atol=1e-14)
+
+
+def test_log_sum_exp_shifts_with_a_common_score_offset():
+    # an extra dimension with q = 1, k = c / scale adds c to every score: the
+    # softmax (and O) is unchanged and the log-sum-exp moves by exactly c
+    B, S, H, D = 1, 40, 2, 8
+    q, k, v = _rand((B, S, H, D), 48), _rand((B, S, H, D), 49), _rand((B, S, H, D), 50)
+    scale, c = 0.5, 7.25
+    q2 = torch.cat([q, torch.ones((B, S, H, 1), dtype=torch.float64)], dim=-1)
+    k2 = torch.cat([k, torch.full((B, S, H, 1), c / scale, dtype=torch.float64)], dim=-1)
+    v2 = torch.cat([v, torch.zeros((B, S, H, 1), dtype=torch.float64)], dim=-1)
+    o1, l1 = oracle.attention_packed(q, k, v, 1, scale, with_lse=True)
+    o2, l2 = oracle.attention_packed(q2, k2, v2, 1, scale, with_lse=True)
+    np.testing.assert_allclose(l2, l1 + c, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o2[..., :D], o1, rtol=0, atol=1e-13)
+
+
+def test_rows_entry_log_sum_exp_matches_packed_entry():
+    B, S, H, D = 2, 19, 2, 8
+    q, k, v = _rand((B, S, H, D), 51), _rand((B, S, H, D), 52), _rand((B, S, H, D), 53)
+    _, lse = oracle.attention_packed(q, k, v, 1, 0.4, with_lse=True)
+    rows = [(b, s, h) for b in range(B) for s in range(S) for h in range(H)]
+    _, got = oracle.attention_rows(q, k, v, rows, 0.4, with_lse=True)
+    want = np.array([lse[b, h, s] for b, s, h in rows])
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- chunk-layout inputs
+def _chunked(x, P):
+    """[B][S][H][D] -> [P][B][S/P][H][D] by numpy reshape/transpose (not oracle.pack)."""
+    B, S, H, D = x.shape
+    return torch.as_tensor(np.ascontiguousarray(
+        np.asarray(x).reshape(B, P, S // P, H, D).transpose(1, 0, 2, 3, 4)))
+
+
+@pytest.mark.parametrize("B,S,P", [(1, 12, 3), (2, 12, 2), (3, 16, 4), (2, 18, 6)])
+def test_chunk_layout_inputs_give_the_same_attention(B, S, P):
+    H, D = 2, 8
+    q, k, v = _rand((B, S, H, D), 54), _rand((B, S, H, D), 55), _rand((B, S, H, D), 56)
+    want, want_lse = oracle.attention_packed(q, k, v, P, 0.45, with_lse=True)
+    got, got_lse = oracle.attention_packed(_chunked(q, P), _chunked(k, P), _chunked(v, P), P, 0.45,
+                                           in_P=P, with_lse=True)
+    assert np.array_equal(got, want) and np.array_equal(got_lse, want_lse)
+    rows = [(b, s, h) for b in range(B) for s in range(S) for h in range(H)][::3]
+    r_want = oracle.attention_rows(q, k, v, rows, 0.45)
+    r_got = oracle.attention_rows(_chunked(q, P), _chunked(k, P), _chunked(v, P), rows, 0.45, in_P=P)
+    assert np.array_equal(r_got, r_want)
+
+
+def test_chunk_layout_hand_indexed_case():
+    # B = 2, S = 4, P = 2 (T = 2), H = D = 1: chunk p holds rows 2p, 2p+1 of
+    # batch 0 then of batch 1.  Keys are zero, so each O row is the mean of its
+    # batch's values: batch 0 values (1, 2, 3, 4) -> 2.5; batch 1 (10, 20, 30, 40) -> 25.
+    v_chunks = _f64([[[[[1.0]], [[2.0]]], [[[10.0]], [[20.0]]]],
+                     [[[[3.0]], [[4.0]]], [[[30.0]], [[40.0]]]]])   # [P][B][T][H][D]
+    q = torch.ones_like(v_chunks)
+    k = torch.zeros_like(v_chunks)
+    out = oracle.attention_packed(q, k, v_chunks, 1, 1.0, in_P=2)    # [1][B][S][H][D]
+    np.testing.assert_allclose(out[0, 0, :, 0, 0], 2.5, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(out[0, 1, :, 0, 0], 25.0, rtol=0, atol=1e-15)
