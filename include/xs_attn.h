@@ -44,8 +44,10 @@ extern "C" {
 #define XS_OK 0
 #define XS_ERR_NULL (-1)        /* a required pointer is NULL */
 #define XS_ERR_SHAPE (-2)       /* B, S, H_local, D or P < 1, or S % P != 0 */
-#define XS_ERR_UNSUPPORTED (-3) /* D not in {64, 128}, scale or a descale not finite, or
-                                   S*H_local*D*elem_bytes >= 4 GiB (one batch's rows) */
+#define XS_ERR_UNSUPPORTED (-3) /* D not in {64, 128}, scale or a descale not finite,
+                                   S*H_local*D*elem_bytes >= 4 GiB (one batch's rows), an
+                                   unknown input layout, or chunked inputs with B > 1, P > 1
+                                   and S/P not a multiple of 64 */
 #define XS_ERR_ALIGN (-4)       /* a pointer is not 16-byte aligned */
 #define XS_ERR_LAUNCH (-5)      /* the HIP launch reported an error */
 #define XS_ERR_OVERLAP (-6)     /* out_packed overlaps q, k or v */
@@ -93,6 +95,41 @@ int xs_attn_fwd_fp8_ws(const void *q8, const void *k8, const void *v8, float q_d
                        float k_descale, float v_descale, void *out_packed, int B, int S,
                        int H_local, int D, int P, float scale, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* Input layouts of q, k, v for the _ex entry points. */
+#define XS_LAYOUT_BSHD 0    /* [B][S][H_local][D] */
+#define XS_LAYOUT_CHUNKED 1 /* [P][B][S/P][H_local][D]: chunk p holds rows p*T .. p*T+T-1
+                               (T = S/P) of every batch -- the layout the Ulysses
+                               pre-attention All-to-All delivers, the same chunk layout as
+                               out_packed.  Byte-identical to BSHD when B = 1 or P = 1. */
+
+/* The split-key entry points with two additions (both optional):
+ *   in_layout  XS_LAYOUT_BSHD or XS_LAYOUT_CHUNKED: q, k, v may be consumed directly
+ *              in the chunk layout the pre-attention All-to-All of Ulysses sequence
+ *              parallelism delivers (X-Stage paper, catalyzex.com abstract: Ulysses
+ *              sequence-parallel attention between two All-to-Alls; gist.science
+ *              explainer, "FlashAttention-A2A (Piggybacking)"), so no relayout pass
+ *              runs before attention.  With B > 1 and P > 1, S/P must be a multiple
+ *              of 64 (XS_ERR_UNSUPPORTED otherwise).
+ *   lse        NULL, or device memory for [B][H_local][S] fp32 (4-byte aligned, not
+ *              overlapping q, k, v or out_packed, else XS_ERR_ALIGN / XS_ERR_OVERLAP):
+ *              receives the natural-log log-sum-exp of every query row,
+ *              lse = log(sum_j exp(scale * q.k_j)) (for fp8, scale*dq*dk * q8.k8_j),
+ *              the quantity an online-softmax merge of partial attention needs
+ *              ("Move the Query, Not the Cache", gist.science explainer, Methodik:
+ *              the Route primitive).  It is the running max plus log of the row sum
+ *              of the kernel's own softmax (the bf16-rounded probabilities for bf16,
+ *              fp32 ones for fp8).
+ * Every other argument, the workspace rules and the error behaviour are those of
+ * xs_attn_fwd_ws / xs_attn_fwd_fp8_ws, which equal these calls with in_layout =
+ * XS_LAYOUT_BSHD and lse = NULL. */
+int xs_attn_fwd_ex(const void *q, const void *k, const void *v, int in_layout, void *out_packed,
+                   float *lse, int B, int S, int H_local, int D, int P, float scale,
+                   void *workspace, size_t workspace_bytes, void *stream);
+int xs_attn_fwd_fp8_ex(const void *q8, const void *k8, const void *v8, int in_layout,
+                       float q_descale, float k_descale, float v_descale, void *out_packed,
+                       float *lse, int B, int S, int H_local, int D, int P, float scale,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace the split-key variants need on the current device for this
  * shape (0: the shape is run unsplit).  Depends on the device's compute-unit

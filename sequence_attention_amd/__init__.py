@@ -9,6 +9,8 @@ the calls raise.
     out_packed = fwd(q, k, v, P)            # bf16 q/k/v [B][S][H][D] on the GPU
     out_packed = fwd_fp8(q8, k8, v8, descales, P)
     o = unpack(out_packed, S)               # back to [B][S][H][D] (a torch view)
+    out_packed, lse = fwd(q, k, v, P, lse=True)          # + [B][H][S] fp32 log-sum-exp
+    out_packed = fwd(qc, kc, vc, P, in_layout="chunked")  # inputs [P][B][S/P][H][D]
 
 By default the calls use the split-key schedule when it fills the GPU better,
 with a workspace allocated from torch's caching allocator (pass a tensor of
@@ -24,10 +26,13 @@ import torch
 
 from ._lib import XsAttnError, check, declared_functions, lib, strerror
 
-__all__ = ["fwd", "fwd_fp8", "unpack", "workspace_size", "split_count", "xs_attn_fwd",
-           "xs_attn_fwd_fp8", "xs_attn_fwd_ws", "xs_attn_fwd_fp8_ws", "xs_attn_workspace_size",
-           "xs_attn_split_count", "xs_attn_strerror", "xs_attn_version", "XsAttnError",
-           "default_scale"]
+__all__ = ["fwd", "fwd_fp8", "unpack", "chunk", "workspace_size", "split_count", "xs_attn_fwd",
+           "xs_attn_fwd_fp8", "xs_attn_fwd_ws", "xs_attn_fwd_fp8_ws", "xs_attn_fwd_ex",
+           "xs_attn_fwd_fp8_ex", "xs_attn_workspace_size", "xs_attn_split_count",
+           "xs_attn_strerror", "xs_attn_version", "XsAttnError", "default_scale",
+           "LAYOUT_BSHD", "LAYOUT_CHUNKED"]
+
+LAYOUT_BSHD, LAYOUT_CHUNKED = 0, 1  # include/xs_attn.h XS_LAYOUT_*
 
 
 def default_scale(D: int) -> float:
@@ -41,20 +46,43 @@ def _stream_ptr(t: torch.Tensor, stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _check_inputs(q, k, v, dtype):
+def _check_inputs(q, k, v, dtype, P, in_layout):
+    """Validate q/k/v metadata; returns (B, S, H, D, layout code)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise TypeError(f"{name} must be a GPU tensor")
         if t.dtype != dtype:
             raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-        if t.dim() != 4 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous [B][S][H][D] tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
         if t.shape != q.shape or t.device != q.device:
             raise ValueError("q, k, v must share shape and device")
+    if in_layout == "bshd":
+        if q.dim() != 4:
+            raise ValueError("bshd inputs must be [B][S][H][D]")
+        B, S, H, D = q.shape
+        return B, S, H, D, LAYOUT_BSHD
+    if in_layout == "chunked":
+        if q.dim() != 5 or q.shape[0] != P:
+            raise ValueError("chunked inputs must be [P][B][S/P][H][D]")
+        _, B, T, H, D = q.shape
+        return B, P * T, H, D, LAYOUT_CHUNKED
+    raise ValueError("in_layout must be 'bshd' or 'chunked'")
 
 
-def _out(q, P, out):
-    B, S, H, D = q.shape
+def _lse(q, B, S, H, lse):
+    """Resolve the lse argument to a tensor or None."""
+    if lse is None or lse is False:
+        return None
+    if lse is True:
+        return torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if (not isinstance(lse, torch.Tensor) or not lse.is_cuda or lse.dtype != torch.float32
+            or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 GPU tensor of shape {(B, H, S)}")
+    return lse
+
+
+def _out(q, B, S, H, D, P, out):
     if S % P:
         raise ValueError(f"S={S} is not a multiple of P={P}")
     shape = (P, B, S // P, H, D)
@@ -95,6 +123,23 @@ def xs_attn_fwd_fp8_ws(q8, k8, v8, q_descale, k_descale, v_descale, out_packed, 
                                     float(scale), ptr(workspace), int(workspace_bytes), stream)
 
 
+def xs_attn_fwd_ex(q, k, v, in_layout, out_packed, lse, B, S, H_local, D, P, scale, workspace,
+                   workspace_bytes, stream) -> int:
+    ptr = lambda x: x.data_ptr() if isinstance(x, torch.Tensor) else x
+    return lib().xs_attn_fwd_ex(ptr(q), ptr(k), ptr(v), int(in_layout), ptr(out_packed), ptr(lse),
+                                B, S, H_local, D, P, float(scale), ptr(workspace),
+                                int(workspace_bytes), stream)
+
+
+def xs_attn_fwd_fp8_ex(q8, k8, v8, in_layout, q_descale, k_descale, v_descale, out_packed, lse, B,
+                       S, H_local, D, P, scale, workspace, workspace_bytes, stream) -> int:
+    ptr = lambda x: x.data_ptr() if isinstance(x, torch.Tensor) else x
+    return lib().xs_attn_fwd_fp8_ex(ptr(q8), ptr(k8), ptr(v8), int(in_layout), float(q_descale),
+                                    float(k_descale), float(v_descale), ptr(out_packed), ptr(lse),
+                                    B, S, H_local, D, P, float(scale), ptr(workspace),
+                                    int(workspace_bytes), stream)
+
+
 def xs_attn_workspace_size(B, S, H_local, D) -> int:
     return int(lib().xs_attn_workspace_size(B, S, H_local, D))
 
@@ -107,11 +152,10 @@ workspace_size = xs_attn_workspace_size
 split_count = xs_attn_split_count
 
 
-def _workspace(q, workspace):
+def _workspace(q, B, S, H, D, workspace):
     """Resolve the workspace argument to (pointer-or-tensor, bytes)."""
     if workspace is None:
         return None, 0
-    B, S, H, D = q.shape
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be a tensor, None or 'auto'")
@@ -133,29 +177,45 @@ def xs_attn_version() -> int:
 
 
 def fwd(q, k, v, P: int, scale: float | None = None, out=None, stream=None,
-        workspace="auto") -> torch.Tensor:
-    """Attention over bf16 [B][S][H][D] inputs; returns bf16 out_packed [P][B][S/P][H][D]."""
-    _check_inputs(q, k, v, torch.bfloat16)
-    B, S, H, D = q.shape
-    out = _out(q, P, out)
+        workspace="auto", lse=None, in_layout: str = "bshd"):
+    """Attention over bf16 inputs; returns bf16 out_packed [P][B][S/P][H][D].
+
+    q, k, v are [B][S][H][D] (in_layout="bshd") or [P][B][S/P][H][D]
+    (in_layout="chunked", what the pre-attention All-to-All delivers).  With
+    lse=True (or a [B][H][S] float32 tensor) the rows' natural-log log-sum-exp is
+    written too and (out_packed, lse) is returned."""
+    B, S, H, D, code = _check_inputs(q, k, v, torch.bfloat16, P, in_layout)
+    out = _out(q, B, S, H, D, P, out)
+    lse_t = _lse(q, B, S, H, lse)
     scale = default_scale(D) if scale is None else float(scale)
-    ws, nbytes = _workspace(q, workspace)
-    check(xs_attn_fwd_ws(q, k, v, out, B, S, H, D, P, scale, ws, nbytes, _stream_ptr(q, stream)))
-    return out
+    ws, nbytes = _workspace(q, B, S, H, D, workspace)
+    check(xs_attn_fwd_ex(q, k, v, code, out, lse_t, B, S, H, D, P, scale, ws, nbytes,
+                         _stream_ptr(q, stream)))
+    return (out, lse_t) if lse_t is not None else out
 
 
 def fwd_fp8(q8, k8, v8, descales, P: int, scale: float | None = None, out=None,
-            stream=None, workspace="auto") -> torch.Tensor:
-    """Attention over e4m3 [B][S][H][D] inputs with per-tensor descales (x = x8 * d)."""
-    _check_inputs(q8, k8, v8, torch.float8_e4m3fn)
-    B, S, H, D = q8.shape
-    out = _out(q8, P, out)
+            stream=None, workspace="auto", lse=None, in_layout: str = "bshd"):
+    """Attention over e4m3 inputs with per-tensor descales (x = x8 * d); layouts,
+    lse and the return value as for fwd."""
+    B, S, H, D, code = _check_inputs(q8, k8, v8, torch.float8_e4m3fn, P, in_layout)
+    out = _out(q8, B, S, H, D, P, out)
+    lse_t = _lse(q8, B, S, H, lse)
     scale = default_scale(D) if scale is None else float(scale)
     dq, dk, dv = (float(d) for d in descales)
-    ws, nbytes = _workspace(q8, workspace)
-    check(xs_attn_fwd_fp8_ws(q8, k8, v8, dq, dk, dv, out, B, S, H, D, P, scale, ws, nbytes,
-                             _stream_ptr(q8, stream)))
-    return out
+    ws, nbytes = _workspace(q8, B, S, H, D, workspace)
+    check(xs_attn_fwd_fp8_ex(q8, k8, v8, code, dq, dk, dv, out, lse_t, B, S, H, D, P, scale, ws,
+                             nbytes, _stream_ptr(q8, stream)))
+    return (out, lse_t) if lse_t is not None else out
+
+
+def chunk(x: torch.Tensor, P: int) -> torch.Tensor:
+    """[B][S][H][D] -> contiguous [P][B][S/P][H][D] (the chunk layout; a torch copy)."""
+    B, S, H, D = x.shape
+    assert S % P == 0
+    raw = x.view(torch.uint8) if x.element_size() == 1 else x.view(torch.int16)
+    y = raw.reshape(B, P, S // P, H, D).permute(1, 0, 2, 3, 4).contiguous()
+    return y.view(x.dtype)
 
 
 def unpack(out_packed: torch.Tensor, S: int) -> torch.Tensor:

@@ -7,7 +7,8 @@
 // the online-softmax merge of partial attention ("Move the Query, Not the
 // Cache", gist.science explainer: Methodik, the Route primitive merges partial
 // attention computed at the owner with an online softmax).  The splits are
-// summed in a fixed order, so the result is deterministic.
+// summed in a fixed order, so the result is deterministic.  The row's
+// log-sum-exp, when asked for, is ln(2^M L) with L = sum_s w_s l_s.
 #include "attn_launch.h"
 #include "device_common.h"
 
@@ -34,6 +35,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     acc += w * *(const f32x4*)(a.ws_o + r * D + d0);
   }
   const float inv = a.o_scale / L;
+  if (a.lse && d0 == 0) a.lse[row] = row_lse(M, L);
   const int S = a.S, H = a.H, T = a.T;
   const int srow = (int)(row % S);
   const int bh = (int)(row / S);

@@ -104,14 +104,15 @@ __device__ __forceinline__ void tile_offsets(uint32_t row_stride, int wave, int 
   }
 }
 
-// Fill one K or V tile of BN rows starting at key kv0 with direct-to-LDS
-// buffer loads.  The buffer resource ends after row S-1, so rows past the end
-// of the sequence read as zeros (their scores are masked).
+// Fill one K or V tile of BN rows starting at key kv0 (rows kv0.. are `extra`
+// bytes further in the chunk input layout) with direct-to-LDS buffer loads.
+// The buffer resource ends after row S-1, so rows past the end of the sequence
+// read as zeros (their scores are masked).
 template <class C>
 __device__ __forceinline__ void load_tile(const uint8_t* head_base, uint32_t row_stride, int kv0,
-                                          int S, const uint8_t XS_LDS* dst,
+                                          size_t extra, int S, const uint8_t XS_LDS* dst,
                                           const uint32_t (&voff)[C::LPW], int wave) {
-  const u32x4 rsrc = make_rsrc(head_base + (size_t)kv0 * row_stride,
+  const u32x4 rsrc = make_rsrc(head_base + (size_t)kv0 * row_stride + extra,
                                (uint32_t)(S - kv0 - 1) * row_stride + (uint32_t)C::ROWB);
   const uint32_t base = lds_addr(dst) + (uint32_t)(wave * C::LPW) * 1024u;
 #pragma unroll
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
   const int m0 = mt * BM;
 
   const uint32_t row_stride = (uint32_t)H * C::ROWB;  // bytes between consecutive rows
-  const size_t head_off = ((size_t)b * S * H + h) * C::ROWB;
+  const size_t head_off = ((size_t)b * a.batch_rows * H + h) * C::ROWB;
   const uint8_t* kbase = (const uint8_t*)a.k + head_off;
   const uint8_t* vbase = (const uint8_t*)a.v + head_off;
   uint32_t koff[C::LPW], voff[C::LPW];
@@ -506,9 +507,13 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
   const int nfull = S / BN;  // blocks with no key past the end of the sequence
   const int jb = split * a.nb_per;                                // this item's key blocks
   const int je = jb + a.nb_per < nblk ? jb + a.nb_per : nblk;    // [jb, je)
-  load_tile<C>(kbase, row_stride, jb * BN, S, kbuf(jb), koff, wave);
-  load_tile<C>(vbase, row_stride, jb * BN, S, vbuf(jb), voff, wave);
-  if (jb + 1 < je) load_tile<C>(kbase, row_stride, (jb + 1) * BN, S, kbuf(jb + 1), koff, wave);
+  ChunkCursor kcur, vcur;
+  kcur.init(jb, a.chunk_rows, a.jump_rows, row_stride);
+  vcur.init(jb, a.chunk_rows, a.jump_rows, row_stride);
+  load_tile<C>(kbase, row_stride, jb * BN, kcur.at(jb), S, kbuf(jb), koff, wave);
+  load_tile<C>(vbase, row_stride, jb * BN, vcur.at(jb), S, vbuf(jb), voff, wave);
+  if (jb + 1 < je)
+    load_tile<C>(kbase, row_stride, (jb + 1) * BN, kcur.at(jb + 1), S, kbuf(jb + 1), koff, wave);
 
   Bf16State<C> st;
   const uint32_t qflip = a.neg ? 0x80008000u : 0u;
@@ -516,7 +521,8 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
   for (int qt = 0; qt < QT; ++qt) {
     int qrow = m0 + wave * C::QW + qt * 32 + (lane & 31);
     qrow = qrow < S ? qrow : S - 1;
-    const uint8_t* qp = (const uint8_t*)a.q + head_off + (size_t)qrow * row_stride + (lane >> 5) * 16;
+    const long long qr = qrow + (a.chunk_rows ? (long long)(qrow / a.chunk_rows) * a.jump_rows : 0);
+    const uint8_t* qp = (const uint8_t*)a.q + head_off + (size_t)qr * row_stride + (lane >> 5) * 16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 t = *(const u32x4*)(qp + ks * 32);
@@ -550,8 +556,8 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
     // ---- block j (scores in sa), next block's scores into sb
     wait_vmcnt<0>();
     __syncthreads();
-    load_tile<C>(kbase, row_stride, (j + 2) * BN, S, kbuf(0), koff, wave);
-    load_tile<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(1), voff, wave);
+    load_tile<C>(kbase, row_stride, (j + 2) * BN, kcur.at(j + 2), S, kbuf(0), koff, wave);
+    load_tile<C>(vbase, row_stride, (j + 1) * BN, vcur.at(j + 1), S, vbuf(1), voff, wave);
     step1<C, 1>(sb, sa, st, lds, off, c);
     if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
     step2<C, 0>(st, sb, sa, lds, off, c);
@@ -559,8 +565,9 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
     // ---- block j+1 (scores in sb), next block's scores into sa
     wait_vmcnt<0>();
     __syncthreads();
-    if (j + 3 < je) load_tile<C>(kbase, row_stride, (j + 3) * BN, S, kbuf(1), koff, wave);
-    load_tile<C>(vbase, row_stride, (j + 2) * BN, S, vbuf(0), voff, wave);
+    if (j + 3 < je)
+      load_tile<C>(kbase, row_stride, (j + 3) * BN, kcur.at(j + 3), S, kbuf(1), koff, wave);
+    load_tile<C>(vbase, row_stride, (j + 2) * BN, vcur.at(j + 2), S, vbuf(0), voff, wave);
     step1<C, 0>(sa, sb, st, lds, off, c);
     if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
     step2<C, 1>(st, sa, sb, lds, off, c);
@@ -569,7 +576,7 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
   if (j + 1 < je) {
     wait_vmcnt<0>();
     __syncthreads();
-    load_tile<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(j + 1), voff, wave);
+    load_tile<C>(vbase, row_stride, (j + 1) * BN, vcur.at(j + 1), S, vbuf(j + 1), voff, wave);
     qk_block<C>(sb, st, kbuf(j + 1), lane);
     softmax_exp<C>(st, sa, c);
     __builtin_amdgcn_sched_barrier(0);
@@ -593,8 +600,10 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
     // normalise, round to bf16, store into the destination slice
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const float inv = a.o_scale / sum_halves(st.l[qt]);
+      const float lrow = sum_halves(st.l[qt]);
+      const float inv = a.o_scale / lrow;
       const int srow = m0 + wave * C::QW + qt * 32 + (lane & 31);
+      if (a.lse && lane < 32 && srow < S) a.lse[(size_t)bh * S + srow] = row_lse(st.m[qt], lrow);
       if (srow < S) {
         const int p = srow / T;
         const int sp = srow - p * T;

@@ -59,9 +59,10 @@ __device__ __forceinline__ int vswz(int R) { return 2 * ((R / C::RPB) & (C::CH /
 
 template <class C>
 __device__ __forceinline__ void load_tile8(const uint8_t* head_base, uint32_t row_stride, int kv0,
-                                           int S, const uint8_t XS_LDS* dst, uint32_t voff, int wave) {
+                                           size_t extra, int S, const uint8_t XS_LDS* dst,
+                                           uint32_t voff, int wave) {
   if (wave < C::LOADS) {
-    const u32x4 rsrc = make_rsrc(head_base + (size_t)kv0 * row_stride,
+    const u32x4 rsrc = make_rsrc(head_base + (size_t)kv0 * row_stride + extra,
                                  (uint32_t)(S - kv0 - 1) * row_stride + (uint32_t)C::ROWB);
     load_lds_b128(rsrc, voff, lds_addr(dst) + (uint32_t)wave * 1024u);
   }
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
   const int m0 = mt * BM;
 
   const uint32_t row_stride = (uint32_t)H * C::ROWB;
-  const size_t head_off = ((size_t)b * S * H + h) * C::ROWB;
+  const size_t head_off = ((size_t)b * a.batch_rows * H + h) * C::ROWB;
   const uint8_t* kbase = (const uint8_t*)a.k + head_off;
   const uint8_t* vbase = (const uint8_t*)a.v + head_off;
   // this lane's 16-byte chunk of the wave's 1 KiB direct load, for K and V
@@ -372,16 +373,21 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
   const int nfull = S / BN;
   const int jb = split * a.nb_per;
   const int je = jb + a.nb_per < nblk ? jb + a.nb_per : nblk;
-  load_tile8<C>(kbase, row_stride, jb * BN, S, kbuf(jb), koff, wave);
-  load_tile8<C>(vbase, row_stride, jb * BN, S, vbuf(jb), voff, wave);
-  if (jb + 1 < je) load_tile8<C>(kbase, row_stride, (jb + 1) * BN, S, kbuf(jb + 1), koff, wave);
+  ChunkCursor kcur, vcur;
+  kcur.init(jb, a.chunk_rows, a.jump_rows, row_stride);
+  vcur.init(jb, a.chunk_rows, a.jump_rows, row_stride);
+  load_tile8<C>(kbase, row_stride, jb * BN, kcur.at(jb), S, kbuf(jb), koff, wave);
+  load_tile8<C>(vbase, row_stride, jb * BN, vcur.at(jb), S, vbuf(jb), voff, wave);
+  if (jb + 1 < je)
+    load_tile8<C>(kbase, row_stride, (jb + 1) * BN, kcur.at(jb + 1), S, kbuf(jb + 1), koff, wave);
 
   Fp8State<C> st;
   {
     const uint32_t qflip = a.neg ? 0x80808080u : 0u;
     int qrow = m0 + wave * C::QW + (lane & 31);
     qrow = qrow < S ? qrow : S - 1;
-    const uint8_t* qp = (const uint8_t*)a.q + head_off + (size_t)qrow * row_stride + (lane >> 5) * 32;
+    const long long qr = qrow + (a.chunk_rows ? (long long)(qrow / a.chunk_rows) * a.jump_rows : 0);
+    const uint8_t* qp = (const uint8_t*)a.q + head_off + (size_t)qr * row_stride + (lane >> 5) * 32;
 #pragma unroll
     for (int t = 0; t < C::KS; ++t) {
       const u32x4 x0 = *(const u32x4*)(qp + t * 64) ^ qflip;
@@ -416,16 +422,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
   for (; j + 2 < je; j += 2) {
     wait_vmcnt<0>();
     __syncthreads();
-    load_tile8<C>(kbase, row_stride, (j + 2) * BN, S, kbuf(0), koff, wave);
-    load_tile8<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(1), voff, wave);
+    load_tile8<C>(kbase, row_stride, (j + 2) * BN, kcur.at(j + 2), S, kbuf(0), koff, wave);
+    load_tile8<C>(vbase, row_stride, (j + 1) * BN, vcur.at(j + 1), S, vbuf(1), voff, wave);
     step_a8<C, 1>(sb, sa, st, lds, off, c);
     if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
     step_b8<C, 0>(st, sb, lds, off, c);
 
     wait_vmcnt<0>();
     __syncthreads();
-    if (j + 3 < je) load_tile8<C>(kbase, row_stride, (j + 3) * BN, S, kbuf(1), koff, wave);
-    load_tile8<C>(vbase, row_stride, (j + 2) * BN, S, vbuf(0), voff, wave);
+    if (j + 3 < je)
+      load_tile8<C>(kbase, row_stride, (j + 3) * BN, kcur.at(j + 3), S, kbuf(1), koff, wave);
+    load_tile8<C>(vbase, row_stride, (j + 2) * BN, vcur.at(j + 2), S, vbuf(0), voff, wave);
     step_a8<C, 0>(sa, sb, st, lds, off, c);
     if (j + 2 >= nfull) mask_tail8<C>(sa, (j + 2) * BN, S, lane);
     step_b8<C, 1>(st, sa, lds, off, c);
@@ -434,7 +441,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
   if (j + 1 < je) {
     wait_vmcnt<0>();
     __syncthreads();
-    load_tile8<C>(vbase, row_stride, (j + 1) * BN, S, vbuf(1), voff, wave);
+    load_tile8<C>(vbase, row_stride, (j + 1) * BN, vcur.at(j + 1), S, vbuf(1), voff, wave);
     step_a8<C, 1>(sb, sa, st, lds, off, c);
     if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
     step_b8<C, 0>(st, sb, lds, off, c);
@@ -454,7 +461,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
   const int srow = m0 + wave * C::QW + (lane & 31);
   if (nsplit == 1) {
     // O * dv / l, rounded to bf16, stored into the destination slice
-    const float inv = a.o_scale / sum_halves(st.l);
+    const float lrow = sum_halves(st.l);
+    const float inv = a.o_scale / lrow;
+    if (a.lse && lane < 32 && srow < S) a.lse[(size_t)bh * S + srow] = row_lse(st.m, lrow);
     if (srow < S) {
       const int p = srow / T;
       const int sp = srow - p * T;

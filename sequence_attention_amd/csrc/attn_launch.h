@@ -24,6 +24,15 @@ struct AttnArgs {
   int nb_per;
   float* ws_o;    // [nsplit][B*H*S][D] fp32
   float* ws_ml;   // [nsplit][B*H*S][2] fp32: running max (log2 units), row sum
+  // Input layout.  Row s of batch b of an input tensor starts at row index
+  //   b*batch_rows + s + (chunk_rows ? s / chunk_rows : 0) * jump_rows
+  // (in units of H*D elements): [B][S][H][D] has batch_rows = S, chunk_rows =
+  // 0; the chunk layout [P][B][T][H][D] has batch_rows = T, chunk_rows = T,
+  // jump_rows = (B-1)*T.
+  int batch_rows;
+  int chunk_rows;
+  long long jump_rows;
+  float* lse;     // NULL or [B][H][S] fp32 log-sum-exp (natural log)
 };
 
 // Tile geometry shared by the bf16 and fp8 kernels and the host-side plan.

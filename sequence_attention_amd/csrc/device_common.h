@@ -123,6 +123,12 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Natural-log log-sum-exp of a row from its running max m (log2 units) and
+// its sum l of 2^(s c - m): ln(2^m l) = (m + log2 l) ln 2.
+__device__ __forceinline__ float row_lse(float m, float l) {
+  return (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+}
+
 // Marks x as used here: keeps the optimiser from sinking the instructions that
 // compute x past this point (into a later block of the software pipeline).
 template <class T>
@@ -143,6 +149,36 @@ __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+
+// Bytes to add to the K/V rows of 64-key block n when the inputs arrive in the
+// chunk layout [P][B][T][H][D] (T a multiple of 64): each chunk boundary skips
+// the (B-1)*T rows of the other batches.  One stream (K or V) loads its blocks
+// in increasing order, one at a time, so a boundary test per load replaces a
+// division.  All members are wave-uniform.
+struct ChunkCursor {
+  int nb;       // first block of the next chunk
+  int tpc;      // blocks per chunk
+  size_t step;  // bytes skipped at a chunk boundary
+  size_t ex;    // bytes skipped before the current chunk
+  __device__ void init(int first_block, int chunk_rows, long long jump_rows, uint32_t row_stride) {
+    if (chunk_rows == 0) {  // [B][S][H][D]: rows are contiguous
+      nb = 0x7fffffff, tpc = 1, step = 0, ex = 0;
+      return;
+    }
+    tpc = chunk_rows / 64;
+    const int p = first_block / tpc;
+    step = (size_t)jump_rows * row_stride;
+    nb = (p + 1) * tpc;
+    ex = (size_t)p * step;
+  }
+  __device__ size_t at(int n) {
+    if (n >= nb) {
+      nb += tpc;
+      ex += step;
+    }
+    return ex;
+  }
+};
 
 // Workgroups are dispatched round-robin over the 8 XCDs (block i -> XCD i%8).
 // Give XCD x a contiguous range of tiles so that the workgroups resident on one

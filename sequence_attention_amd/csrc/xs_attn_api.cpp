@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // |scale| * log2(e): the kernels compute p = 2^(s*c - m).  A zero scale is
@@ -65,6 +65,33 @@ int validate(const void* q, const void* k, const void* v, void* out, int B, int 
   args->nb_per = (S + xs::kBlockN - 1) / xs::kBlockN;
   args->ws_o = nullptr;
   args->ws_ml = nullptr;
+  args->batch_rows = S;
+  args->chunk_rows = 0;
+  args->jump_rows = 0;
+  args->lse = nullptr;
+  return XS_OK;
+}
+
+// Input layout and the optional log-sum-exp output, on validated arguments.
+int apply_layout_and_lse(xs::AttnArgs* a, int in_layout, float* lse, size_t in_elem_bytes) {
+  if (in_layout != XS_LAYOUT_BSHD && in_layout != XS_LAYOUT_CHUNKED) return XS_ERR_UNSUPPORTED;
+  // With B = 1 or P = 1 the chunk layout is byte-identical to [B][S][H][D].
+  if (in_layout == XS_LAYOUT_CHUNKED && a->B > 1 && a->P > 1) {
+    if (a->T % xs::kBlockN != 0) return XS_ERR_UNSUPPORTED;  // K/V blocks may not straddle chunks
+    a->batch_rows = a->T;
+    a->chunk_rows = a->T;
+    a->jump_rows = (long long)(a->B - 1) * a->T;
+  }
+  if (lse) {
+    if (((uintptr_t)lse & 3u) != 0) return XS_ERR_ALIGN;
+    const size_t n = (size_t)a->B * a->S * a->H * a->D;
+    const size_t lse_bytes = (size_t)a->B * a->H * a->S * sizeof(float);
+    const size_t in_bytes = n * in_elem_bytes;
+    if (overlaps(lse, lse_bytes, a->q, in_bytes) || overlaps(lse, lse_bytes, a->k, in_bytes) ||
+        overlaps(lse, lse_bytes, a->v, in_bytes) || overlaps(lse, lse_bytes, a->out, n * 2))
+      return XS_ERR_OVERLAP;
+    a->lse = lse;
+  }
   return XS_OK;
 }
 
@@ -148,28 +175,40 @@ int launch(const xs::AttnArgs& a, bool fp8, hipStream_t stream) {
 
 extern "C" {
 
-int xs_attn_fwd_ws(const void* q, const void* k, const void* v, void* out_packed, int B, int S,
-                   int H_local, int D, int P, float scale, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+int xs_attn_fwd_ex(const void* q, const void* k, const void* v, int in_layout, void* out_packed,
+                   float* lse, int B, int S, int H_local, int D, int P, float scale,
+                   void* workspace, size_t workspace_bytes, void* stream) {
   xs::AttnArgs a;
   int rc = validate(q, k, v, out_packed, B, S, H_local, D, P, scale, 2, &a);
+  if (rc != XS_OK) return rc;
+  rc = apply_layout_and_lse(&a, in_layout, lse, 2);
   if (rc != XS_OK) return rc;
   rc = attach_workspace(&a, workspace, workspace_bytes);
   if (rc != XS_OK) return rc;
   return launch(a, false, (hipStream_t)stream);
 }
 
-int xs_attn_fwd(const void* q, const void* k, const void* v, void* out_packed, int B, int S,
-                int H_local, int D, int P, float scale, void* stream) {
-  return xs_attn_fwd_ws(q, k, v, out_packed, B, S, H_local, D, P, scale, nullptr, 0, stream);
+int xs_attn_fwd_ws(const void* q, const void* k, const void* v, void* out_packed, int B, int S,
+                   int H_local, int D, int P, float scale, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return xs_attn_fwd_ex(q, k, v, XS_LAYOUT_BSHD, out_packed, nullptr, B, S, H_local, D, P, scale,
+                        workspace, workspace_bytes, stream);
 }
 
-int xs_attn_fwd_fp8_ws(const void* q8, const void* k8, const void* v8, float q_descale,
-                       float k_descale, float v_descale, void* out_packed, int B, int S,
-                       int H_local, int D, int P, float scale, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+int xs_attn_fwd(const void* q, const void* k, const void* v, void* out_packed, int B, int S,
+                int H_local, int D, int P, float scale, void* stream) {
+  return xs_attn_fwd_ex(q, k, v, XS_LAYOUT_BSHD, out_packed, nullptr, B, S, H_local, D, P, scale,
+                        nullptr, 0, stream);
+}
+
+int xs_attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v8, int in_layout,
+                       float q_descale, float k_descale, float v_descale, void* out_packed,
+                       float* lse, int B, int S, int H_local, int D, int P, float scale,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   xs::AttnArgs a;
   int rc = validate(q8, k8, v8, out_packed, B, S, H_local, D, P, scale, 1, &a);
+  if (rc != XS_OK) return rc;
+  rc = apply_layout_and_lse(&a, in_layout, lse, 1);
   if (rc != XS_OK) return rc;
   if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale))
     return XS_ERR_UNSUPPORTED;
@@ -185,11 +224,20 @@ int xs_attn_fwd_fp8_ws(const void* q8, const void* k8, const void* v8, float q_d
   return launch(a, true, (hipStream_t)stream);
 }
 
+int xs_attn_fwd_fp8_ws(const void* q8, const void* k8, const void* v8, float q_descale,
+                       float k_descale, float v_descale, void* out_packed, int B, int S,
+                       int H_local, int D, int P, float scale, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return xs_attn_fwd_fp8_ex(q8, k8, v8, XS_LAYOUT_BSHD, q_descale, k_descale, v_descale,
+                            out_packed, nullptr, B, S, H_local, D, P, scale, workspace,
+                            workspace_bytes, stream);
+}
+
 int xs_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale,
                     float k_descale, float v_descale, void* out_packed, int B, int S, int H_local,
                     int D, int P, float scale, void* stream) {
-  return xs_attn_fwd_fp8_ws(q8, k8, v8, q_descale, k_descale, v_descale, out_packed, B, S,
-                            H_local, D, P, scale, nullptr, 0, stream);
+  return xs_attn_fwd_fp8_ex(q8, k8, v8, XS_LAYOUT_BSHD, q_descale, k_descale, v_descale,
+                            out_packed, nullptr, B, S, H_local, D, P, scale, nullptr, 0, stream);
 }
 
 size_t xs_attn_workspace_size(int B, int S, int H_local, int D) {
@@ -211,7 +259,8 @@ const char* xs_attn_strerror(int status) {
     case XS_ERR_SHAPE:
       return "invalid shape: B, S, H_local, D and P must be >= 1 and S a multiple of P";
     case XS_ERR_UNSUPPORTED:
-      return "unsupported argument: D must be 64 or 128 and scales finite";
+      return "unsupported argument: D must be 64 or 128, scales finite, the input layout known "
+             "(chunked inputs with B > 1 and P > 1 need S/P to be a multiple of 64)";
     case XS_ERR_ALIGN:
       return "a pointer is not 16-byte aligned";
     case XS_ERR_LAUNCH:

@@ -20,8 +20,8 @@ Q, K, V, O = 0x10000000, 0x20000000, 0x30000000, 0x40000000
 def test_library_exports_every_declared_function():
     names = _lib.declared_functions()
     assert set(names) == {"xs_attn_fwd", "xs_attn_fwd_fp8", "xs_attn_fwd_ws", "xs_attn_fwd_fp8_ws",
-                          "xs_attn_workspace_size", "xs_attn_split_count", "xs_attn_strerror",
-                          "xs_attn_version"}
+                          "xs_attn_fwd_ex", "xs_attn_fwd_fp8_ex", "xs_attn_workspace_size",
+                          "xs_attn_split_count", "xs_attn_strerror", "xs_attn_version"}
     L = _lib.lib()
     for n in names:
         assert getattr(L, n) is not None
@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert xs.xs_attn_version() == 10100
+    assert xs.xs_attn_version() == 10200
     for code in (XS_OK, XS_ERR_NULL, XS_ERR_SHAPE, XS_ERR_UNSUPPORTED, XS_ERR_ALIGN, XS_ERR_LAUNCH,
                  XS_ERR_OVERLAP, XS_ERR_WORKSPACE, 12345):
         s = xs.xs_attn_strerror(code)
@@ -140,3 +140,51 @@ def test_workspace_errors_before_any_launch():
     assert _fwd_ws(W + 8, need) == XS_ERR_ALIGN
     assert _fwd_ws(W, need - 16) == XS_ERR_WORKSPACE
     assert _fwd_ws(W, need, D=96) == XS_ERR_UNSUPPORTED
+
+
+def _fwd_ex(**kw):
+    a = dict(q=Q, k=K, v=V, layout=0, out=O, lse=None, B=2, S=256, H=2, D=64, P=2, scale=0.125)
+    a.update(kw)
+    return xs.xs_attn_fwd_ex(a["q"], a["k"], a["v"], a["layout"], a["out"], a["lse"], a["B"],
+                             a["S"], a["H"], a["D"], a["P"], a["scale"], None, 0, None)
+
+
+def _fwd8_ex(**kw):
+    a = dict(q=Q, k=K, v=V, layout=0, out=O, lse=None, B=2, S=256, H=2, D=64, P=2, scale=0.125)
+    a.update(kw)
+    return xs.xs_attn_fwd_fp8_ex(a["q"], a["k"], a["v"], a["layout"], 0.01, 0.01, 0.01, a["out"],
+                                 a["lse"], a["B"], a["S"], a["H"], a["D"], a["P"], a["scale"], None,
+                                 0, None)
+
+
+@pytest.mark.parametrize("call", [_fwd_ex, _fwd8_ex])
+def test_ex_rejects_unknown_layouts(call):
+    for layout in (-1, 2, 7):
+        assert call(layout=layout) == XS_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("call", [_fwd_ex, _fwd8_ex])
+def test_ex_chunked_inputs_need_whole_key_blocks_per_chunk(call):
+    # B > 1 and P > 1: S/P must be a multiple of 64
+    W = 0x50000000
+    assert call(layout=1, S=192, P=2) == XS_ERR_UNSUPPORTED          # T = 96
+    # T = 576 = 9 * 64 is allowed (a misaligned lse shows the layout check passed)
+    assert call(layout=1, S=4608, P=8, B=3, lse=W + 2) == XS_ERR_ALIGN
+    # with B = 1 or P = 1 the chunk layout is the plain layout: no restriction
+    assert call(layout=1, S=192, P=2, B=1, lse=W + 2) == XS_ERR_ALIGN    # got past the layout check
+    assert call(layout=1, S=192, P=1, B=2, lse=W + 2) == XS_ERR_ALIGN
+
+
+@pytest.mark.parametrize("call", [_fwd_ex, _fwd8_ex])
+def test_ex_lse_alignment_and_overlap(call):
+    W = 0x50000000
+    assert call(lse=W + 2) == XS_ERR_ALIGN
+    assert call(lse=Q) == XS_ERR_OVERLAP
+    assert call(lse=O + 64) == XS_ERR_OVERLAP
+    assert call(lse=V - 4) == XS_ERR_OVERLAP        # the lse range runs into v
+
+
+def test_ex_validates_the_base_arguments_first():
+    assert _fwd_ex(q=0) == XS_ERR_NULL
+    assert _fwd_ex(D=96) == XS_ERR_UNSUPPORTED
+    assert _fwd_ex(out=Q) == XS_ERR_OVERLAP
