@@ -52,6 +52,7 @@ extern "C" {
 #define XS_ERR_LAUNCH (-5)      /* the HIP launch reported an error */
 #define XS_ERR_OVERLAP (-6)     /* out_packed overlaps q, k or v */
 #define XS_ERR_WORKSPACE (-7)   /* workspace smaller than xs_attn_workspace_size() */
+/* (XS_ERR_UNSUPPORTED also when B*H_local*ceil(S/256) exceeds 2^31 - 1 query tiles.) */
 
 /* Attention forward over bf16 inputs with the destination-ordered epilogue.
  *   q, k, v     bf16 [B][S][H_local][D], device memory (read only)
@@ -71,22 +72,29 @@ int xs_attn_fwd_fp8(const void *q8, const void *k8, const void *v8, float q_desc
                     float k_descale, float v_descale, void *out_packed, int B, int S, int H_local,
                     int D, int P, float scale, void *stream);
 
-/* Split-key variants.  When the grid of 256-row query tiles would leave compute
- * units idle (few heads, or a last partial round of tiles), the key range of
- * every tile is cut into nsplit chunks processed by separate workgroups; each
- * writes unnormalised fp32 partials (O and, per row, the running max and row
- * sum) into `workspace`, and a second kernel on the same stream merges them
- * with the online-softmax rule into out_packed.  This is the merge of partial
+/* Scheduled variants.  The work of a call is a sequence of units (one 256-row
+ * query tile x two 64-key blocks).  The library chooses, per shape and device, a
+ * number of workgroups that share the units equally: one per tile (nothing to
+ * merge), k equal key-range pieces per tile, or one persistent workgroup per
+ * compute unit walking an equal contiguous share -- so tile outputs finish at
+ * staggered times rather than in lockstep rounds, and a workgroup requests its
+ * next tile's first K/V blocks and queries before it stores the current one
+ * (X-Stage paper, gist.science explainer, "FlashAttention-A2A (Piggybacking)":
+ * the tile owner stores its output and immediately resumes the next tile's
+ * loop).  A tile whose key range is shared by several workgroups is cut: each
+ * piece writes unnormalised fp32 partials (O and, per row, the running max and
+ * row sum) into `workspace`, and a second kernel on the same stream merges them
+ * with the online-softmax rule into out_packed -- the merge of partial
  * attention by online softmax of "Move the Query, Not the Cache" (gist.science
  * explainer, Methodik: the Route primitive), applied inside one GPU.
  *   workspace        device memory, 16-byte aligned, at least
  *                    xs_attn_workspace_size(B, S, H_local, D) bytes; owned by the
  *                    caller, not retained after the call; its contents are
- *                    scratch (overwritten).  Calls that overlap in time must not
- *                    share a workspace.
- *   workspace NULL   run without splitting (identical to xs_attn_fwd).
- * Results differ from the unsplit call only by rounding (the splits are merged
- * in a fixed order, so they are deterministic); they do not depend on P.
+ *                    scratch (overwritten, never read before written).  Calls
+ *                    that overlap in time must not share a workspace.
+ *   workspace NULL   no tile is cut (identical to xs_attn_fwd).
+ * Results differ from the uncut schedule only by rounding (pieces are merged in
+ * key order, so they are deterministic); they do not depend on P.
  * Returns XS_ERR_WORKSPACE if workspace is non-NULL but too small. */
 int xs_attn_fwd_ws(const void *q, const void *k, const void *v, void *out_packed, int B, int S,
                    int H_local, int D, int P, float scale, void *workspace,
@@ -131,13 +139,13 @@ int xs_attn_fwd_fp8_ex(const void *q8, const void *k8, const void *v8, int in_la
                        float *lse, int B, int S, int H_local, int D, int P, float scale,
                        void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace the split-key variants need on the current device for this
- * shape (0: the shape is run unsplit).  Depends on the device's compute-unit
- * count; returns 0 for invalid sizes.  No allocation, no kernel launch. */
+/* Bytes of workspace the scheduled variants need on the current device for this
+ * shape (0: no tile is cut).  Depends on the device's compute-unit count;
+ * returns 0 for invalid sizes.  No allocation, no kernel launch. */
 size_t xs_attn_workspace_size(int B, int S, int H_local, int D);
 
-/* The number of key-range splits the split-key variants use for this shape on
- * the current device (1 = unsplit); 0 for invalid sizes. */
+/* The most pieces the scheduled variants cut any query tile into for this shape
+ * on the current device (1 = no tile is cut); 0 for invalid sizes. */
 int xs_attn_split_count(int B, int S, int H_local, int D);
 
 /* Static, never-NULL description of a status code. */

@@ -1,44 +1,60 @@
-// attn_combine.hip -- merges the fp32 partial results of a key range split
-// into the bf16 destination-ordered output.
+// attn_combine.hip -- merges the fp32 partial results of the query tiles that
+// the work schedule cut between workgroups into the bf16 destination-ordered
+// output.
 //
-// Each split s of a query row holds O_s = sum_j 2^(s_j c - m_s) v_j (not
+// Each piece s of a query row holds O_s = sum_j 2^(s_j c - m_s) v_j (not
 // normalised), its running max m_s (log2 units) and row sum l_s.  The row is
 //   M = max_s m_s,  w_s = 2^(m_s - M),  O = sum_s w_s O_s / sum_s w_s l_s,
 // the online-softmax merge of partial attention ("Move the Query, Not the
 // Cache", gist.science explainer: Methodik, the Route primitive merges partial
-// attention computed at the owner with an online softmax).  The splits are
-// summed in a fixed order, so the result is deterministic.  The row's
+// attention computed at the owner with an online softmax).  The pieces are
+// summed in key order, so the result is deterministic.  The row's
 // log-sum-exp, when asked for, is ln(2^M L) with L = sum_s w_s l_s.
 #include "attn_launch.h"
 #include "device_common.h"
 
 namespace xs {
 
+// One workgroup per RPB rows of one query tile.  Tiles held whole by one chunk
+// of the schedule were stored by the attention kernel: those workgroups exit.
+// For a cut tile the pieces are, in key order, the last piece of the chunk
+// that owns its first unit (slot 2c+1, or 2c if that chunk starts exactly at
+// the tile) and the first piece of every later chunk up to the owner of its
+// last unit (slot 2c).
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int LPR = D / 4;             // lanes per row, 4 consecutive d each
   constexpr int RPB = 256 / LPR;         // rows per workgroup
-  const size_t rows = (size_t)a.B * a.H * a.S;
-  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  if (row >= rows) return;
+  constexpr int GPT = kBlockM / RPB;     // workgroups per tile
+  const Sched sch{a.units, a.groups, a.npair};
+  const int tile = blockIdx.x / GPT;
+  const long long u0 = (long long)tile * a.npair, u1 = u0 + a.npair - 1;
+  const int c_lo = sch.owner(u0), c_hi = sch.owner(u1);
+  if (c_lo == c_hi) return;
+  const int mtiles = (a.S + kBlockM - 1) / kBlockM;
+  const int bh = tile / mtiles;
+  const int r = (blockIdx.x % GPT) * RPB + threadIdx.x / LPR;  // row within the tile
+  const int srow = (tile - bh * mtiles) * kBlockM + r;
+  if (srow >= a.S) return;
   const int d0 = (threadIdx.x % LPR) * 4;
+  // every share holds at least one unit (the plan keeps groups <= units)
+  const size_t first = 2 * (size_t)c_lo + (sch.start(c_lo) < u0 ? 1 : 0);
+  auto slot_of = [&](int c) { return c == c_lo ? first : 2 * (size_t)c; };
 
   float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_ml[2 * ((size_t)s * rows + row)]);
+  for (int c = c_lo; c <= c_hi; ++c) M = fmaxf(M, a.ws_ml[2 * (slot_of(c) * kBlockM + r)]);
   float L = 0.0f;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int s = 0; s < a.nsplit; ++s) {
-    const size_t r = (size_t)s * rows + row;
-    const f32x2 ml = *(const f32x2*)(a.ws_ml + 2 * r);
+  for (int c = c_lo; c <= c_hi; ++c) {
+    const size_t sr = slot_of(c) * kBlockM + r;
+    const f32x2 ml = *(const f32x2*)(a.ws_ml + 2 * sr);
     const float w = fast_exp2(ml[0] - M);
     L += w * ml[1];
-    acc += w * *(const f32x4*)(a.ws_o + r * D + d0);
+    acc += w * *(const f32x4*)(a.ws_o + sr * D + d0);
   }
   const float inv = a.o_scale / L;
-  if (a.lse && d0 == 0) a.lse[row] = row_lse(M, L);
+  if (a.lse && d0 == 0) a.lse[(size_t)bh * a.S + srow] = row_lse(M, L);
   const int S = a.S, H = a.H, T = a.T;
-  const int srow = (int)(row % S);
-  const int bh = (int)(row / S);
   const int h = bh % H, b = bh / H;
   const int p = srow / T;
   const int sp = srow - p * T;
@@ -49,9 +65,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 template <int D>
 static hipError_t launch_combine_d(const AttnArgs& a, hipStream_t stream) {
   constexpr int RPB = 256 / (D / 4);
-  const size_t rows = (size_t)a.B * a.H * a.S;
-  const size_t blocks = (rows + RPB - 1) / RPB;
-  if (blocks > 0x7fffffffULL) return hipErrorInvalidValue;
+  const long long blocks = a.units / a.npair * (kBlockM / RPB);
+  if (blocks < 1 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   AttnArgs args = a;
   void* kargs[] = {&args};
   return hipLaunchKernel((const void*)attn_combine_kernel<D>, dim3((unsigned)blocks), dim3(256), kargs, 0,

@@ -35,6 +35,7 @@
 //    reduction order never depend on P; only the store address does.
 #include "attn_launch.h"
 #include "device_common.h"
+#include "piece.h"
 
 #ifndef XS_QT
 #define XS_QT 1
@@ -472,175 +473,212 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, co
   }
 }
 
+// Decodes the piece that starts at unit u of a chunk ending at uend and issues
+// its first loads (K and V of block jb into stage 0, K of jb+1 into stage 1).
+template <class C>
+__device__ __forceinline__ PieceAddr begin_piece(const AttnArgs& a, long long u, long long uend,
+                                                 int nblk, uint32_t row_stride, uint8_t XS_LDS* lds,
+                                                 const uint32_t (&koff)[C::LPW],
+                                                 const uint32_t (&voff)[C::LPW], int wave) {
+  PieceAddr pa = decode_piece<C::BM, C::ROWB>(a, u, uend, nblk, row_stride);
+  const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
+  const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
+  load_tile<C>(kbase, row_stride, pa.jb * C::BN, pa.kcur.at(pa.jb), a.S, lds, koff, wave);
+  load_tile<C>(vbase, row_stride, pa.jb * C::BN, pa.vcur.at(pa.jb), a.S, lds + 2 * C::TILE, voff,
+               wave);
+  if (pa.jb + 1 < pa.je)
+    load_tile<C>(kbase, row_stride, (pa.jb + 1) * C::BN, pa.kcur.at(pa.jb + 1), a.S, lds + C::TILE,
+                 koff, wave);
+  return pa;
+}
+
+// Loads the piece's query rows (clamped to the sequence) as Q^T B-operand
+// fragments, negated when the scale is negative.
+template <class C>
+__device__ __forceinline__ void load_q(u32x4 (&qf)[C::QT][C::KS], const AttnArgs& a,
+                                       const PieceAddr& pa, uint32_t row_stride, uint32_t qflip,
+                                       int wave, int lane) {
+#pragma unroll
+  for (int qt = 0; qt < C::QT; ++qt) {
+    int qrow = pa.m0 + wave * C::QW + qt * 32 + (lane & 31);
+    qrow = qrow < a.S ? qrow : a.S - 1;
+    const long long qr = qrow + (a.chunk_rows ? (long long)(qrow / a.chunk_rows) * a.jump_rows : 0);
+    const uint8_t* qp = (const uint8_t*)a.q + pa.head_off + (size_t)qr * row_stride + (lane >> 5) * 16;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qf[qt][ks] = *(const u32x4*)(qp + ks * 32) ^ qflip;
+  }
+}
+
+// Persistent workgroups: each walks its chunk of the schedule (attn_launch.h,
+// Sched) piece by piece.  Chunks are equal shares of the (tile, key-block pair)
+// sequence, so the workgroups finish their tiles at staggered times instead of
+// in lockstep rounds, and only tiles cut between two chunks need a merge.
+// Before a piece's output stores, the next piece's first K/V blocks are
+// already requested, so the stores drain while those loads are in flight.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel(AttnArgs a) {
-  constexpr int QT = C::QT, KS = C::KS, DT = C::DT, BM = C::BM, BN = C::BN;
+  constexpr int QT = C::QT, DT = C::DT, BN = C::BN;
   // K stage 0 | K stage 1 | V stage 0 | V stage 1
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];
   uint8_t XS_LDS* const lds = (uint8_t XS_LDS*)smem;
   auto kbuf = [&](int i) { return lds + (i & 1) * C::TILE; };
   auto vbuf = [&](int i) { return lds + (2 + (i & 1)) * C::TILE; };
 
-  const int S = a.S, H = a.H;
-  const int mtiles = (S + BM - 1) / BM;
-  const int nsplit = a.nsplit;
-  // work item = ((b*H + h)*nsplit + split)*mtiles + m-tile, XCD-aware order: the
-  // items resident on one XCD at once share a head and a key range
-  const int item = xcd_tile(blockIdx.x, a.B * H * nsplit * mtiles);
-  const int mt = item % mtiles;
-  const int split = (item / mtiles) % nsplit;
-  const int bh = item / (mtiles * nsplit);
-  const int h = bh % H, b = bh / H;
+  const int S = a.S, H = a.H, T = a.T, B = a.B;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int m0 = mt * BM;
-
   const uint32_t row_stride = (uint32_t)H * C::ROWB;  // bytes between consecutive rows
-  const size_t head_off = ((size_t)b * a.batch_rows * H + h) * C::ROWB;
-  const uint8_t* kbase = (const uint8_t*)a.k + head_off;
-  const uint8_t* vbase = (const uint8_t*)a.v + head_off;
   uint32_t koff[C::LPW], voff[C::LPW];
   tile_offsets<C, false>(row_stride, wave, lane, koff);
   tile_offsets<C, true>(row_stride, wave, lane, voff);
-
   const int nblk = (S + BN - 1) / BN;
   const int nfull = S / BN;  // blocks with no key past the end of the sequence
-  const int jb = split * a.nb_per;                                // this item's key blocks
-  const int je = jb + a.nb_per < nblk ? jb + a.nb_per : nblk;    // [jb, je)
-  ChunkCursor kcur, vcur;
-  kcur.init(jb, a.chunk_rows, a.jump_rows, row_stride);
-  vcur.init(jb, a.chunk_rows, a.jump_rows, row_stride);
-  load_tile<C>(kbase, row_stride, jb * BN, kcur.at(jb), S, kbuf(jb), koff, wave);
-  load_tile<C>(vbase, row_stride, jb * BN, vcur.at(jb), S, vbuf(jb), voff, wave);
-  if (jb + 1 < je)
-    load_tile<C>(kbase, row_stride, (jb + 1) * BN, kcur.at(jb + 1), S, kbuf(jb + 1), koff, wave);
-
-  Bf16State<C> st;
   const uint32_t qflip = a.neg ? 0x80008000u : 0u;
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    int qrow = m0 + wave * C::QW + qt * 32 + (lane & 31);
-    qrow = qrow < S ? qrow : S - 1;
-    const long long qr = qrow + (a.chunk_rows ? (long long)(qrow / a.chunk_rows) * a.jump_rows : 0);
-    const uint8_t* qp = (const uint8_t*)a.q + head_off + (size_t)qr * row_stride + (lane >> 5) * 16;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 t = *(const u32x4*)(qp + ks * 32);
-      st.qf[qt][ks] = t ^ qflip;
-    }
-    st.m[qt] = -INFINITY;
-    st.l[qt] = 0.0f;
-    st.alpha[qt] = 1.0f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st.o[qt][dt] = f32x16{};
-  }
-  st.rescale = false;
   const float c = a.c;
-
-  wait_vmcnt<0>();
-  __syncthreads();
-
-  // prologue: score block 0 and take its max
-  Scores<C> sa, sb;
-  qk_block<C>(sa, st, kbuf(jb), lane);
-  if (jb >= nfull) mask_tail<C>(sa, jb * BN, S, lane);
-  softmax_max<C>(st, sa, c);
-
-  // Steady state, two blocks per trip so the score buffers swap statically.
-  // Entering a step for block i: scores of block i are in one buffer with
-  // their max taken; K_{i+1} and V_i are loaded (or in flight).
-  // (jb is even: K_i and V_i live in stage i % 2)
   const LdsOffs<C> off = lds_offsets<C>(lane);
-  int j = jb;
-  for (; j + 2 < je; j += 2) {
-    // ---- block j (scores in sa), next block's scores into sb
-    wait_vmcnt<0>();
-    __syncthreads();
-    load_tile<C>(kbase, row_stride, (j + 2) * BN, kcur.at(j + 2), S, kbuf(0), koff, wave);
-    load_tile<C>(vbase, row_stride, (j + 1) * BN, vcur.at(j + 1), S, vbuf(1), voff, wave);
-    step1<C, 1>(sb, sa, st, lds, off, c);
-    if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
-    step2<C, 0>(st, sb, sa, lds, off, c);
 
-    // ---- block j+1 (scores in sb), next block's scores into sa
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (j + 3 < je)
-      load_tile<C>(kbase, row_stride, (j + 3) * BN, kcur.at(j + 3), S, kbuf(1), koff, wave);
-    load_tile<C>(vbase, row_stride, (j + 2) * BN, vcur.at(j + 2), S, vbuf(0), voff, wave);
-    step1<C, 0>(sa, sb, st, lds, off, c);
-    if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
-    step2<C, 1>(st, sa, sb, lds, off, c);
-  }
-  // the last one or two blocks (scores of block j in sa)
-  if (j + 1 < je) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    load_tile<C>(vbase, row_stride, (j + 1) * BN, vcur.at(j + 1), S, vbuf(j + 1), voff, wave);
-    qk_block<C>(sb, st, kbuf(j + 1), lane);
-    softmax_exp<C>(st, sa, c);
-    __builtin_amdgcn_sched_barrier(0);
-    if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
-    pv_block<C>(st, vbuf(j), lane);
-    softmax_max<C>(st, sb, c);
-    wait_vmcnt<0>();
-    __syncthreads();
-    softmax_exp<C>(st, sb, c);
-    pv_block<C>(st, vbuf(j + 1), lane);
-  } else {
-    wait_vmcnt<0>();  // V_j may have been issued by the last loop step
-    __syncthreads();
-    softmax_exp<C>(st, sa, c);
-    pv_block<C>(st, vbuf(j), lane);
-  }
+  // this workgroup's chunk; the workgroups of one XCD take consecutive chunks
+  const Sched sch{a.units, a.groups, a.npair};
+  const int chunk = xcd_tile(blockIdx.x, a.groups);
+  long long u = sch.start(chunk);
+  const long long uend = sch.start(chunk + 1);
+  if (u >= uend) return;
+  PieceAddr pa = begin_piece<C>(a, u, uend, nblk, row_stride, lds, koff, voff, wave);
+  Bf16State<C> st;
+  load_q<C>(st.qf, a, pa, row_stride, qflip, wave, lane);
 
-  // ---- epilogue
-  const int T = a.T, B = a.B;
-  if (nsplit == 1) {
-    // normalise, round to bf16, store into the destination slice
+  for (int piece = 0;; ++piece) {
+    const int jb = pa.jb, je = pa.je, m0 = pa.m0;
+    const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
+    const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
+
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const float lrow = sum_halves(st.l[qt]);
-      const float inv = a.o_scale / lrow;
-      const int srow = m0 + wave * C::QW + qt * 32 + (lane & 31);
-      if (a.lse && lane < 32 && srow < S) a.lse[(size_t)bh * S + srow] = row_lse(st.m[qt], lrow);
-      if (srow < S) {
-        const int p = srow / T;
-        const int sp = srow - p * T;
-        uint16_t* orow = (uint16_t*)a.out + ((((size_t)p * B + b) * T + sp) * H + h) * C::D;
+      st.m[qt] = -INFINITY;
+      st.l[qt] = 0.0f;
+      st.alpha[qt] = 1.0f;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt) st.o[qt][dt] = f32x16{};
+    }
+    st.rescale = false;
+
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    // prologue: score block jb and take its max
+    Scores<C> sa, sb;
+    qk_block<C>(sa, st, kbuf(jb), lane);
+    if (jb >= nfull) mask_tail<C>(sa, jb * BN, S, lane);
+    softmax_max<C>(st, sa, c);
+
+    // Steady state, two blocks per trip so the score buffers swap statically.
+    // Entering a step for block i: scores of block i are in one buffer with
+    // their max taken; K_{i+1} and V_i are loaded (or in flight).
+    // (jb is even: K_i and V_i live in stage i % 2)
+    int j = jb;
+    for (; j + 2 < je; j += 2) {
+      // ---- block j (scores in sa), next block's scores into sb
+      wait_vmcnt<0>();
+      __syncthreads();
+      load_tile<C>(kbase, row_stride, (j + 2) * BN, pa.kcur.at(j + 2), S, kbuf(0), koff, wave);
+      load_tile<C>(vbase, row_stride, (j + 1) * BN, pa.vcur.at(j + 1), S, vbuf(1), voff, wave);
+      step1<C, 1>(sb, sa, st, lds, off, c);
+      if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
+      step2<C, 0>(st, sb, sa, lds, off, c);
+
+      // ---- block j+1 (scores in sb), next block's scores into sa
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (j + 3 < je)
+        load_tile<C>(kbase, row_stride, (j + 3) * BN, pa.kcur.at(j + 3), S, kbuf(1), koff, wave);
+      load_tile<C>(vbase, row_stride, (j + 2) * BN, pa.vcur.at(j + 2), S, vbuf(0), voff, wave);
+      step1<C, 0>(sa, sb, st, lds, off, c);
+      if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
+      step2<C, 1>(st, sa, sb, lds, off, c);
+    }
+    // the last one or two blocks (scores of block j in sa)
+    if (j + 1 < je) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      load_tile<C>(vbase, row_stride, (j + 1) * BN, pa.vcur.at(j + 1), S, vbuf(j + 1), voff, wave);
+      qk_block<C>(sb, st, kbuf(j + 1), lane);
+      softmax_exp<C>(st, sa, c);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
+      pv_block<C>(st, vbuf(j), lane);
+      softmax_max<C>(st, sb, c);
+      wait_vmcnt<0>();
+      __syncthreads();
+      softmax_exp<C>(st, sb, c);
+      pv_block<C>(st, vbuf(j + 1), lane);
+    } else {
+      wait_vmcnt<0>();  // V_j may have been issued by the last loop step
+      __syncthreads();
+      softmax_exp<C>(st, sa, c);
+      pv_block<C>(st, vbuf(j), lane);
+    }
+
+    // ---- next piece: request its first K/V blocks and its queries before
+    // this piece's stores (this piece's Q fragments are no longer needed)
+    u += piece_units(pa);
+    const bool more = u < uend;
+    const PieceAddr cur = pa;
+    if (more) {
+      __syncthreads();  // every wave is done reading this piece's tiles
+      pa = begin_piece<C>(a, u, uend, nblk, row_stride, lds, koff, voff, wave);
+      load_q<C>(st.qf, a, pa, row_stride, qflip, wave, lane);
+    }
+
+    // ---- epilogue
+    if (cur.whole) {
+      // normalise, round to bf16, store into the destination slice
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int d0 = dt * 32 + r4 * 8 + 4 * (lane >> 5);
-            const f32x16& o = st.o[qt][dt];
-            u32x2 w = {pack_bf16(o[4 * r4 + 0] * inv, o[4 * r4 + 1] * inv),
-                       pack_bf16(o[4 * r4 + 2] * inv, o[4 * r4 + 3] * inv)};
-            *(u32x2*)(orow + d0) = w;
-          }
+      for (int qt = 0; qt < QT; ++qt) {
+        const float lrow = sum_halves(st.l[qt]);
+        const float inv = a.o_scale / lrow;
+        const int srow = m0 + wave * C::QW + qt * 32 + (lane & 31);
+        if (a.lse && lane < 32 && srow < S) a.lse[(size_t)cur.bh * S + srow] = row_lse(st.m[qt], lrow);
+        if (srow < S) {
+          const int p = srow / T;
+          const int sp = srow - p * T;
+          uint16_t* orow = (uint16_t*)a.out + ((((size_t)p * B + cur.b) * T + sp) * H + cur.h) * C::D;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int d0 = dt * 32 + r4 * 8 + 4 * (lane >> 5);
+              const f32x16& o = st.o[qt][dt];
+              u32x2 w = {pack_bf16(o[4 * r4 + 0] * inv, o[4 * r4 + 1] * inv),
+                         pack_bf16(o[4 * r4 + 2] * inv, o[4 * r4 + 3] * inv)};
+              *(u32x2*)(orow + d0) = w;
+            }
+        }
+      }
+    } else {
+      // a tile cut between chunks: unnormalised fp32 partials into this
+      // chunk's slot (2*chunk for its first piece, 2*chunk+1 for its last),
+      // merged by attn_combine
+      const size_t slot = 2 * (size_t)chunk + (piece > 0 ? 1 : 0);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float lsum = sum_halves(st.l[qt]);
+        const int r = wave * C::QW + qt * 32 + (lane & 31);  // row within the tile
+        if (m0 + r < S) {
+          const size_t sr = slot * C::BM + r;
+          float* orow = a.ws_o + sr * C::D;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x16& o = st.o[qt][dt];
+              *(f32x4*)(orow + dt * 32 + r4 * 8 + 4 * (lane >> 5)) =
+                  f32x4{o[4 * r4 + 0], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]};
+            }
+          if (lane < 32) *(f32x2*)(a.ws_ml + 2 * sr) = f32x2{st.m[qt], lsum};
+        }
       }
     }
-  } else {
-    // unnormalised fp32 partials of this key range, merged by attn_combine
-    const size_t rows = (size_t)B * H * S;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float lsum = sum_halves(st.l[qt]);
-      const int srow = m0 + wave * C::QW + qt * 32 + (lane & 31);
-      if (srow < S) {
-        const size_t r = (size_t)split * rows + (size_t)bh * S + srow;
-        float* orow = a.ws_o + r * C::D;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x16& o = st.o[qt][dt];
-            *(f32x4*)(orow + dt * 32 + r4 * 8 + 4 * (lane >> 5)) =
-                f32x4{o[4 * r4 + 0], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]};
-          }
-        if (lane < 32) *(f32x2*)(a.ws_ml + 2 * r) = f32x2{st.m[qt], lsum};
-      }
-    }
+    if (!more) break;
   }
 }
 
@@ -648,13 +686,11 @@ template <int D>
 static hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   using C = Bf16Cfg<D, XS_QT, XS_NW, XS_BN>;
   static_assert(C::BM == kBlockM && C::BN == kBlockN, "tile geometry");
-  const int mtiles = (a.S + C::BM - 1) / C::BM;
-  const long long items = (long long)a.B * a.H * a.nsplit * mtiles;
-  if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (a.groups < 1) return hipErrorInvalidValue;
   AttnArgs args = a;
   void* kargs[] = {&args};
-  return hipLaunchKernel((const void*)attn_fwd_bf16_kernel<C>, dim3((unsigned)items), dim3(C::THREADS),
-                         kargs, 0, stream);
+  return hipLaunchKernel((const void*)attn_fwd_bf16_kernel<C>, dim3((unsigned)a.groups),
+                         dim3(C::THREADS), kargs, 0, stream);
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream) {

@@ -21,6 +21,7 @@
 //  * Row sums add the fp32 probabilities before quantisation.
 #include "attn_launch.h"
 #include "device_common.h"
+#include "piece.h"
 
 namespace xs {
 
@@ -336,30 +337,56 @@ __device__ __forceinline__ void pv_only8(Fp8State<C>& st, const uint8_t XS_LDS* 
   }
 }
 
+// Decodes the piece that starts at unit u of a chunk ending at uend and issues
+// its first loads (K and V of block jb into stage 0, K of jb+1 into stage 1).
+template <class C>
+__device__ __forceinline__ PieceAddr begin_piece8(const AttnArgs& a, long long u, long long uend,
+                                                  int nblk, uint32_t row_stride,
+                                                  uint8_t XS_LDS* lds, uint32_t koff,
+                                                  uint32_t voff, int wave) {
+  PieceAddr pa = decode_piece<C::BM, C::ROWB>(a, u, uend, nblk, row_stride);
+  const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
+  const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
+  load_tile8<C>(kbase, row_stride, pa.jb * C::BN, pa.kcur.at(pa.jb), a.S, lds, koff, wave);
+  load_tile8<C>(vbase, row_stride, pa.jb * C::BN, pa.vcur.at(pa.jb), a.S, lds + 2 * C::TILE, voff,
+                wave);
+  if (pa.jb + 1 < pa.je)
+    load_tile8<C>(kbase, row_stride, (pa.jb + 1) * C::BN, pa.kcur.at(pa.jb + 1), a.S,
+                  lds + C::TILE, koff, wave);
+  return pa;
+}
+
+// Loads the piece's query rows (clamped to the sequence) as Q^T B-operand
+// fragments, negated when the scale is negative.
+template <class C>
+__device__ __forceinline__ void load_q8(i32x8 (&qf)[C::KS], const AttnArgs& a, const PieceAddr& pa,
+                                        uint32_t row_stride, uint32_t qflip, int wave, int lane) {
+  int qrow = pa.m0 + wave * C::QW + (lane & 31);
+  qrow = qrow < a.S ? qrow : a.S - 1;
+  const long long qr = qrow + (a.chunk_rows ? (long long)(qrow / a.chunk_rows) * a.jump_rows : 0);
+  const uint8_t* qp = (const uint8_t*)a.q + pa.head_off + (size_t)qr * row_stride + (lane >> 5) * 32;
+#pragma unroll
+  for (int t = 0; t < C::KS; ++t) {
+    const u32x4 x0 = *(const u32x4*)(qp + t * 64) ^ qflip;
+    const u32x4 x1 = *(const u32x4*)(qp + t * 64 + 16) ^ qflip;
+    qf[t] = __builtin_bit_cast(i32x8, (u32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}));
+  }
+}
+
+// Persistent workgroups walking their chunk of the schedule piece by piece, as
+// in the bf16 kernel (attn_fwd_bf16.hip).
 template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a) {
-  constexpr int BM = C::BM, BN = C::BN;
+  constexpr int BN = C::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];
   uint8_t XS_LDS* const lds = (uint8_t XS_LDS*)smem;
   auto kbuf = [&](int i) { return lds + (i & 1) * C::TILE; };
   auto vbuf = [&](int i) { return lds + (2 + (i & 1)) * C::TILE; };
 
-  const int S = a.S, H = a.H;
-  const int mtiles = (S + BM - 1) / BM;
-  const int nsplit = a.nsplit;
-  const int item = xcd_tile(blockIdx.x, a.B * H * nsplit * mtiles);
-  const int mt = item % mtiles;
-  const int split = (item / mtiles) % nsplit;
-  const int bh = item / (mtiles * nsplit);
-  const int h = bh % H, b = bh / H;
+  const int S = a.S, H = a.H, T = a.T, B = a.B;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int m0 = mt * BM;
-
   const uint32_t row_stride = (uint32_t)H * C::ROWB;
-  const size_t head_off = ((size_t)b * a.batch_rows * H + h) * C::ROWB;
-  const uint8_t* kbase = (const uint8_t*)a.k + head_off;
-  const uint8_t* vbase = (const uint8_t*)a.v + head_off;
   // this lane's 16-byte chunk of the wave's 1 KiB direct load, for K and V
   uint32_t koff, voff;
   {
@@ -368,132 +395,138 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
     koff = (uint32_t)R * row_stride + (uint32_t)((cp ^ kswz<C>(R)) * 16);
     voff = (uint32_t)vrow_key(R) * row_stride + (uint32_t)((cp ^ vswz<C>(R)) * 16);
   }
-
   const int nblk = (S + BN - 1) / BN;
   const int nfull = S / BN;
-  const int jb = split * a.nb_per;
-  const int je = jb + a.nb_per < nblk ? jb + a.nb_per : nblk;
-  ChunkCursor kcur, vcur;
-  kcur.init(jb, a.chunk_rows, a.jump_rows, row_stride);
-  vcur.init(jb, a.chunk_rows, a.jump_rows, row_stride);
-  load_tile8<C>(kbase, row_stride, jb * BN, kcur.at(jb), S, kbuf(jb), koff, wave);
-  load_tile8<C>(vbase, row_stride, jb * BN, vcur.at(jb), S, vbuf(jb), voff, wave);
-  if (jb + 1 < je)
-    load_tile8<C>(kbase, row_stride, (jb + 1) * BN, kcur.at(jb + 1), S, kbuf(jb + 1), koff, wave);
-
-  Fp8State<C> st;
-  {
-    const uint32_t qflip = a.neg ? 0x80808080u : 0u;
-    int qrow = m0 + wave * C::QW + (lane & 31);
-    qrow = qrow < S ? qrow : S - 1;
-    const long long qr = qrow + (a.chunk_rows ? (long long)(qrow / a.chunk_rows) * a.jump_rows : 0);
-    const uint8_t* qp = (const uint8_t*)a.q + head_off + (size_t)qr * row_stride + (lane >> 5) * 32;
-#pragma unroll
-    for (int t = 0; t < C::KS; ++t) {
-      const u32x4 x0 = *(const u32x4*)(qp + t * 64) ^ qflip;
-      const u32x4 x1 = *(const u32x4*)(qp + t * 64 + 16) ^ qflip;
-      st.qf[t] = __builtin_bit_cast(i32x8, (u32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}));
-    }
-  }
-  st.m = -INFINITY;
-  st.l = 0.0f;
-  st.alpha = 1.0f;
-  st.rescale = false;
-#pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) st.o[dt] = f32x16{};
+  const uint32_t qflip = a.neg ? 0x80808080u : 0u;
   const float c = a.c;
-
-  wait_vmcnt<0>();
-  __syncthreads();
-
-  // prologue: score block jb, take its max, probabilities of its keys 0..31
-  Scores8<C> sa, sb;
-  qk_block8<C>(sa, st, kbuf(jb), lane);
-  if (jb >= nfull) mask_tail8<C>(sa, jb * BN, S, lane);
-  softmax_max8<C>(st, sa, c);
-  exp_tile8<C>(st, sa, 0, c, st.p0);
-
-  // Steady state, two blocks per trip so the score buffers swap statically.
-  // Entering the trip for block i: its scores are in one buffer with their max
-  // taken and the probabilities of keys 0..31 in st.p0; K_{i+1} and V_i are
-  // loaded or in flight.  (jb is even: K_i and V_i live in stage i % 2.)
   const LdsOffs8<C> off = lds_offsets8<C>(lane);
-  int j = jb;
-  for (; j + 2 < je; j += 2) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    load_tile8<C>(kbase, row_stride, (j + 2) * BN, kcur.at(j + 2), S, kbuf(0), koff, wave);
-    load_tile8<C>(vbase, row_stride, (j + 1) * BN, vcur.at(j + 1), S, vbuf(1), voff, wave);
-    step_a8<C, 1>(sb, sa, st, lds, off, c);
-    if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
-    step_b8<C, 0>(st, sb, lds, off, c);
+
+  const Sched sch{a.units, a.groups, a.npair};
+  const int chunk = xcd_tile(blockIdx.x, a.groups);
+  long long u = sch.start(chunk);
+  const long long uend = sch.start(chunk + 1);
+  if (u >= uend) return;
+  PieceAddr pa = begin_piece8<C>(a, u, uend, nblk, row_stride, lds, koff, voff, wave);
+  Fp8State<C> st;
+  load_q8<C>(st.qf, a, pa, row_stride, qflip, wave, lane);
+
+  for (int piece = 0;; ++piece) {
+    const int jb = pa.jb, je = pa.je, m0 = pa.m0;
+    const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
+    const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
+
+    st.m = -INFINITY;
+    st.l = 0.0f;
+    st.alpha = 1.0f;
+    st.rescale = false;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) st.o[dt] = f32x16{};
 
     wait_vmcnt<0>();
     __syncthreads();
-    if (j + 3 < je)
-      load_tile8<C>(kbase, row_stride, (j + 3) * BN, kcur.at(j + 3), S, kbuf(1), koff, wave);
-    load_tile8<C>(vbase, row_stride, (j + 2) * BN, vcur.at(j + 2), S, vbuf(0), voff, wave);
-    step_a8<C, 0>(sa, sb, st, lds, off, c);
-    if (j + 2 >= nfull) mask_tail8<C>(sa, (j + 2) * BN, S, lane);
-    step_b8<C, 1>(st, sa, lds, off, c);
-  }
-  // the last one or two blocks (j is even; scores of block j in sa)
-  if (j + 1 < je) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    load_tile8<C>(vbase, row_stride, (j + 1) * BN, vcur.at(j + 1), S, vbuf(1), voff, wave);
-    step_a8<C, 1>(sb, sa, st, lds, off, c);
-    if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
-    step_b8<C, 0>(st, sb, lds, off, c);
-    wait_vmcnt<0>();
-    __syncthreads();
-    exp_tile8<C>(st, sb, 1, c, st.p1);
-    pv_only8<C, 1>(st, lds, off);
-  } else {
-    wait_vmcnt<0>();  // V_j may have been issued by the last loop trip
-    __syncthreads();
-    exp_tile8<C>(st, sa, 1, c, st.p1);
-    pv_only8<C, 0>(st, lds, off);
-  }
 
-  // ---- epilogue
-  const int T = a.T, B = a.B;
-  const int srow = m0 + wave * C::QW + (lane & 31);
-  if (nsplit == 1) {
-    // O * dv / l, rounded to bf16, stored into the destination slice
-    const float lrow = sum_halves(st.l);
-    const float inv = a.o_scale / lrow;
-    if (a.lse && lane < 32 && srow < S) a.lse[(size_t)bh * S + srow] = row_lse(st.m, lrow);
-    if (srow < S) {
-      const int p = srow / T;
-      const int sp = srow - p * T;
-      uint16_t* orow = (uint16_t*)a.out + ((((size_t)p * B + b) * T + sp) * H + h) * C::D;
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = dt * 32 + r4 * 8 + 4 * (lane >> 5);
-          const f32x16& o = st.o[dt];
-          u32x2 w = {pack_bf16(o[4 * r4 + 0] * inv, o[4 * r4 + 1] * inv),
-                     pack_bf16(o[4 * r4 + 2] * inv, o[4 * r4 + 3] * inv)};
-          *(u32x2*)(orow + d0) = w;
-        }
+    // prologue: score block jb, take its max, probabilities of its keys 0..31
+    Scores8<C> sa, sb;
+    qk_block8<C>(sa, st, kbuf(jb), lane);
+    if (jb >= nfull) mask_tail8<C>(sa, jb * BN, S, lane);
+    softmax_max8<C>(st, sa, c);
+    exp_tile8<C>(st, sa, 0, c, st.p0);
+
+    // Steady state, two blocks per trip so the score buffers swap statically.
+    // Entering the trip for block i: its scores are in one buffer with their max
+    // taken and the probabilities of keys 0..31 in st.p0; K_{i+1} and V_i are
+    // loaded or in flight.  (jb is even: K_i and V_i live in stage i % 2.)
+    int j = jb;
+    for (; j + 2 < je; j += 2) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      load_tile8<C>(kbase, row_stride, (j + 2) * BN, pa.kcur.at(j + 2), S, kbuf(0), koff, wave);
+      load_tile8<C>(vbase, row_stride, (j + 1) * BN, pa.vcur.at(j + 1), S, vbuf(1), voff, wave);
+      step_a8<C, 1>(sb, sa, st, lds, off, c);
+      if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
+      step_b8<C, 0>(st, sb, lds, off, c);
+
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (j + 3 < je)
+        load_tile8<C>(kbase, row_stride, (j + 3) * BN, pa.kcur.at(j + 3), S, kbuf(1), koff, wave);
+      load_tile8<C>(vbase, row_stride, (j + 2) * BN, pa.vcur.at(j + 2), S, vbuf(0), voff, wave);
+      step_a8<C, 0>(sa, sb, st, lds, off, c);
+      if (j + 2 >= nfull) mask_tail8<C>(sa, (j + 2) * BN, S, lane);
+      step_b8<C, 1>(st, sa, lds, off, c);
     }
-  } else {
-    const float lsum = sum_halves(st.l);
-    if (srow < S) {
-      const size_t r = (size_t)split * ((size_t)B * H * S) + (size_t)bh * S + srow;
-      float* orow = a.ws_o + r * C::D;
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x16& o = st.o[dt];
-          *(f32x4*)(orow + dt * 32 + r4 * 8 + 4 * (lane >> 5)) =
-              f32x4{o[4 * r4 + 0], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]};
-        }
-      if (lane < 32) *(f32x2*)(a.ws_ml + 2 * r) = f32x2{st.m, lsum};
+    // the last one or two blocks (j is even; scores of block j in sa)
+    if (j + 1 < je) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      load_tile8<C>(vbase, row_stride, (j + 1) * BN, pa.vcur.at(j + 1), S, vbuf(1), voff, wave);
+      step_a8<C, 1>(sb, sa, st, lds, off, c);
+      if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
+      step_b8<C, 0>(st, sb, lds, off, c);
+      wait_vmcnt<0>();
+      __syncthreads();
+      exp_tile8<C>(st, sb, 1, c, st.p1);
+      pv_only8<C, 1>(st, lds, off);
+    } else {
+      wait_vmcnt<0>();  // V_j may have been issued by the last loop trip
+      __syncthreads();
+      exp_tile8<C>(st, sa, 1, c, st.p1);
+      pv_only8<C, 0>(st, lds, off);
     }
+
+    // ---- next piece: request its first K/V blocks and its queries before
+    // this piece's stores
+    u += piece_units(pa);
+    const bool more = u < uend;
+    const PieceAddr cur = pa;
+    if (more) {
+      __syncthreads();  // every wave is done reading this piece's tiles
+      pa = begin_piece8<C>(a, u, uend, nblk, row_stride, lds, koff, voff, wave);
+      load_q8<C>(st.qf, a, pa, row_stride, qflip, wave, lane);
+    }
+
+    // ---- epilogue
+    const int srow = m0 + wave * C::QW + (lane & 31);
+    if (cur.whole) {
+      // O * dv / l, rounded to bf16, stored into the destination slice
+      const float lrow = sum_halves(st.l);
+      const float inv = a.o_scale / lrow;
+      if (a.lse && lane < 32 && srow < S) a.lse[(size_t)cur.bh * S + srow] = row_lse(st.m, lrow);
+      if (srow < S) {
+        const int p = srow / T;
+        const int sp = srow - p * T;
+        uint16_t* orow = (uint16_t*)a.out + ((((size_t)p * B + cur.b) * T + sp) * H + cur.h) * C::D;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int d0 = dt * 32 + r4 * 8 + 4 * (lane >> 5);
+            const f32x16& o = st.o[dt];
+            u32x2 w = {pack_bf16(o[4 * r4 + 0] * inv, o[4 * r4 + 1] * inv),
+                       pack_bf16(o[4 * r4 + 2] * inv, o[4 * r4 + 3] * inv)};
+            *(u32x2*)(orow + d0) = w;
+          }
+      }
+    } else {
+      // a tile cut between chunks: fp32 partials into this chunk's slot
+      const float lsum = sum_halves(st.l);
+      const size_t slot = 2 * (size_t)chunk + (piece > 0 ? 1 : 0);
+      const int r = srow - m0;
+      if (srow < S) {
+        const size_t sr = slot * C::BM + r;
+        float* orow = a.ws_o + sr * C::D;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x16& o = st.o[dt];
+            *(f32x4*)(orow + dt * 32 + r4 * 8 + 4 * (lane >> 5)) =
+                f32x4{o[4 * r4 + 0], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]};
+          }
+        if (lane < 32) *(f32x2*)(a.ws_ml + 2 * sr) = f32x2{st.m, lsum};
+      }
+    }
+    if (!more) break;
   }
 }
 
@@ -501,13 +534,11 @@ template <int D>
 static hipError_t launch_d8(const AttnArgs& a, hipStream_t stream) {
   using C = Fp8Cfg<D>;
   static_assert(C::BM == kBlockM && C::BN == kBlockN, "tile geometry");
-  const int mtiles = (a.S + C::BM - 1) / C::BM;
-  const long long items = (long long)a.B * a.H * a.nsplit * mtiles;
-  if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (a.groups < 1) return hipErrorInvalidValue;
   AttnArgs args = a;
   void* kargs[] = {&args};
-  return hipLaunchKernel((const void*)attn_fwd_fp8_kernel<C>, dim3((unsigned)items), dim3(C::THREADS),
-                         kargs, 0, stream);
+  return hipLaunchKernel((const void*)attn_fwd_fp8_kernel<C>, dim3((unsigned)a.groups),
+                         dim3(C::THREADS), kargs, 0, stream);
 }
 
 hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream) {

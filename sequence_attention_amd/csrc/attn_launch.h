@@ -16,14 +16,16 @@ struct AttnArgs {
   float c;        // |scale| * log2(e), times q_descale * k_descale for fp8
   int neg;        // nonzero when scale < 0: queries are negated as they are loaded
   float o_scale;  // factor applied with 1/l in the epilogue (v_descale for fp8)
-  // Split of the key range: work item (b, h, split, m-tile) covers key blocks
-  // [split*nb_per, min(nblk, (split+1)*nb_per)).  With nsplit > 1 the items
-  // write unnormalised fp32 partials (O, and m, l per row) to the workspace
-  // and attn_combine merges them into out.
-  int nsplit;
-  int nb_per;
-  float* ws_o;    // [nsplit][B*H*S][D] fp32
-  float* ws_ml;   // [nsplit][B*H*S][2] fp32: running max (log2 units), row sum
+  // Work schedule (see Sched below): `groups` workgroups share the sequence of
+  // `units` = tiles * npair (query tile, pair of 64-key blocks) units.  Tiles
+  // cut between two workgroups leave unnormalised fp32 partials (O, and m, l
+  // per row) in the workspace slots of those workgroups; attn_combine merges
+  // them into out.
+  int groups;
+  int npair;
+  long long units;
+  float* ws_o;    // [2*groups][BM][D] fp32 (NULL when no tile is cut)
+  float* ws_ml;   // [2*groups][BM][2] fp32: running max (log2 units), row sum
   // Input layout.  Row s of batch b of an input tensor starts at row index
   //   b*batch_rows + s + (chunk_rows ? s / chunk_rows : 0) * jump_rows
   // (in units of H*D elements): [B][S][H][D] has batch_rows = S, chunk_rows =
@@ -45,6 +47,25 @@ struct AttnArgs {
 constexpr int kBlockM = XS_BM;         // query rows per workgroup
 constexpr int kBlockN = 64;            // keys per K/V block
 constexpr int kGroupsPerCU = XS_WGPC;  // workgroups resident per compute unit
+
+// The work schedule, shared by the kernels, the merge and the host plan.
+// Units are numbered u = tile * npair + pair (tile = (b*H + h) * mtiles + m-tile,
+// pair = key blocks 2*pair, 2*pair+1).  Workgroup chunk c (c = 0 .. groups-1,
+// XCD-aware: the workgroups of one XCD take consecutive chunks) owns units
+// [start(c), start(c+1)) with start(c) = floor(c * units / groups), and walks
+// them as pieces: maximal runs inside one tile.  A piece that is a whole tile
+// is normalised and stored directly; a cut piece (only the first and the last
+// piece of a chunk can be cut) writes its partials into slot 2c (first piece)
+// or 2c+1 (any later piece).
+struct Sched {
+  long long units;
+  int groups, npair;
+  __host__ __device__ long long start(int c) const { return (long long)c * units / groups; }
+  // the chunk that owns unit u
+  __host__ __device__ int owner(long long u) const {
+    return (int)(((u + 1) * (long long)groups - 1) / units);
+  }
+};
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);
 

@@ -42,6 +42,8 @@ int validate(const void* q, const void* k, const void* v, void* out, int B, int 
   if (elems * 2.0 > 9.0e18) return XS_ERR_UNSUPPORTED;
   // K/V rows of one (batch, head) are addressed with 32-bit buffer offsets
   if ((double)S * H * D * (double)in_elem_bytes >= 4294967296.0) return XS_ERR_UNSUPPORTED;
+  // query tiles are counted in 32-bit integers
+  if ((double)B * H * ((S + xs::kBlockM - 1) / xs::kBlockM) > 2147483647.0) return XS_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return XS_ERR_ALIGN;
   const size_t n = (size_t)B * S * H * D;
   const size_t in_bytes = n * in_elem_bytes, out_bytes = n * 2;
@@ -61,8 +63,9 @@ int validate(const void* q, const void* k, const void* v, void* out, int B, int 
   args->neg = scale < 0.0f;
   args->c = scores_factor(scale);
   args->o_scale = 1.0f;
-  args->nsplit = 1;
-  args->nb_per = (S + xs::kBlockN - 1) / xs::kBlockN;
+  args->groups = 0;
+  args->npair = 0;
+  args->units = 0;
   args->ws_o = nullptr;
   args->ws_ml = nullptr;
   args->batch_rows = S;
@@ -103,71 +106,101 @@ int device_cus() {
   return n;
 }
 
-// Split of the key range.  Model of the run time on `cus` compute units with
-// one workgroup resident per CU: ceil(items / cus) rounds, each as long as one
-// item (its key blocks plus about two blocks of prologue/epilogue work), plus,
-// when split, the extra HBM traffic of the fp32 partials (written once, read
-// once by the merge) and the merge launch.  Picks the cheapest nsplit <= 16.
+// Work schedule (attn_launch.h, Sched): `groups` workgroups share the units
+// (query tile, pair of key blocks) equally; a tile is cut wherever a share
+// ends inside it (partials + merge).  Candidates: groups = k * tiles (k = 1 ..
+// 16: every tile in k equal pieces, k = 1 uncut) and groups = the resident
+// slots (one persistent workgroup per CU walking an equal share).  The plan
+// picks the cheapest by a run-time model: rounds of resident workgroups x
+// (units per share + 1.5 units of prologue/epilogue per piece) x time per
+// unit, plus, when tiles are cut, the partials' HBM traffic and the merge
+// launch; cutting must gain 3 % over the best uncut schedule.
 struct Plan {
-  int nsplit, nb_per;
+  int groups, npair;
+  long long units, tiles;
+  bool cut;
 };
-Plan plan_split(long long ntiles, int nblk, long long rows, int D, int cus) {
-  const double t_block = D == 128 ? 1.9e-6 : 1.0e-6;  // s per 64-key block per workgroup
-  const double hbm = 4.0e12, t_launch = 5.0e-6;
-  auto cost = [&](int ns, int nbp) {
-    const double rounds = (double)((ntiles * ns + cus - 1) / cus);
-    double t = rounds * (nbp + 2) * t_block;
-    if (ns > 1) t += 2.0 * ns * (double)rows * (4.0 * D + 8.0) / hbm + t_launch;
-    return t;
-  };
-  Plan best{1, nblk};
-  double best_cost = cost(1, nblk);
-  for (int ns = 2; ns <= 16 && ns <= nblk; ++ns) {
-    // an even number of blocks per split, so every split starts on an even
-    // block and the kernels' double-buffer stages have fixed parity
-    const int nbp = ((nblk + ns - 1) / ns + 1) & ~1;
-    if ((nblk + nbp - 1) / nbp != ns) continue;  // fewer splits would do: skip
-    const double c = cost(ns, nbp);
-    if (c < 0.97 * best_cost) {
-      best_cost = c;
-      best = Plan{ns, nbp};
-    }
+
+Plan make_plan(long long groups, int npair, long long tiles) {
+  const long long units = tiles * npair;
+  // every share boundary floor(c*units/groups) must be a multiple of npair
+  const bool cut = !(units % groups == 0 && (units / groups) % npair == 0);
+  return Plan{(int)groups, npair, units, tiles, cut};
+}
+
+double plan_cost(const Plan& p, int slots, int D) {
+  const double t_pair = 2.0 * (D == 128 ? 1.9e-6 : 1.0e-6);  // s per 2 key blocks per workgroup
+  const double hbm = 4.0e12, t_launch = 5.0e-6, ovh = 1.5;
+  const double rounds = (double)((p.groups + slots - 1) / slots);
+  const long long per = (p.units + p.groups - 1) / p.groups;
+  double pieces;  // most pieces in one share
+  if (!p.cut)
+    pieces = (double)(per / p.npair);
+  else if (p.units % p.groups == 0 && p.npair % per == 0)
+    pieces = 1.0;  // shares of equal size that tile each tile exactly
+  else
+    pieces = (double)((per + p.npair - 1) / p.npair) + 1.0;
+  double t = rounds * ((double)per + ovh * pieces) * t_pair;
+  if (p.cut) {
+    // at most one cut tile per share boundary, each in about groups/tiles + 1 pieces
+    const double cut_tiles = (double)(p.groups < p.tiles ? p.groups : p.tiles);
+    const double ratio = (double)p.groups / (double)p.tiles + 1.0;
+    const double pieces_per_tile = ratio > 2.0 ? ratio : 2.0;
+    t += cut_tiles * xs::kBlockM * (pieces_per_tile * (4.0 * D + 8.0) + 2.0 * D) / hbm + t_launch;
   }
+  return t;
+}
+
+Plan plan_for(int B, int S, int H, int D, bool allow_cut) {
+  const long long tiles = (long long)B * H * ((S + xs::kBlockM - 1) / xs::kBlockM);
+  const int nblk = (S + xs::kBlockN - 1) / xs::kBlockN;
+  const int npair = (nblk + 1) / 2;
+  const long long units = tiles * npair;
+  const int slots = device_cus() * xs::kGroupsPerCU;
+  Plan best = make_plan(tiles, npair, tiles);
+  double best_cost = plan_cost(best, slots, D);
+  auto consider = [&](long long g) {
+    if (g < 1 || g > units || g > 0x7fffffffLL) return;
+    const Plan p = make_plan(g, npair, tiles);
+    if (p.cut && !allow_cut) return;
+    const double c = plan_cost(p, slots, D);
+    if ((p.cut && c < 0.97 * best_cost) || (!p.cut && c <= best_cost)) {
+      best = p;
+      best_cost = c;
+    }
+  };
+  consider(slots < units ? slots : units);  // persistent, equal shares
+  for (int k = 2; k <= 16 && k <= npair; ++k)
+    if (tiles * k <= slots) consider(tiles * k);  // k equal pieces per tile, one round
   return best;
 }
 
-Plan plan_for(int B, int S, int H, int D) {
-  const long long ntiles = (long long)B * H * ((S + xs::kBlockM - 1) / xs::kBlockM);
-  const int nblk = (S + xs::kBlockN - 1) / xs::kBlockN;
-  return plan_split(ntiles, nblk, (long long)B * H * S, D, device_cus() * xs::kGroupsPerCU);
+size_t workspace_bytes(const Plan& pl, int D) {
+  if (!pl.cut) return 0;
+  return 2 * (size_t)pl.groups * xs::kBlockM * ((size_t)D * 4 + 8);
 }
 
-size_t workspace_bytes(const Plan& pl, int B, int S, int H, int D) {
-  if (pl.nsplit <= 1) return 0;
-  const size_t rows = (size_t)B * S * H;
-  return (size_t)pl.nsplit * rows * ((size_t)D * 4 + 8);
-}
-
-// Attaches the split plan and workspace to validated arguments.
+// Attaches the schedule and, when it cuts tiles, the workspace to validated
+// arguments.  Without a workspace the schedule never cuts.
 int attach_workspace(xs::AttnArgs* a, void* ws, size_t ws_bytes) {
-  if (ws == nullptr) return XS_OK;  // no workspace: one item per tile
-  if (((uintptr_t)ws & 15u) != 0) return XS_ERR_ALIGN;
-  const Plan pl = plan_for(a->B, a->S, a->H, a->D);
-  const size_t need = workspace_bytes(pl, a->B, a->S, a->H, a->D);
-  if (need == 0) return XS_OK;
-  if (ws_bytes < need) return XS_ERR_WORKSPACE;
-  const size_t rows = (size_t)a->B * a->S * a->H;
-  a->nsplit = pl.nsplit;
-  a->nb_per = pl.nb_per;
-  a->ws_o = (float*)ws;
-  a->ws_ml = (float*)((char*)ws + (size_t)pl.nsplit * rows * a->D * 4);
+  if (ws != nullptr && ((uintptr_t)ws & 15u) != 0) return XS_ERR_ALIGN;
+  const Plan pl = plan_for(a->B, a->S, a->H, a->D, ws != nullptr);
+  const size_t need = workspace_bytes(pl, a->D);
+  if (need > 0 && ws_bytes < need) return XS_ERR_WORKSPACE;
+  a->groups = pl.groups;
+  a->npair = pl.npair;
+  a->units = pl.units;
+  if (need > 0) {
+    a->ws_o = (float*)ws;
+    a->ws_ml = (float*)((char*)ws + 2 * (size_t)pl.groups * xs::kBlockM * a->D * 4);
+  }
   return XS_OK;
 }
 
 int launch(const xs::AttnArgs& a, bool fp8, hipStream_t stream) {
   const hipError_t e = fp8 ? xs::launch_attn_fp8(a, stream) : xs::launch_attn_bf16(a, stream);
   if (e != hipSuccess) return XS_ERR_LAUNCH;
-  if (a.nsplit > 1 && xs::launch_attn_combine(a, stream) != hipSuccess) return XS_ERR_LAUNCH;
+  if (a.ws_o != nullptr && xs::launch_attn_combine(a, stream) != hipSuccess) return XS_ERR_LAUNCH;
   return XS_OK;
 }
 
@@ -242,12 +275,20 @@ int xs_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_desc
 
 size_t xs_attn_workspace_size(int B, int S, int H_local, int D) {
   if (B < 1 || S < 1 || H_local < 1 || (D != 64 && D != 128)) return 0;
-  return workspace_bytes(plan_for(B, S, H_local, D), B, S, H_local, D);
+  return workspace_bytes(plan_for(B, S, H_local, D, true), D);
 }
 
 int xs_attn_split_count(int B, int S, int H_local, int D) {
   if (B < 1 || S < 1 || H_local < 1 || (D != 64 && D != 128)) return 0;
-  return plan_for(B, S, H_local, D).nsplit;
+  const Plan p = plan_for(B, S, H_local, D, true);
+  if (!p.cut) return 1;
+  const xs::Sched sch{p.units, p.groups, p.npair};
+  int most = 1;
+  for (long long t = 0; t < p.tiles; ++t) {
+    const int n = sch.owner((t + 1) * p.npair - 1) - sch.owner(t * p.npair) + 1;
+    most = n > most ? n : most;
+  }
+  return most;
 }
 
 const char* xs_attn_strerror(int status) {

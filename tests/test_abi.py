@@ -119,18 +119,41 @@ def _fwd_ws(ws, nbytes, **kw):
                              a["P"], a["scale"], ws, nbytes, None)
 
 
-def test_split_plan_fills_the_grid():
+def _owner(u, units, groups):
+    return ((u + 1) * groups - 1) // units
+
+
+def test_schedule_plan_fills_the_grid():
     # 256 compute units (what the plan assumes when no GPU is visible), 256-row
-    # tiles, 64-key blocks: cost = ceil(items / 256) rounds x blocks per item
-    assert xs.split_count(1, 32768, 5, 128) == 2    # 640 tiles: 2.5 rounds -> 5 exact rounds
-    assert xs.split_count(1, 131072, 3, 128) == 1   # 1536 tiles: 6 exact rounds
-    assert xs.split_count(2, 32768, 4, 128) == 1    # 1024 tiles: 4 exact rounds
-    assert xs.split_count(1, 4608, 3, 128) == 4     # 54 tiles: one round of 216 items
+    # tiles, units of two 64-key blocks.  Persistent shares cut a tile only where
+    # a share ends inside it.
+    assert xs.split_count(1, 32768, 5, 128) == 2    # 640 tiles on 256 shares: 2.5 tiles each
+    assert xs.split_count(1, 131072, 3, 128) == 1   # 1536 tiles: 6 whole tiles per share
+    assert xs.split_count(2, 32768, 4, 128) == 1    # 1024 tiles: 4 whole tiles per share
+    assert xs.split_count(1, 256, 2, 64) == 1       # tiny: one workgroup per tile is cheaper
     assert xs.split_count(0, 4608, 3, 128) == 0
-    n = xs.workspace_size(1, 32768, 5, 128)
-    assert n == 2 * 32768 * 5 * (128 * 4 + 8)
+    # image: 54 tiles x 36 units; 216 shares of 9 units (every tile in 4 equal
+    # pieces, one piece per share) beat 256 shares of 7-8 units that straddle
+    # tiles; the pieces per tile follow from the schedule's own arithmetic
+    units, groups, npair = 54 * 36, 216, 36
+    most = max(_owner((t + 1) * npair - 1, units, groups) - _owner(t * npair, units, groups) + 1
+               for t in range(54))
+    assert xs.split_count(1, 4608, 3, 128) == most == 4
+    assert xs.workspace_size(1, 4608, 3, 128) == 2 * 216 * 256 * (128 * 4 + 8)
+    # workspace: two fp32 slots of 256 rows (O, m, l) per share, only when tiles are cut
+    assert xs.workspace_size(1, 32768, 5, 128) == 2 * 256 * 256 * (128 * 4 + 8)
     assert xs.workspace_size(1, 131072, 3, 128) == 0
+    assert xs.workspace_size(2, 32768, 4, 128) == 0
     assert xs.workspace_size(1, 4608, 3, 96) == 0
+
+
+def test_schedule_owner_arithmetic():
+    # owner(u) is the share whose range [floor(c U / G), floor((c+1) U / G)) holds u
+    for units, groups in ((10, 4), (1944, 256), (163840, 256), (7, 7), (5, 3)):
+        starts = [c * units // groups for c in range(groups + 1)]
+        for u in range(units):
+            c = _owner(u, units, groups)
+            assert starts[c] <= u < starts[c + 1]
 
 
 def test_workspace_errors_before_any_launch():
