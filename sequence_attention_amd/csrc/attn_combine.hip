@@ -15,20 +15,22 @@
 
 namespace xs {
 
-// One workgroup per RPB rows of one query tile.  Tiles held whole by one chunk
+// One workgroup per RPB rows of one query tile.  Tiles held whole by one share
 // of the schedule were stored by the attention kernel: those workgroups exit.
-// For a cut tile the pieces are, in key order, the last piece of the chunk
-// that owns its first unit (slot 2c+1, or 2c if that chunk starts exactly at
-// the tile) and the first piece of every later chunk up to the owner of its
-// last unit (slot 2c).
+// For a cut tile the pieces are, in key order, the last piece of the share
+// that owns its first unit (slot 2c+1, or 2c if that share's remainder run
+// starts exactly at the tile) and the first piece of every later share up to
+// the owner of its last unit (slot 2c).
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int LPR = D / 4;             // lanes per row, 4 consecutive d each
   constexpr int RPB = 256 / LPR;         // rows per workgroup
   constexpr int GPT = kBlockM / RPB;     // workgroups per tile
-  const Sched sch{a.units, a.groups, a.npair};
-  const int tile = blockIdx.x / GPT;
-  const long long u0 = (long long)tile * a.npair, u1 = u0 + a.npair - 1;
+  const Sched sch{a.units, a.groups, a.npair, a.dp};
+  // only the remainder tiles can be cut: the grid covers them alone
+  const int rt = blockIdx.x / GPT;  // index among the remainder tiles
+  const int tile = a.dp * a.groups + rt;
+  const long long u0 = (long long)rt * a.npair, u1 = u0 + a.npair - 1;
   const int c_lo = sch.owner(u0), c_hi = sch.owner(u1);
   if (c_lo == c_hi) return;
   const int mtiles = (a.S + kBlockM - 1) / kBlockM;
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int srow = (tile - bh * mtiles) * kBlockM + r;
   if (srow >= a.S) return;
   const int d0 = (threadIdx.x % LPR) * 4;
-  // every share holds at least one unit (the plan keeps groups <= units)
+  // every share holds at least one remainder unit (the plan keeps units >= groups)
   const size_t first = 2 * (size_t)c_lo + (sch.start(c_lo) < u0 ? 1 : 0);
   auto slot_of = [&](int c) { return c == c_lo ? first : 2 * (size_t)c; };
 

@@ -473,14 +473,14 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, co
   }
 }
 
-// Decodes the piece that starts at unit u of a chunk ending at uend and issues
-// its first loads (K and V of block jb into stage 0, K of jb+1 into stage 1).
+// Takes the next piece of the walk and issues its first loads (K and V of
+// block jb into stage 0, K of jb+1 into stage 1).
 template <class C>
-__device__ __forceinline__ PieceAddr begin_piece(const AttnArgs& a, long long u, long long uend,
+__device__ __forceinline__ PieceAddr begin_piece(ShareWalk& walk, const Sched& sch, const AttnArgs& a,
                                                  int nblk, uint32_t row_stride, uint8_t XS_LDS* lds,
                                                  const uint32_t (&koff)[C::LPW],
-                                                 const uint32_t (&voff)[C::LPW], int wave) {
-  PieceAddr pa = decode_piece<C::BM, C::ROWB>(a, u, uend, nblk, row_stride);
+                                                 const uint32_t (&voff)[C::LPW], int wave, int& slot) {
+  PieceAddr pa = next_piece<C::BM, C::ROWB>(walk, sch, a, nblk, row_stride, slot);
   const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
   const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
   load_tile<C>(kbase, row_stride, pa.jb * C::BN, pa.kcur.at(pa.jb), a.S, lds, koff, wave);
@@ -509,10 +509,10 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[C::QT][C::KS], const AttnArgs
   }
 }
 
-// Persistent workgroups: each walks its chunk of the schedule (attn_launch.h,
-// Sched) piece by piece.  Chunks are equal shares of the (tile, key-block pair)
-// sequence, so the workgroups finish their tiles at staggered times instead of
-// in lockstep rounds, and only tiles cut between two chunks need a merge.
+// Persistent workgroups: each walks its share of the schedule (attn_launch.h,
+// Sched) piece by piece: whole tiles in rounds, then an equal run of the
+// remaining tiles' (tile, key-block pair) units, so no workgroup idles at the
+// end and only tiles cut between two shares need a merge.
 // Before a piece's output stores, the next piece's first K/V blocks are
 // already requested, so the stores drain while those loads are in flight.
 template <class C>
@@ -537,17 +537,17 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
   const float c = a.c;
   const LdsOffs<C> off = lds_offsets<C>(lane);
 
-  // this workgroup's chunk; the workgroups of one XCD take consecutive chunks
-  const Sched sch{a.units, a.groups, a.npair};
-  const int chunk = xcd_tile(blockIdx.x, a.groups);
-  long long u = sch.start(chunk);
-  const long long uend = sch.start(chunk + 1);
-  if (u >= uend) return;
-  PieceAddr pa = begin_piece<C>(a, u, uend, nblk, row_stride, lds, koff, voff, wave);
+  // this workgroup's share; the workgroups of one XCD take consecutive shares
+  const Sched sch{a.units, a.groups, a.npair, a.dp};
+  ShareWalk walk;
+  walk.init(sch, xcd_tile(blockIdx.x, a.groups));
+  if (!walk.more(sch)) return;
+  int slot;
+  PieceAddr pa = begin_piece<C>(walk, sch, a, nblk, row_stride, lds, koff, voff, wave, slot);
   Bf16State<C> st;
   load_q<C>(st.qf, a, pa, row_stride, qflip, wave, lane);
 
-  for (int piece = 0;; ++piece) {
+  for (;;) {
     const int jb = pa.jb, je = pa.je, m0 = pa.m0;
     const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
     const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
@@ -620,12 +620,12 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
 
     // ---- next piece: request its first K/V blocks and its queries before
     // this piece's stores (this piece's Q fragments are no longer needed)
-    u += piece_units(pa);
-    const bool more = u < uend;
+    const bool more = walk.more(sch);
     const PieceAddr cur = pa;
+    const int cur_slot = slot;
     if (more) {
       __syncthreads();  // every wave is done reading this piece's tiles
-      pa = begin_piece<C>(a, u, uend, nblk, row_stride, lds, koff, voff, wave);
+      pa = begin_piece<C>(walk, sch, a, nblk, row_stride, lds, koff, voff, wave, slot);
       load_q<C>(st.qf, a, pa, row_stride, qflip, wave, lane);
     }
 
@@ -655,16 +655,14 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
         }
       }
     } else {
-      // a tile cut between chunks: unnormalised fp32 partials into this
-      // chunk's slot (2*chunk for its first piece, 2*chunk+1 for its last),
-      // merged by attn_combine
-      const size_t slot = 2 * (size_t)chunk + (piece > 0 ? 1 : 0);
+      // a tile cut between shares: unnormalised fp32 partials into this
+      // share's slot, merged by attn_combine
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         const float lsum = sum_halves(st.l[qt]);
         const int r = wave * C::QW + qt * 32 + (lane & 31);  // row within the tile
         if (m0 + r < S) {
-          const size_t sr = slot * C::BM + r;
+          const size_t sr = (size_t)cur_slot * C::BM + r;
           float* orow = a.ws_o + sr * C::D;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)

@@ -337,14 +337,14 @@ __device__ __forceinline__ void pv_only8(Fp8State<C>& st, const uint8_t XS_LDS* 
   }
 }
 
-// Decodes the piece that starts at unit u of a chunk ending at uend and issues
-// its first loads (K and V of block jb into stage 0, K of jb+1 into stage 1).
+// Takes the next piece of the walk and issues its first loads (K and V of
+// block jb into stage 0, K of jb+1 into stage 1).
 template <class C>
-__device__ __forceinline__ PieceAddr begin_piece8(const AttnArgs& a, long long u, long long uend,
-                                                  int nblk, uint32_t row_stride,
+__device__ __forceinline__ PieceAddr begin_piece8(ShareWalk& walk, const Sched& sch,
+                                                  const AttnArgs& a, int nblk, uint32_t row_stride,
                                                   uint8_t XS_LDS* lds, uint32_t koff,
-                                                  uint32_t voff, int wave) {
-  PieceAddr pa = decode_piece<C::BM, C::ROWB>(a, u, uend, nblk, row_stride);
+                                                  uint32_t voff, int wave, int& slot) {
+  PieceAddr pa = next_piece<C::BM, C::ROWB>(walk, sch, a, nblk, row_stride, slot);
   const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
   const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
   load_tile8<C>(kbase, row_stride, pa.jb * C::BN, pa.kcur.at(pa.jb), a.S, lds, koff, wave);
@@ -401,16 +401,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
   const float c = a.c;
   const LdsOffs8<C> off = lds_offsets8<C>(lane);
 
-  const Sched sch{a.units, a.groups, a.npair};
-  const int chunk = xcd_tile(blockIdx.x, a.groups);
-  long long u = sch.start(chunk);
-  const long long uend = sch.start(chunk + 1);
-  if (u >= uend) return;
-  PieceAddr pa = begin_piece8<C>(a, u, uend, nblk, row_stride, lds, koff, voff, wave);
+  const Sched sch{a.units, a.groups, a.npair, a.dp};
+  ShareWalk walk;
+  walk.init(sch, xcd_tile(blockIdx.x, a.groups));
+  if (!walk.more(sch)) return;
+  int slot;
+  PieceAddr pa = begin_piece8<C>(walk, sch, a, nblk, row_stride, lds, koff, voff, wave, slot);
   Fp8State<C> st;
   load_q8<C>(st.qf, a, pa, row_stride, qflip, wave, lane);
 
-  for (int piece = 0;; ++piece) {
+  for (;;) {
     const int jb = pa.jb, je = pa.je, m0 = pa.m0;
     const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
     const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
@@ -476,12 +476,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
 
     // ---- next piece: request its first K/V blocks and its queries before
     // this piece's stores
-    u += piece_units(pa);
-    const bool more = u < uend;
+    const bool more = walk.more(sch);
     const PieceAddr cur = pa;
+    const int cur_slot = slot;
     if (more) {
       __syncthreads();  // every wave is done reading this piece's tiles
-      pa = begin_piece8<C>(a, u, uend, nblk, row_stride, lds, koff, voff, wave);
+      pa = begin_piece8<C>(walk, sch, a, nblk, row_stride, lds, koff, voff, wave, slot);
       load_q8<C>(st.qf, a, pa, row_stride, qflip, wave, lane);
     }
 
@@ -508,12 +508,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
           }
       }
     } else {
-      // a tile cut between chunks: fp32 partials into this chunk's slot
+      // a tile cut between shares: fp32 partials into this share's slot
       const float lsum = sum_halves(st.l);
-      const size_t slot = 2 * (size_t)chunk + (piece > 0 ? 1 : 0);
       const int r = srow - m0;
       if (srow < S) {
-        const size_t sr = slot * C::BM + r;
+        const size_t sr = (size_t)cur_slot * C::BM + r;
         float* orow = a.ws_o + sr * C::D;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)

@@ -16,13 +16,14 @@ struct AttnArgs {
   float c;        // |scale| * log2(e), times q_descale * k_descale for fp8
   int neg;        // nonzero when scale < 0: queries are negated as they are loaded
   float o_scale;  // factor applied with 1/l in the epilogue (v_descale for fp8)
-  // Work schedule (see Sched below): `groups` workgroups share the sequence of
-  // `units` = tiles * npair (query tile, pair of 64-key blocks) units.  Tiles
-  // cut between two workgroups leave unnormalised fp32 partials (O, and m, l
-  // per row) in the workspace slots of those workgroups; attn_combine merges
-  // them into out.
+  // Work schedule (see Sched below): `groups` workgroups; each first takes
+  // `dp` whole tiles, then an equal share of the `units` (query tile, pair of
+  // 64-key blocks) units of the remaining tiles.  Tiles cut between two
+  // workgroups leave unnormalised fp32 partials (O, and m, l per row) in the
+  // workspace slots of those workgroups; attn_combine merges them into out.
   int groups;
   int npair;
+  int dp;
   long long units;
   float* ws_o;    // [2*groups][BM][D] fp32 (NULL when no tile is cut)
   float* ws_ml;   // [2*groups][BM][2] fp32: running max (log2 units), row sum
@@ -49,19 +50,23 @@ constexpr int kBlockN = 64;            // keys per K/V block
 constexpr int kGroupsPerCU = XS_WGPC;  // workgroups resident per compute unit
 
 // The work schedule, shared by the kernels, the merge and the host plan.
-// Units are numbered u = tile * npair + pair (tile = (b*H + h) * mtiles + m-tile,
-// pair = key blocks 2*pair, 2*pair+1).  Workgroup chunk c (c = 0 .. groups-1,
-// XCD-aware: the workgroups of one XCD take consecutive chunks) owns units
-// [start(c), start(c+1)) with start(c) = floor(c * units / groups), and walks
-// them as pieces: maximal runs inside one tile.  A piece that is a whole tile
-// is normalised and stored directly; a cut piece (only the first and the last
-// piece of a chunk can be cut) writes its partials into slot 2c (first piece)
-// or 2c+1 (any later piece).
+// Tiles are numbered tile = (b*H + h) * mtiles + m-tile.  Workgroup share c
+// (c = 0 .. groups-1, XCD-aware: the workgroups of one XCD take consecutive
+// shares) first processes the whole tiles r*groups + c for r = 0 .. dp-1 --
+// in rounds, so the workgroups of an XCD stream neighbouring tiles of one head
+// over the same keys together and share K/V in L2 -- and then an equal share
+// of the remaining tiles' units: units u = (tile - dp*groups) * npair + pair
+// (pair = key blocks 2*pair, 2*pair+1), share c owning [start(c), start(c+1))
+// with start(c) = floor(c * units / groups), walked as pieces (maximal runs
+// inside one tile).  A piece that is a whole tile is normalised and stored
+// directly; a cut piece (only the first and the last piece of a share's
+// remainder run can be cut) writes its partials into slot 2c (first) or 2c+1
+// (any later piece).
 struct Sched {
-  long long units;
-  int groups, npair;
+  long long units;  // units of the remainder tiles
+  int groups, npair, dp;
   __host__ __device__ long long start(int c) const { return (long long)c * units / groups; }
-  // the chunk that owns unit u
+  // the share that owns remainder unit u
   __host__ __device__ int owner(long long u) const {
     return (int)(((u + 1) * (long long)groups - 1) / units);
   }

@@ -16,16 +16,44 @@ struct PieceAddr {
   ChunkCursor kcur, vcur;
 };
 
-// The piece that starts at unit u of a chunk ending at uend, for query tiles of
-// BM rows and input rows of ROWB bytes (one head).
+// Pieces of one workgroup's share of the schedule, in order: its whole tiles
+// first, then the pieces of its run of remainder units.  Wave-uniform state.
+struct ShareWalk {
+  int chunk, round;
+  long long u, uend;
+  int sk_pieces;  // remainder pieces handed out so far
+  __device__ void init(const Sched& s, int c) {
+    chunk = c, round = 0, sk_pieces = 0;
+    u = s.start(c);
+    uend = s.start(c + 1);
+  }
+  __device__ bool more(const Sched& s) const { return round < s.dp || u < uend; }
+};
+
+// The next piece of the walk (more() must hold), for query tiles of BM rows
+// and input rows of ROWB bytes (one head); `slot` receives the workspace slot
+// a cut piece writes.
 template <int BM, int ROWB>
-__device__ __forceinline__ PieceAddr decode_piece(const AttnArgs& a, long long u, long long uend,
-                                                  int nblk, uint32_t row_stride) {
-  const int npair = a.npair, mtiles = (a.S + BM - 1) / BM;
-  const int tile = (int)(u / npair);
-  const int p0 = (int)(u - (long long)tile * npair);
-  const long long left = uend - u;
-  const int p1 = left < npair - p0 ? p0 + (int)left : npair;
+__device__ __forceinline__ PieceAddr next_piece(ShareWalk& w, const Sched& sch, const AttnArgs& a,
+                                                int nblk, uint32_t row_stride, int& slot) {
+  const int npair = sch.npair, mtiles = (a.S + BM - 1) / BM;
+  int tile, p0, p1;
+  if (w.round < sch.dp) {
+    tile = w.round * sch.groups + w.chunk;
+    p0 = 0;
+    p1 = npair;
+    ++w.round;
+    slot = -1;
+  } else {
+    const int rt = (int)(w.u / npair);
+    tile = sch.dp * sch.groups + rt;
+    p0 = (int)(w.u - (long long)rt * npair);
+    const long long left = w.uend - w.u;
+    p1 = left < npair - p0 ? p0 + (int)left : npair;
+    w.u += p1 - p0;
+    slot = 2 * w.chunk + (w.sk_pieces > 0 ? 1 : 0);
+    ++w.sk_pieces;
+  }
   PieceAddr pa;
   pa.bh = tile / mtiles;
   pa.m0 = (tile - pa.bh * mtiles) * BM;
@@ -39,8 +67,5 @@ __device__ __forceinline__ PieceAddr decode_piece(const AttnArgs& a, long long u
   pa.vcur.init(pa.jb, a.chunk_rows, a.jump_rows, row_stride);
   return pa;
 }
-
-// Units (key-block pairs) a piece covers.
-__device__ __forceinline__ int piece_units(const PieceAddr& pa) { return (pa.je - pa.jb + 1) / 2; }
 
 }  // namespace xs

@@ -65,6 +65,7 @@ int validate(const void* q, const void* k, const void* v, void* out, int B, int 
   args->o_scale = 1.0f;
   args->groups = 0;
   args->npair = 0;
+  args->dp = 0;
   args->units = 0;
   args->ws_o = nullptr;
   args->ws_ml = nullptr;
@@ -106,45 +107,54 @@ int device_cus() {
   return n;
 }
 
-// Work schedule (attn_launch.h, Sched): `groups` workgroups share the units
-// (query tile, pair of key blocks) equally; a tile is cut wherever a share
-// ends inside it (partials + merge).  Candidates: groups = k * tiles (k = 1 ..
-// 16: every tile in k equal pieces, k = 1 uncut) and groups = the resident
-// slots (one persistent workgroup per CU walking an equal share).  The plan
-// picks the cheapest by a run-time model: rounds of resident workgroups x
-// (units per share + 1.5 units of prologue/epilogue per piece) x time per
-// unit, plus, when tiles are cut, the partials' HBM traffic and the merge
-// launch; cutting must gain 3 % over the best uncut schedule.
+// Work schedule (attn_launch.h, Sched): `groups` workgroups; each takes dp
+// whole tiles in rounds, then an equal share of the remaining tiles' units
+// (query tile, pair of key blocks), cutting a tile wherever a share ends inside
+// it (partials + merge).  Candidates: groups = tiles (one whole tile each),
+// groups = k * tiles (k = 2 .. 16: every tile in k equal pieces, one round) and
+// groups = the resident slots (one persistent workgroup per CU: dp = tiles /
+// slots rounds of whole tiles, then the remainder shared).  The plan picks the
+// cheapest by a run-time model: rounds of resident workgroups x (units per
+// workgroup + 1.5 units of prologue/epilogue per piece) x time per unit, plus,
+// when tiles are cut, the partials' HBM traffic and the merge launch; cutting
+// must gain 3 % over the best uncut schedule.
 struct Plan {
-  int groups, npair;
-  long long units, tiles;
+  int groups, npair, dp;
+  long long units, tiles;  // units of the remainder tiles
   bool cut;
 };
 
+// Invariant kept for the kernels and the merge: units == 0 or units >= groups
+// (every share owns at least one remainder unit).
 Plan make_plan(long long groups, int npair, long long tiles) {
-  const long long units = tiles * npair;
-  // every share boundary floor(c*units/groups) must be a multiple of npair
-  const bool cut = !(units % groups == 0 && (units / groups) % npair == 0);
-  return Plan{(int)groups, npair, units, tiles, cut};
+  long long dp = groups <= tiles ? tiles / groups : 0;
+  while (dp > 0 && tiles > dp * groups && (tiles - dp * groups) * npair < groups) --dp;
+  const long long units = (tiles - dp * groups) * npair;
+  // every remainder share boundary floor(c*units/groups) must be a multiple of npair
+  const bool cut = units > 0 && !(units % groups == 0 && (units / groups) % npair == 0);
+  return Plan{(int)groups, npair, (int)dp, units, tiles, cut};
 }
 
 double plan_cost(const Plan& p, int slots, int D) {
   const double t_pair = 2.0 * (D == 128 ? 1.9e-6 : 1.0e-6);  // s per 2 key blocks per workgroup
   const double hbm = 4.0e12, t_launch = 5.0e-6, ovh = 1.5;
   const double rounds = (double)((p.groups + slots - 1) / slots);
-  const long long per = (p.units + p.groups - 1) / p.groups;
-  double pieces;  // most pieces in one share
-  if (!p.cut)
+  const long long per = (p.units + p.groups - 1) / p.groups;  // remainder units per share
+  double pieces;  // most remainder pieces in one share
+  if (per == 0)
+    pieces = 0.0;
+  else if (!p.cut)
     pieces = (double)(per / p.npair);
   else if (p.units % p.groups == 0 && p.npair % per == 0)
     pieces = 1.0;  // shares of equal size that tile each tile exactly
   else
     pieces = (double)((per + p.npair - 1) / p.npair) + 1.0;
-  double t = rounds * ((double)per + ovh * pieces) * t_pair;
+  double t = rounds * ((double)p.dp * (p.npair + ovh) + (double)per + ovh * pieces) * t_pair;
   if (p.cut) {
     // at most one cut tile per share boundary, each in about groups/tiles + 1 pieces
-    const double cut_tiles = (double)(p.groups < p.tiles ? p.groups : p.tiles);
-    const double ratio = (double)p.groups / (double)p.tiles + 1.0;
+    const double rtiles = (double)p.units / p.npair;
+    const double cut_tiles = (double)p.groups < rtiles ? (double)p.groups : rtiles;
+    const double ratio = (double)p.groups / rtiles + 1.0;
     const double pieces_per_tile = ratio > 2.0 ? ratio : 2.0;
     t += cut_tiles * xs::kBlockM * (pieces_per_tile * (4.0 * D + 8.0) + 2.0 * D) / hbm + t_launch;
   }
@@ -155,12 +165,11 @@ Plan plan_for(int B, int S, int H, int D, bool allow_cut) {
   const long long tiles = (long long)B * H * ((S + xs::kBlockM - 1) / xs::kBlockM);
   const int nblk = (S + xs::kBlockN - 1) / xs::kBlockN;
   const int npair = (nblk + 1) / 2;
-  const long long units = tiles * npair;
   const int slots = device_cus() * xs::kGroupsPerCU;
   Plan best = make_plan(tiles, npair, tiles);
   double best_cost = plan_cost(best, slots, D);
   auto consider = [&](long long g) {
-    if (g < 1 || g > units || g > 0x7fffffffLL) return;
+    if (g < 1 || g > tiles * npair || g > 0x7fffffffLL) return;
     const Plan p = make_plan(g, npair, tiles);
     if (p.cut && !allow_cut) return;
     const double c = plan_cost(p, slots, D);
@@ -169,7 +178,7 @@ Plan plan_for(int B, int S, int H, int D, bool allow_cut) {
       best_cost = c;
     }
   };
-  consider(slots < units ? slots : units);  // persistent, equal shares
+  consider(slots);  // persistent: one workgroup per slot
   for (int k = 2; k <= 16 && k <= npair; ++k)
     if (tiles * k <= slots) consider(tiles * k);  // k equal pieces per tile, one round
   return best;
@@ -189,6 +198,7 @@ int attach_workspace(xs::AttnArgs* a, void* ws, size_t ws_bytes) {
   if (need > 0 && ws_bytes < need) return XS_ERR_WORKSPACE;
   a->groups = pl.groups;
   a->npair = pl.npair;
+  a->dp = pl.dp;
   a->units = pl.units;
   if (need > 0) {
     a->ws_o = (float*)ws;
@@ -282,9 +292,9 @@ int xs_attn_split_count(int B, int S, int H_local, int D) {
   if (B < 1 || S < 1 || H_local < 1 || (D != 64 && D != 128)) return 0;
   const Plan p = plan_for(B, S, H_local, D, true);
   if (!p.cut) return 1;
-  const xs::Sched sch{p.units, p.groups, p.npair};
+  const xs::Sched sch{p.units, p.groups, p.npair, p.dp};
   int most = 1;
-  for (long long t = 0; t < p.tiles; ++t) {
+  for (long long t = 0; t < p.units / p.npair; ++t) {  // remainder tiles
     const int n = sch.owner((t + 1) * p.npair - 1) - sch.owner(t * p.npair) + 1;
     most = n > most ? n : most;
   }
