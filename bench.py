@@ -42,6 +42,9 @@ def parse():
                     help="target wall time of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    ap.add_argument("--burst-gap", action="store_true",
+                    help="characterise the Burst-Gap model with the microbenchmark (fine-grained "
+                         "host memory as the remote link) and check it on the attention epilogue")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -110,6 +113,14 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.burst_gap:
+        from sequence_attention_amd import burst_gap
+        cases = [(workloads.WORKLOADS[n], workloads.make_inputs(workloads.WORKLOADS[n]))
+                 for n in ("image", "video", "long")]
+        res = burst_gap.characterise(torch.device("cuda:0"), cases,
+                                     log=lambda m: print(m, file=sys.stderr, flush=True))
+        print(json.dumps({"metric": "burst_gap_characterisation", "n_gpus": 1, **res}), flush=True)
         return
     import sequence_attention_amd as xs
 

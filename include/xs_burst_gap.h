@@ -1,0 +1,63 @@
+/*
+ * xs_burst_gap.h -- C ABI of the Burst-Gap microbenchmark of the same library
+ * (libxs_attn.so), for characterising how device-issued store bursts drain on
+ * one GPU.
+ *
+ * What it measures (X-Stage paper, gist.science explainer, "Methodik: Die
+ * X-Stage-Abstraktion und das Burst-Gap-Modell" and "Zentrale Beitraege",
+ * item "Charakterisierung und Vorhersage"): K producers each issue a burst of
+ * stores, then compute for a gap G without memory traffic, and repeat.  The
+ * sender-visible issue time of a burst of aggregate volume V is modelled as
+ *   T_iss(G; K, V) = max(T0_iss(K, V), V/R - G)
+ * with T0_iss the backpressure-free issue time, R the effective drain rate and
+ * Q the outstanding capacity.  The pages measure remote stores over a GPU
+ * interconnect; on one GPU the destination is any device-accessible memory --
+ * fine-grained host memory stands in for the remote link.
+ */
+#ifndef XS_BURST_GAP_H
+#define XS_BURST_GAP_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define XS_BG_ERR_NULL (-1)   /* dst or times is NULL */
+#define XS_BG_ERR_ARG (-2)    /* a size out of range (see below) */
+#define XS_BG_ERR_ALIGN (-4)  /* dst not 16-byte or times not 8-byte aligned */
+#define XS_BG_ERR_LAUNCH (-5) /* the HIP launch reported an error */
+
+/* Runs `producers` workgroups of 256 threads.  dst is used as a ring of
+ * ring = min(nburst, floor(dst_bytes / (producers*bytes))) regions of
+ * producers*bytes bytes; in burst b, producer p stores all `bytes` bytes of
+ * [(r*producers + p)*bytes, (r*producers + p + 1)*bytes), r = b % ring (16
+ * bytes per lane per step, fully coalesced; the 16 bytes lane t writes are the
+ * uint32 words {p, t, b, 0x5eed}), then spins `gap_cycles` shader clocks
+ * without memory traffic.  A ring of nburst regions makes every burst write
+ * fresh addresses, as output tiles do.
+ *   dst         device-accessible memory of at least producers*bytes bytes,
+ *               16-byte aligned; bytes past the ring are not touched.
+ *   producers   1 .. 4096
+ *   bytes       per producer and burst: a multiple of 4096, at most 1 GiB
+ *   nburst      1 .. 4096
+ *   gap_cycles  0 .. 2^32 shader clocks, and nburst*gap_cycles <= 2^34 (a
+ *               run of seconds at most)
+ *   times       device memory, 8-byte aligned, producers*4*(nburst+3) uint64:
+ *               for producer p and wave w (4 per producer) the record at
+ *               (p*4 + w)*(nburst+3) holds, in shader clocks (s_memtime), the
+ *               issue time of each burst (first store to issue of the last
+ *               store, no wait for completion), then the time its stores took
+ *               to complete after the last gap, then the clocks of the whole
+ *               run, then the same run in 100 MHz ticks (s_memrealtime) --
+ *               the last two give the clock rate for converting to seconds.
+ *   stream      hipStream_t as void*, NULL = default stream; asynchronous.
+ * Returns 0 or an XS_BG_ERR_* code (validated before any HIP call). */
+int xs_burst_gap(void *dst, size_t dst_bytes, int producers, size_t bytes, int nburst,
+                 long long gap_cycles, unsigned long long *times, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XS_BURST_GAP_H */

@@ -8,6 +8,7 @@ import re
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libxs_attn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "xs_attn.h")
+HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_PKG), "include", "xs_burst_gap.h")]
 
 _lib = None
 
@@ -49,6 +50,8 @@ def lib() -> ctypes.CDLL:
         L.xs_attn_strerror.restype = ctypes.c_char_p
         L.xs_attn_version.argtypes = []
         L.xs_attn_version.restype = ci
+        L.xs_burst_gap.argtypes = [vp, sz, ci, sz, ci, ctypes.c_longlong, vp, vp]
+        L.xs_burst_gap.restype = ci
         _lib = L
     return _lib
 
@@ -63,6 +66,9 @@ def check(status: int) -> None:
 
 
 def declared_functions() -> list[str]:
-    """Names of the functions declared in include/xs_attn.h."""
-    text = open(HEADER_PATH).read()
-    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(xs_attn_\w+)\s*\(", text, flags=re.M)
+    """Names of the functions declared in include/*.h."""
+    names = []
+    for path in HEADER_PATHS:
+        text = open(path).read()
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(xs_\w+)\s*\(", text, flags=re.M)
+    return names

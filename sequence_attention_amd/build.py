@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libxs_attn.so")
 OBJDIR = os.path.join(PKG, "_build")
-SOURCES = ["xs_attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "attn_combine.hip"]
+SOURCES = ["xs_attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "attn_combine.hip",
+           "burst_gap.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

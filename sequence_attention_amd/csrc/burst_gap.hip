@@ -1,0 +1,102 @@
+// burst_gap.hip -- the Burst-Gap microbenchmark: producers issue bursts of
+// stores into a destination (fine-grained host memory standing in for a remote
+// link), separated by a computation-free gap, and time how long each burst takes
+// to issue.
+//
+// Model being characterised (X-Stage paper, gist.science explainer, "Methodik:
+// Die X-Stage-Abstraktion und das Burst-Gap-Modell"): the sender-visible issue
+// time of a burst of aggregate volume V from K producers that leave a gap G
+// between bursts is T_iss(G; K, V) = max(T0_iss(K, V), V/R - G), with T0_iss
+// the backpressure-free issue time, R the effective drain rate and Q the
+// outstanding capacity (volume in flight before the issue stalls).  On one GPU
+// the "remote stores" are ordinary vector stores to host-coherent memory over
+// PCIe: issued stores retire into the memory pipeline and drain while the wave
+// moves on, until the pipeline's outstanding capacity is exhausted.
+//
+// Each producer is one workgroup of 4 waves; lane i of a burst step stores 16
+// bytes at offset 16*(step*256 + i) of the producer's region, so a burst is a
+// fully coalesced sweep of `bytes` bytes.  Successive bursts go to successive
+// regions of a ring that the destination holds.  Every wave records, per burst, the
+// shader clocks from its first store to the issue of its last store (no wait
+// for completion), then spins `gap_cycles` clocks without memory traffic.
+// After the last burst it records how long its stores take to complete.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "xs_burst_gap.h"
+
+namespace xs {
+
+struct BurstGapArgs {
+  uint8_t* dst;
+  unsigned long long* times;
+  size_t bytes;          // per producer and burst
+  long long gap_cycles;
+  int nburst;
+  int producers;
+  int ring;              // regions of producers*bytes bytes in dst, used in turn
+};
+
+constexpr int kBgThreads = 256;
+constexpr int kBgWaves = kBgThreads / 64;
+
+__global__ __launch_bounds__(kBgThreads) void burst_gap_kernel(BurstGapArgs a) {
+  const int p = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t steps = a.bytes / (16 * kBgThreads);
+  const int stride = a.nburst + 3;
+  unsigned long long* out = a.times + ((size_t)p * kBgWaves + wave) * stride;
+
+  __builtin_amdgcn_s_barrier();
+  const uint64_t c_start = __builtin_amdgcn_s_memtime();
+  const uint64_t r_start = __builtin_amdgcn_s_memrealtime();
+  for (int b = 0; b < a.nburst; ++b) {
+    const u32x4 val = {(uint32_t)p, (uint32_t)threadIdx.x, (uint32_t)b, 0x5eedu};
+    // burst b fills region b % ring, so bursts write fresh addresses while the
+    // ring lasts (as output tiles do), not lines still held in a cache
+    uint8_t* region = a.dst + ((size_t)(b % a.ring) * a.producers + p) * a.bytes;
+    asm volatile("" ::: "memory");
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    for (size_t s = 0; s < steps; ++s)
+      *(u32x4*)(region + 16 * (s * kBgThreads + threadIdx.x)) = val;
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    asm volatile("" ::: "memory");
+    if (lane == 0) out[b] = t1 - t0;
+    // the gap: computation-free spin on the clock (no memory traffic)
+    const uint64_t g_end = t1 + (uint64_t)a.gap_cycles;
+    while (__builtin_amdgcn_s_memtime() < g_end) __builtin_amdgcn_s_sleep(1);
+  }
+  const uint64_t d0 = __builtin_amdgcn_s_memtime();
+  wait_vmcnt<0>();
+  const uint64_t d1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r_end = __builtin_amdgcn_s_memrealtime();
+  if (lane == 0) {
+    out[a.nburst] = d1 - d0;                // drain of the last burst after its gap
+    out[a.nburst + 1] = d1 - c_start;       // shader clocks of the whole walk
+    out[a.nburst + 2] = r_end - r_start;    // 100 MHz ticks of the whole walk
+  }
+}
+
+}  // namespace xs
+
+extern "C" int xs_burst_gap(void* dst, size_t dst_bytes, int producers, size_t bytes, int nburst,
+                            long long gap_cycles, unsigned long long* times, void* stream) {
+  if (!dst || !times) return XS_BG_ERR_NULL;
+  if (producers < 1 || producers > 4096 || nburst < 1 || nburst > 4096 || gap_cycles < 0 ||
+      gap_cycles > (1LL << 32) || (long long)nburst * gap_cycles > (1LL << 34) || bytes == 0 ||
+      bytes % (16 * xs::kBgThreads) != 0 || bytes > ((size_t)1 << 30))
+    return XS_BG_ERR_ARG;
+  if (((uintptr_t)dst & 15u) != 0 || ((uintptr_t)times & 7u) != 0) return XS_BG_ERR_ALIGN;
+  const size_t per_burst = (size_t)producers * bytes;
+  if (dst_bytes < per_burst) return XS_BG_ERR_ARG;
+  const size_t ring = dst_bytes / per_burst;
+  xs::BurstGapArgs a{(uint8_t*)dst, times, bytes, gap_cycles, nburst, producers,
+                     (int)(ring < (size_t)nburst ? ring : (size_t)nburst)};
+  void* kargs[] = {&a};
+  if (hipLaunchKernel((const void*)xs::burst_gap_kernel, dim3((unsigned)producers),
+                      dim3(xs::kBgThreads), kargs, 0, (hipStream_t)stream) != hipSuccess)
+    return XS_BG_ERR_LAUNCH;
+  return 0;
+}

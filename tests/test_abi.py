@@ -21,7 +21,8 @@ def test_library_exports_every_declared_function():
     names = _lib.declared_functions()
     assert set(names) == {"xs_attn_fwd", "xs_attn_fwd_fp8", "xs_attn_fwd_ws", "xs_attn_fwd_fp8_ws",
                           "xs_attn_fwd_ex", "xs_attn_fwd_fp8_ex", "xs_attn_workspace_size",
-                          "xs_attn_split_count", "xs_attn_strerror", "xs_attn_version"}
+                          "xs_attn_split_count", "xs_attn_strerror", "xs_attn_version",
+                          "xs_burst_gap"}
     L = _lib.lib()
     for n in names:
         assert getattr(L, n) is not None
@@ -211,3 +212,17 @@ def test_ex_validates_the_base_arguments_first():
     assert _fwd_ex(q=0) == XS_ERR_NULL
     assert _fwd_ex(D=96) == XS_ERR_UNSUPPORTED
     assert _fwd_ex(out=Q) == XS_ERR_OVERLAP
+
+
+def test_burst_gap_validates_before_any_launch():
+    L = _lib.lib()
+    D, T = 0x60000000, 0x70000000
+    assert L.xs_burst_gap(0, 1 << 20, 4, 4096, 2, 0, T, None) == -1
+    assert L.xs_burst_gap(D, 1 << 20, 4, 4096, 2, 0, 0, None) == -1
+    for producers, nbytes, nburst, gap in ((0, 4096, 2, 0), (4097, 4096, 2, 0), (4, 4000, 2, 0),
+                                           (4, 0, 2, 0), (4, 4096, 0, 0), (4, 4096, 2, -1),
+                                           (4, 4096, 2, 1 << 33), (4, 4096, 4096, 1 << 32),
+                                           (1024, 4096, 2, 0)):           # last: dst too small
+        assert L.xs_burst_gap(D, 1 << 20, producers, nbytes, nburst, gap, T, None) == -2
+    assert L.xs_burst_gap(D + 8, 1 << 20, 4, 4096, 2, 0, T, None) == -4
+    assert L.xs_burst_gap(D, 1 << 20, 4, 4096, 2, 0, T + 4, None) == -4
