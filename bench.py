@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--burst-gap", action="store_true",
                     help="characterise the Burst-Gap model with the microbenchmark (fine-grained "
                          "host memory as the remote link) and check it on the attention epilogue")
+    ap.add_argument("--epilogue-overhead", action="store_true",
+                    help="time the fused destination-ordered epilogue against a plain [B][S][H][D] "
+                         "epilogue and against attention followed by a separate relayout")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -105,6 +108,67 @@ def cpu_baseline(w, inp, target_s):
     }
 
 
+def epilogue_overhead(args):
+    """The fused epilogue's cost: the same kernel and schedule writing
+    (a) a plain [B][S][H][D] output (P = 1, the identity relayout),
+    (b) the P-way destination-ordered buffer (the product path), and
+    (c) (a) followed by a separate relayout pass into the P-way buffer (torch
+        copy of a permuted view) -- the serial analogue;
+    on the video share (B = 1: the P-way buffer is byte-identical to [B][S][H][D])
+    and on a B = 2 share (the relayout moves data).  Results must agree bit for bit."""
+    import sequence_attention_amd as xs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    cases = [workloads.WORKLOADS["video"],
+             workloads.custom(2, 32768, 4, 128, 8, index=4, name="video_b2")]
+    results = []
+    for w in cases:
+        inp = workloads.make_inputs(w)
+        q, k, v = (inp[n].to(dev) for n in "qkv")
+        ws_bytes = xs.workspace_size(w.B, w.S, w.H, w.D)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+        plain = torch.empty((1, w.B, w.S, w.H, w.D), dtype=torch.bfloat16, device=dev)
+        packed = torch.empty((w.P, w.B, w.S // w.P, w.H, w.D), dtype=torch.bfloat16, device=dev)
+        serial = torch.empty_like(packed)
+
+        def run_plain():
+            xs.fwd(q, k, v, 1, inp["scale"], out=plain, stream=stream, workspace=ws)
+
+        def run_packed():
+            xs.fwd(q, k, v, w.P, inp["scale"], out=packed, stream=stream, workspace=ws)
+
+        def run_serial():
+            run_plain()
+            serial.copy_(plain[0].view(w.B, w.P, w.S // w.P, w.H, w.D).permute(1, 0, 2, 3, 4))
+
+        fns = (("plain", run_plain), ("packed", run_packed), ("serial", run_serial))
+        for _ in range(args.warmup):
+            for _, fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        # interleaved, so clock and power drift hit the three variants alike
+        samples = {name: [] for name, _ in fns}
+        for _ in range(args.steps):
+            for name, fn in fns:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                samples[name].append(e0.elapsed_time(e1))
+        times = {name: float(np.median(v)) for name, v in samples.items()}
+        same = bool(torch.equal(packed.view(torch.int16), serial.view(torch.int16)))
+        results.append({"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "P": w.P,
+                        "plain_ms": round(times["plain"], 4), "packed_ms": round(times["packed"], 4),
+                        "serial_ms": round(times["serial"], 4),
+                        "packed_vs_plain_pct": round(100 * (times["packed"] / times["plain"] - 1), 2),
+                        "serial_vs_plain_pct": round(100 * (times["serial"] / times["plain"] - 1), 2),
+                        "packed_equals_serial_bitwise": same})
+    print(json.dumps({"metric": "epilogue_overhead", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "results": results}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -113,6 +177,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.epilogue_overhead:
+        epilogue_overhead(args)
         return
     if args.burst_gap:
         from sequence_attention_amd import burst_gap
