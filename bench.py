@@ -35,8 +35,8 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X published dense MFMA pea
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="video", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-baseline sample")

@@ -17,15 +17,18 @@
 //  * The transposed probabilities P^T leave the accumulator already in the
 //    B-operand layout of O^T += V^T P^T (the key order inside a k-step is
 //    permuted identically on both operands), so P never goes through LDS.
-//  * K/V tiles of BN = 64 keys are double buffered in LDS and filled with
-//    direct-to-LDS 16-byte buffer loads (no VGPR round trip).  K rows are XOR
-//    swizzled for conflict-free ds_read_b128 of the A operand; V rows are
-//    swizzled for ds_read_b64_tr_b16, which delivers V^T fragments directly.
-//  * Software pipeline inside the wave, one barrier per block:
+//  * K/V tiles of BN = 64 keys stream through a four-stage LDS ring (128 KiB
+//    for D = 128), filled with direct-to-LDS 16-byte buffer loads (no VGPR
+//    round trip) issued two blocks ahead, with one barrier per two blocks.
+//    K rows are XOR swizzled for conflict-free ds_read_b128 of the A operand;
+//    V rows are swizzled for ds_read_b64_tr_b16, which delivers V^T fragments
+//    directly.
+//  * Software pipeline inside the wave:
 //      step 1: QK^T of block j+1 (MFMA)  ||  exp/sum/convert of keys 0-31 of block j
 //      step 2: P V of block j (MFMA)     ||  exp/sum/convert of keys 32-63 of block j,
 //                                            then the row max of block j+1
-//    so the matrix core and the vector ALU work on different blocks at once.
+//    so the matrix core and the vector ALU work on different blocks at once;
+//    each pair's conversion runs one micro-step after its exponentials.
 //  * Online softmax in base 2: p = 2^(s*c - m), c = scale*log2(e) folded into
 //    one FMA per score.  The running max is moved only when a block's max
 //    exceeds it by more than 2^TAU (p <= 2^TAU), so rescaling O is a rare
@@ -66,6 +69,7 @@ struct Bf16Cfg {
   static constexpr int DT = D / 32;      // 32-row d tiles of O^T
   static constexpr int NT = BN / 32;     // 32-key tiles per block
   static constexpr int THREADS = 64 * NW;
+  static constexpr int STAGES = 4;       // LDS ring depth for K and for V
   static constexpr float TAU = 8.0f;     // lazy-rescale threshold (log2 units)
   static_assert(LOADS % NW == 0 && LOADS >= NW, "tile loads must split evenly over waves");
 };
@@ -129,7 +133,7 @@ template <class C>
 struct Bf16State {
   f32x16 o[C::QT][C::DT];     // O^T accumulators: lane owns query lane%32 of each sub-tile
   u32x4 qf[C::QT][C::KS];     // Q^T B-operand fragments
-  u32x4 pb[C::QT][C::NT][2];  // bf16 probabilities (P^T B-operand fragments)
+  u32x4 pb[C::QT][2 * C::NT]; // bf16 probabilities, P^T B-operand fragment F = keys 16F..16F+15
   float m[C::QT];             // running max of s*c (log2 units), shared by both half-waves
   float l[C::QT];             // lane-local part of the running sum of p
   float alpha[C::QT];         // pending rescale of O (applied before the next P V)
@@ -157,38 +161,20 @@ __device__ __forceinline__ void qk_block(Scores<C>& sc, const Bf16State<C>& st,
   }
 }
 
-// ---- step-2 MFMA work: O^T = alpha O^T + V_j^T P^T
+// O^T *= alpha, one 32x32 tile at a time (the scheduling barriers keep the
+// tiles apart, so the rare rescale does not raise the register pressure).
 template <class C>
-__device__ __forceinline__ void pv_block(Bf16State<C>& st, const uint8_t XS_LDS* sV, int lane) {
-  constexpr int QT = C::QT, NT = C::NT, DT = C::DT, CH = C::CH, ROWB = C::ROWB;
-  if (st.rescale) {
+__device__ __forceinline__ void rescale_o(Bf16State<C>& st) {
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
+  for (int qt = 0; qt < C::QT; ++qt) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) st.o[qt][dt] *= st.alpha[qt];
-      st.alpha[qt] = 1.0f;
+    for (int dt = 0; dt < C::DT; ++dt) {
+      st.o[qt][dt] *= st.alpha[qt];
+      __builtin_amdgcn_sched_barrier(0);
     }
-    st.rescale = false;
+    st.alpha[qt] = 1.0f;
   }
-  const int ln = opaque(lane);
-  const int g = ln >> 4, L = ln & 15;
-  const int vrow = 4 * (g >> 1) + (L >> 2);  // row within an 8-row group
-  const int vsw = vswz<C>(vrow);  // rows of a fragment differ from vrow by multiples of 8
-  const uint8_t XS_LDS* vbase = sV + vrow * ROWB + 8 * (L & 1);
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int chunk = (dt * 4 + 2 * (g & 1) + ((L & 3) >> 1)) ^ vsw;
-        const uint8_t XS_LDS* p0 = vbase + (nt * 32 + 16 * h) * ROWB + (chunk << 4);
-        const u32x2 lo = lds_read_tr16(p0);
-        const u32x2 up = lds_read_tr16(p0 + 8 * ROWB);
-        const u32x4 vf = u32x4{lo[0], lo[1], up[0], up[1]};
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma_bf16(vf, st.pb[qt][nt][h], st.o[qt][dt]);
-      }
+  st.rescale = false;
 }
 
 // Keys at or past S (only in the last, partial block) get score -inf.
@@ -237,17 +223,6 @@ __device__ __forceinline__ void softmax_max(Bf16State<C>& st, const Scores<C>& s
 
 // ---- step-1 VALU work: p = 2^(s c - m) -> bf16 P^T fragments, row sums
 template <class C>
-__device__ __forceinline__ void keep_probs(const Bf16State<C>& st) {
-#pragma unroll
-  for (int qt = 0; qt < C::QT; ++qt)
-#pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) {
-      keep(st.pb[qt][nt][0]);
-      keep(st.pb[qt][nt][1]);
-    }
-}
-
-template <class C>
 __device__ __forceinline__ void softmax_exp(Bf16State<C>& st, const Scores<C>& sc, float c) {
   constexpr int QT = C::QT, NT = C::NT;
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
@@ -267,7 +242,7 @@ __device__ __forceinline__ void softmax_exp(Bf16State<C>& st, const Scores<C>& s
           w[i] = pack_bf16(p0, p1);
           lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]), ones, lsum, false);
         }
-        st.pb[qt][nt][h] = u32x4{w[0], w[1], w[2], w[3]};
+        st.pb[qt][2 * nt + h] = u32x4{w[0], w[1], w[2], w[3]};
       }
     st.l[qt] = lsum;
   }
@@ -292,7 +267,7 @@ __device__ __forceinline__ void softmax_exp(Bf16State<C>& st, const Scores<C>& s
 template <class C>
 struct LdsOffs {
   uint32_t k[C::KS];  // K fragment of k-step ks (row lane%32, chunk 2ks + lane/32)
-  uint32_t v[C::DT];  // first V^T transpose read of d-tile dt (rows 0..7 group)
+  uint32_t v[C::DT];  // first V^T transpose read of d-tile dt (rows 0..7 group), V region
 };
 
 template <class C>
@@ -308,47 +283,76 @@ __device__ __forceinline__ LdsOffs<C> lds_offsets(int lane) {
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) {
     const int chunk = (dt * 4 + 2 * (g & 1) + ((L & 3) >> 1)) ^ vsw;
-    o.v[dt] = (uint32_t)(vrow * C::ROWB + 8 * (L & 1) + (chunk << 4));
+    o.v[dt] = (uint32_t)(C::STAGES * C::TILE + vrow * C::ROWB + 8 * (L & 1) + (chunk << 4));
   }
   return o;
 }
 
-// exp2(s c - m) of score pair e (0..7) of 32-key tile nt, query sub-tile qt,
-// packed to bf16, added to the row sum; pinned to the current micro-step.
+// The probabilities of one score pair in two halves, a micro-step apart, so
+// the conversion never waits on the transcendental unit's latency:
+//  exp_pair2: p = 2^(s c - m) of pair idx (0 .. 8 NT - 1: registers 2(idx%8),
+//             2(idx%8)+1 of 32-key tile idx/8) of query sub-tile qt;
+//  pack_sum:  the pair rounded to bf16 (word idx%4 of P^T fragment idx/4) and
+//             added to the row sum.
+// Both are pinned to the micro-step they are issued in.
 template <class C>
-__device__ __forceinline__ void exp_pair(const Scores<C>& cur, int qt, int nt, int e, float c,
-                                         float neg_m, float& lsum, uint32_t& w) {
+__device__ __forceinline__ f32x2 exp_pair2(const Scores<C>& cur, int qt, int idx, float c,
+                                           float neg_m) {
+  const int nt = idx / 8, e = idx % 8;
+  float p0 = fast_exp2(__builtin_fmaf(cur.s[nt][qt][2 * e], c, neg_m));
+  float p1 = fast_exp2(__builtin_fmaf(cur.s[nt][qt][2 * e + 1], c, neg_m));
+  pin(p0);
+  pin(p1);
+  return f32x2{p0, p1};
+}
+
+__device__ __forceinline__ uint32_t pack_sum(f32x2 p, float& lsum) {
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  const float p0 = fast_exp2(__builtin_fmaf(cur.s[nt][qt][2 * e], c, neg_m));
-  const float p1 = fast_exp2(__builtin_fmaf(cur.s[nt][qt][2 * e + 1], c, neg_m));
-  uint32_t pk = pack_bf16(p0, p1);
+  uint32_t pk = pack_bf16(p[0], p[1]);
   lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, lsum, false);
   pin(pk);
   pin(lsum);
-  w = pk;
+  return pk;
 }
 
-// Step 1: S^T of the next block from K stage KST || probabilities of keys 0..31
-// of the current block.  Each K fragment feeds the QT query sub-tiles.
+#ifndef XS_NE1
+#define XS_NE1 0
+#endif
+
+// The score pairs of a block in the order the pipeline computes them: first
+// those of the first half of the block's keys (P^T fragments F < NT, used by
+// the first half of P V) for every sub-tile, then those of the second half.
+// Step 1 computes pairs 0 .. NE1-1, step 2 the rest under its first half.
+template <class C>
+struct PairOrder {
+  static constexpr int HP = 4 * C::NT * C::QT;  // pairs per half
+  static constexpr int NP = 2 * HP;
+  static constexpr int NE1 = XS_NE1 > 0 && XS_NE1 <= NP && XS_NE1 >= HP ? XS_NE1 : HP;
+  static constexpr int qt(int k) { return (k % HP) / (4 * C::NT); }
+  static constexpr int idx(int k) { return (k / HP) * 4 * C::NT + k % (4 * C::NT); }
+};
+
+// Step 1: S^T of the next block from K stage KST || the first NE1 probability
+// pairs of the current block.  Each K fragment feeds the QT query sub-tiles.
 template <class C, int KST>
 __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16State<C>& st,
                                       const uint8_t XS_LDS* lds, const LdsOffs<C>& off, float c) {
-  static_assert(C::NT == 2, "pipeline written for 64-key blocks");
+  using PO = PairOrder<C>;
   constexpr int QT = C::QT, NT = C::NT, KS = C::KS, ROWB = C::ROWB;
   constexpr int NF = KS * NT;
   constexpr int LEAD = XS_LEAD < NF ? XS_LEAD : NF;
   constexpr int R = LEAD + 1;
-  constexpr int NE = 8 * QT;  // score pairs of keys 0..31, all sub-tiles
+  constexpr int NE = PO::NE1;
   const uint8_t XS_LDS* kb = lds + KST * C::TILE;
   auto kread = [&](int f) { return lds_read_b128(kb + off.k[f / NT] + (f % NT) * 32 * ROWB); };
   float neg_m[QT], lsum[QT];
-  uint32_t w[QT][8];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     neg_m[qt] = -st.m[qt];
     lsum[qt] = st.l[qt];
   }
   u32x4 kf[R];
+  f32x2 pe[NE];
 #pragma unroll
   for (int f = 0; f < LEAD; ++f) kf[f] = kread(f);
 #pragma unroll
@@ -358,52 +362,52 @@ __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
       nxt.s[nt][qt] = mfma_bf16(kf[f % R], st.qf[qt][ks], ks == 0 ? f32x16{} : nxt.s[nt][qt]);
-    // the score pairs of tile 0, spread evenly over the NF micro-steps
+    // the first NE pairs, spread evenly over the NF micro-steps: packed one
+    // micro-step after their exponentials
 #pragma unroll
-    for (int e = 0; e < NE; ++e)
-      if (e * NF / NE == f) exp_pair<C>(cur, e / 8, 0, e % 8, c, neg_m[e / 8], lsum[e / 8], w[e / 8][e % 8]);
+    for (int k = 0; k < NE; ++k)
+      if (f > 0 && k * NF / NE == f - 1) {
+        const int qt = PO::qt(k), idx = PO::idx(k);
+        st.pb[qt][idx / 4][idx % 4] = pack_sum(pe[k], lsum[qt]);
+      }
+#pragma unroll
+    for (int k = 0; k < NE; ++k)
+      if (k * NF / NE == f) pe[k] = exp_pair2<C>(cur, PO::qt(k), PO::idx(k), c, neg_m[PO::qt(k)]);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
+  for (int k = 0; k < NE; ++k)
+    if (k * NF / NE == NF - 1) {
+      const int qt = PO::qt(k), idx = PO::idx(k);
+      st.pb[qt][idx / 4][idx % 4] = pack_sum(pe[k], lsum[qt]);
+    }
+#pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     st.l[qt] = lsum[qt];
-    st.pb[qt][0][0] = u32x4{w[qt][0], w[qt][1], w[qt][2], w[qt][3]};
-    st.pb[qt][0][1] = u32x4{w[qt][4], w[qt][5], w[qt][6], w[qt][7]};
-    keep(st.pb[qt][0][0]);
-    keep(st.pb[qt][0][1]);
+#pragma unroll
+    for (int F = 0; F < 2 * NT; ++F) keep(st.pb[qt][F]);
   }
 }
 
 // Step 2: O^T = alpha O^T + V^T P^T from V stage VST; under the first half
-// (keys 0..31) the probabilities of keys 32..63, under the second half the row
-// max of the next block (lazy move of the running max; the O rescale it may
-// ask for is applied at the start of the next step 2).
+// (the first half of the block's keys) the remaining probability pairs, under
+// the second half the row max of the next block (lazy move of the running max;
+// the O rescale it may ask for is applied at the start of the next step 2).
 template <class C, int VST>
 __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, const Scores<C>& cur,
                                       const uint8_t XS_LDS* lds, const LdsOffs<C>& off, float c) {
+  using PO = PairOrder<C>;
   constexpr int QT = C::QT, NT = C::NT, DT = C::DT, ROWB = C::ROWB;
-  constexpr int NF = NT * 2 * DT;          // V fragments, keys 0..31 first
+  constexpr int NF = 2 * NT * DT;          // V fragments F-major: keys 16F..16F+15
   constexpr int HALF = NF / 2;
   constexpr int LEAD = XS_LEAD < NF ? XS_LEAD : NF;
   constexpr int R = LEAD + 1;
-  constexpr int NE = 8 * QT;               // score pairs of keys 32..63
-  constexpr int NM = 32 * QT;              // scores of the next block per lane
-  if (st.rescale) {
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) st.o[qt][dt] *= st.alpha[qt];
-      st.alpha[qt] = 1.0f;
-    }
-    st.rescale = false;
-  }
-  const uint8_t XS_LDS* vb = lds + (2 + VST) * C::TILE;
-  auto vaddr = [&](int f) {
-    const int nt = f / (2 * DT), h = (f / DT) % 2, dt = f % DT;
-    return vb + off.v[dt] + (nt * 32 + 16 * h) * ROWB;
-  };
+  constexpr int NE = PO::NP - PO::NE1;     // pairs left for this step
+  constexpr int NM = 16 * NT * QT;         // scores of the next block per lane
+  if (st.rescale) rescale_o<C>(st);
+  const uint8_t XS_LDS* vb = lds + VST * C::TILE;  // off.v holds the V region's base
+  auto vaddr = [&](int f) { return vb + off.v[f % DT] + (f / DT) * 16 * ROWB; };
   float neg_m[QT], lsum[QT], mx[QT];
-  uint32_t w[QT][8];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     neg_m[qt] = -st.m[qt];
@@ -411,6 +415,7 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, co
     mx[qt] = nxt.s[0][qt][0];
   }
   u32x2 vlo[R], vhi[R];
+  f32x2 pe[NE > 0 ? NE : 1];
 #pragma unroll
   for (int f = 0; f < LEAD; ++f) {
     vlo[f] = lds_read_tr16(vaddr(f));
@@ -422,29 +427,31 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, co
       vlo[(f + LEAD) % R] = lds_read_tr16(vaddr(f + LEAD));
       vhi[(f + LEAD) % R] = lds_read_tr16(vaddr(f + LEAD) + 8 * ROWB);
     }
-    if (f == HALF) {
-      // probabilities of keys 32..63 complete: assemble their operands
+    // pack the pairs whose exponentials the previous micro-step issued (before
+    // this micro-step's MFMA, which may need them)
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        st.pb[qt][1][0] = u32x4{w[qt][0], w[qt][1], w[qt][2], w[qt][3]};
-        st.pb[qt][1][1] = u32x4{w[qt][4], w[qt][5], w[qt][6], w[qt][7]};
+    for (int k = 0; k < NE; ++k)
+      if (f > 0 && f <= HALF && k * HALF / NE == f - 1) {
+        const int qt = PO::qt(PO::NE1 + k), idx = PO::idx(PO::NE1 + k);
+        st.pb[qt][idx / 4][idx % 4] = pack_sum(pe[k], lsum[qt]);
       }
-    }
-    const int nt = f / (2 * DT), h = (f / DT) % 2, dt = f % DT;
+    const int F = f / DT, dt = f % DT;
     const u32x4 vf = u32x4{vlo[f % R][0], vlo[f % R][1], vhi[f % R][0], vhi[f % R][1]};
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma_bf16(vf, st.pb[qt][nt][h], st.o[qt][dt]);
+    for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma_bf16(vf, st.pb[qt][F], st.o[qt][dt]);
     if (f < HALF) {
 #pragma unroll
-      for (int e = 0; e < NE; ++e)
-        if (e * HALF / NE == f)
-          exp_pair<C>(cur, e / 8, 1, e % 8, c, neg_m[e / 8], lsum[e / 8], w[e / 8][e % 8]);
+      for (int k = 0; k < NE; ++k)
+        if (k * HALF / NE == f) {
+          const int qt = PO::qt(PO::NE1 + k), idx = PO::idx(PO::NE1 + k);
+          pe[k] = exp_pair2<C>(cur, qt, idx, c, neg_m[qt]);
+        }
     } else {
       constexpr int EPS = NM / HALF;  // max over the scores of the next block
 #pragma unroll
       for (int ee = 0; ee < EPS; ++ee) {
         const int e = (f - HALF) * EPS + ee;  // 0 .. NM-1
-        const int qt = e / 32, r = e % 32;
+        const int qt = e / (16 * NT), r = e % (16 * NT);
         mx[qt] = fmaxf(mx[qt], nxt.s[r / 16][qt][r % 16]);
       }
 #pragma unroll
@@ -473,22 +480,61 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, co
   }
 }
 
-// Takes the next piece of the walk and issues its first loads (K and V of
-// block jb into stage 0, K of jb+1 into stage 1).
+// O^T = alpha O^T + V^T P^T of the last block of a piece from the V stage at
+// byte offset stage_off (no next block to overlap with: its probabilities are
+// complete).
+template <class C>
+__device__ __forceinline__ void pv_only(Bf16State<C>& st, const uint8_t XS_LDS* lds,
+                                        const LdsOffs<C>& off, uint32_t stage_off) {
+  constexpr int QT = C::QT, DT = C::DT, ROWB = C::ROWB;
+  constexpr int NF = 2 * C::NT * DT;
+  constexpr int LEAD = XS_LEAD < NF ? XS_LEAD : NF;
+  constexpr int R = LEAD + 1;
+  if (st.rescale) rescale_o<C>(st);
+  const uint8_t XS_LDS* vb = lds + stage_off;
+  auto vaddr = [&](int f) { return vb + off.v[f % DT] + (f / DT) * 16 * ROWB; };
+  u32x2 vlo[R], vhi[R];
+#pragma unroll
+  for (int f = 0; f < LEAD; ++f) {
+    vlo[f] = lds_read_tr16(vaddr(f));
+    vhi[f] = lds_read_tr16(vaddr(f) + 8 * ROWB);
+  }
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + LEAD < NF) {
+      vlo[(f + LEAD) % R] = lds_read_tr16(vaddr(f + LEAD));
+      vhi[(f + LEAD) % R] = lds_read_tr16(vaddr(f + LEAD) + 8 * ROWB);
+    }
+    const u32x4 vf = u32x4{vlo[f % R][0], vlo[f % R][1], vhi[f % R][0], vhi[f % R][1]};
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) st.o[qt][f % DT] = mfma_bf16(vf, st.pb[qt][f / DT], st.o[qt][f % DT]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Takes the next piece of the walk and issues its first loads: K of blocks jb,
+// jb+1, jb+2 and V of blocks jb, jb+1 into ring stages 0, 1, 2 (stage of block
+// i = (i - jb) % 4).
 template <class C>
 __device__ __forceinline__ PieceAddr begin_piece(ShareWalk& walk, const Sched& sch, const AttnArgs& a,
                                                  int nblk, uint32_t row_stride, uint8_t XS_LDS* lds,
                                                  const uint32_t (&koff)[C::LPW],
                                                  const uint32_t (&voff)[C::LPW], int wave, int& slot) {
-  PieceAddr pa = next_piece<C::BM, C::ROWB>(walk, sch, a, nblk, row_stride, slot);
+  PieceAddr pa = next_piece<C::BM, C::ROWB, C::BN>(walk, sch, a, nblk, row_stride, slot);
   const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
   const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
+  uint8_t XS_LDS* const vlds = lds + C::STAGES * C::TILE;
   load_tile<C>(kbase, row_stride, pa.jb * C::BN, pa.kcur.at(pa.jb), a.S, lds, koff, wave);
-  load_tile<C>(vbase, row_stride, pa.jb * C::BN, pa.vcur.at(pa.jb), a.S, lds + 2 * C::TILE, voff,
-               wave);
-  if (pa.jb + 1 < pa.je)
+  load_tile<C>(vbase, row_stride, pa.jb * C::BN, pa.vcur.at(pa.jb), a.S, vlds, voff, wave);
+  if (pa.jb + 1 < pa.je) {
     load_tile<C>(kbase, row_stride, (pa.jb + 1) * C::BN, pa.kcur.at(pa.jb + 1), a.S, lds + C::TILE,
                  koff, wave);
+    load_tile<C>(vbase, row_stride, (pa.jb + 1) * C::BN, pa.vcur.at(pa.jb + 1), a.S,
+                 vlds + C::TILE, voff, wave);
+  }
+  if (pa.jb + 2 < pa.je)
+    load_tile<C>(kbase, row_stride, (pa.jb + 2) * C::BN, pa.kcur.at(pa.jb + 2), a.S,
+                 lds + 2 * C::TILE, koff, wave);
   return pa;
 }
 
@@ -518,11 +564,11 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[C::QT][C::KS], const AttnArgs
 template <class C>
 __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int QT = C::QT, DT = C::DT, BN = C::BN;
-  // K stage 0 | K stage 1 | V stage 0 | V stage 1
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];
+  // K stages 0..3 | V stages 0..3
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGES * C::TILE];
   uint8_t XS_LDS* const lds = (uint8_t XS_LDS*)smem;
-  auto kbuf = [&](int i) { return lds + (i & 1) * C::TILE; };
-  auto vbuf = [&](int i) { return lds + (2 + (i & 1)) * C::TILE; };
+  auto kbuf = [&](int s) { return lds + s * C::TILE; };
+  auto vbuf = [&](int s) { return lds + (C::STAGES + s) * C::TILE; };
 
   const int S = a.S, H = a.H, T = a.T, B = a.B;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -567,55 +613,83 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
 
     // prologue: score block jb and take its max
     Scores<C> sa, sb;
-    qk_block<C>(sa, st, kbuf(jb), lane);
+    qk_block<C>(sa, st, kbuf(0), lane);
     if (jb >= nfull) mask_tail<C>(sa, jb * BN, S, lane);
     softmax_max<C>(st, sa, c);
 
-    // Steady state, two blocks per trip so the score buffers swap statically.
-    // Entering a step for block i: scores of block i are in one buffer with
-    // their max taken; K_{i+1} and V_i are loaded (or in flight).
-    // (jb is even: K_i and V_i live in stage i % 2)
+    // K/V blocks stream through a four-stage LDS ring (block i in stage
+    // (i - jb) % 4) with one barrier per two blocks: at the barrier before
+    // blocks i, i+1 (i - jb even) the loads of K_{i+1}, K_{i+2}, V_i, V_{i+1}
+    // (issued at the previous barrier) are complete and every wave is done
+    // with blocks i-2, i-1, so K_{i+3}, K_{i+4}, V_{i+2}, V_{i+3} go into the
+    // stages those blocks used.  Entering a step for block i: its scores are in
+    // one buffer with their max taken.  Four blocks per trip keep the stages
+    // and score buffers static.
+    auto ld_k = [&](int i, int stage) {
+      load_tile<C>(kbase, row_stride, i * BN, pa.kcur.at(i), S, kbuf(stage), koff, wave);
+    };
+    auto ld_v = [&](int i, int stage) {
+      load_tile<C>(vbase, row_stride, i * BN, pa.vcur.at(i), S, vbuf(stage), voff, wave);
+    };
     int j = jb;
-    for (; j + 2 < je; j += 2) {
-      // ---- block j (scores in sa), next block's scores into sb
+    for (; j + 4 < je; j += 4) {
       wait_vmcnt<0>();
       __syncthreads();
-      load_tile<C>(kbase, row_stride, (j + 2) * BN, pa.kcur.at(j + 2), S, kbuf(0), koff, wave);
-      load_tile<C>(vbase, row_stride, (j + 1) * BN, pa.vcur.at(j + 1), S, vbuf(1), voff, wave);
-      step1<C, 1>(sb, sa, st, lds, off, c);
+      ld_k(j + 3, 3);
+      ld_k(j + 4, 0);
+      ld_v(j + 2, 2);
+      ld_v(j + 3, 3);
+      step1<C, 1>(sb, sa, st, lds, off, c);  // block j
       if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
       step2<C, 0>(st, sb, sa, lds, off, c);
-
-      // ---- block j+1 (scores in sb), next block's scores into sa
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (j + 3 < je)
-        load_tile<C>(kbase, row_stride, (j + 3) * BN, pa.kcur.at(j + 3), S, kbuf(1), koff, wave);
-      load_tile<C>(vbase, row_stride, (j + 2) * BN, pa.vcur.at(j + 2), S, vbuf(0), voff, wave);
-      step1<C, 0>(sa, sb, st, lds, off, c);
+      step1<C, 2>(sa, sb, st, lds, off, c);  // block j+1
       if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
       step2<C, 1>(st, sa, sb, lds, off, c);
+
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (j + 5 < je) ld_k(j + 5, 1);
+      if (j + 6 < je) ld_k(j + 6, 2);
+      ld_v(j + 4, 0);
+      if (j + 5 < je) ld_v(j + 5, 1);
+      step1<C, 3>(sb, sa, st, lds, off, c);  // block j+2
+      if (j + 3 >= nfull) mask_tail<C>(sb, (j + 3) * BN, S, lane);
+      step2<C, 2>(st, sb, sa, lds, off, c);
+      step1<C, 0>(sa, sb, st, lds, off, c);  // block j+3
+      if (j + 4 >= nfull) mask_tail<C>(sa, (j + 4) * BN, S, lane);
+      step2<C, 3>(st, sa, sb, lds, off, c);
     }
-    // the last one or two blocks (scores of block j in sa)
-    if (j + 1 < je) {
+    // the last one to four blocks j .. je-1 (stages 0..3, scores of block j in sa)
+    {
+      const int r = je - j;
       wait_vmcnt<0>();
       __syncthreads();
-      load_tile<C>(vbase, row_stride, (j + 1) * BN, pa.vcur.at(j + 1), S, vbuf(j + 1), voff, wave);
-      qk_block<C>(sb, st, kbuf(j + 1), lane);
-      softmax_exp<C>(st, sa, c);
-      __builtin_amdgcn_sched_barrier(0);
-      if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
-      pv_block<C>(st, vbuf(j), lane);
-      softmax_max<C>(st, sb, c);
-      wait_vmcnt<0>();
-      __syncthreads();
-      softmax_exp<C>(st, sb, c);
-      pv_block<C>(st, vbuf(j + 1), lane);
-    } else {
-      wait_vmcnt<0>();  // V_j may have been issued by the last loop step
-      __syncthreads();
-      softmax_exp<C>(st, sa, c);
-      pv_block<C>(st, vbuf(j), lane);
+      if (r > 3) ld_k(j + 3, 3);
+      if (r > 2) ld_v(j + 2, 2);
+      if (r > 3) ld_v(j + 3, 3);
+      if (r > 1) {
+        step1<C, 1>(sb, sa, st, lds, off, c);  // block j
+        if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
+        step2<C, 0>(st, sb, sa, lds, off, c);
+      }
+      if (r > 2) {
+        step1<C, 2>(sa, sb, st, lds, off, c);  // block j+1
+        if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
+        step2<C, 1>(st, sa, sb, lds, off, c);
+        wait_vmcnt<0>();
+        __syncthreads();
+      }
+      if (r > 3) {
+        step1<C, 3>(sb, sa, st, lds, off, c);  // block j+2
+        if (j + 3 >= nfull) mask_tail<C>(sb, (j + 3) * BN, S, lane);
+        step2<C, 2>(st, sb, sa, lds, off, c);
+      }
+      // the last block, j + r - 1: scores in sa when r is odd
+      if (r & 1)
+        softmax_exp<C>(st, sa, c);
+      else
+        softmax_exp<C>(st, sb, c);
+      pv_only<C>(st, lds, off, (uint32_t)(r - 1) * C::TILE);
     }
 
     // ---- next piece: request its first K/V blocks and its queries before
@@ -683,7 +757,7 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
 template <int D>
 static hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   using C = Bf16Cfg<D, XS_QT, XS_NW, XS_BN>;
-  static_assert(C::BM == kBlockM && C::BN == kBlockN, "tile geometry");
+  static_assert(C::BM == kBlockM, "tile geometry");
   if (a.groups < 1) return hipErrorInvalidValue;
   AttnArgs args = a;
   void* kargs[] = {&args};

@@ -344,7 +344,7 @@ __device__ __forceinline__ PieceAddr begin_piece8(ShareWalk& walk, const Sched& 
                                                   const AttnArgs& a, int nblk, uint32_t row_stride,
                                                   uint8_t XS_LDS* lds, uint32_t koff,
                                                   uint32_t voff, int wave, int& slot) {
-  PieceAddr pa = next_piece<C::BM, C::ROWB>(walk, sch, a, nblk, row_stride, slot);
+  PieceAddr pa = next_piece<C::BM, C::ROWB, C::BN>(walk, sch, a, nblk, row_stride, slot);
   const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
   const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
   load_tile8<C>(kbase, row_stride, pa.jb * C::BN, pa.kcur.at(pa.jb), a.S, lds, koff, wave);

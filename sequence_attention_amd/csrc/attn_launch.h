@@ -46,7 +46,8 @@ struct AttnArgs {
 #define XS_WGPC 1
 #endif
 constexpr int kBlockM = XS_BM;         // query rows per workgroup
-constexpr int kBlockN = 64;            // keys per K/V block
+constexpr int kBlockN = 64;            // keys per K/V block of the schedule
+constexpr int kUnitKeys = 2 * kBlockN; // keys per schedule unit (a pair of blocks)
 constexpr int kGroupsPerCU = XS_WGPC;  // workgroups resident per compute unit
 
 // The work schedule, shared by the kernels, the merge and the host plan.

@@ -171,8 +171,9 @@ struct ChunkCursor {
     nb = (p + 1) * tpc;
     ex = (size_t)p * step;
   }
+  // n must not decrease from one call to the next
   __device__ size_t at(int n) {
-    if (n >= nb) {
+    while (n >= nb) {
       nb += tpc;
       ex += step;
     }

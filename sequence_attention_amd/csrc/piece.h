@@ -30,10 +30,10 @@ struct ShareWalk {
   __device__ bool more(const Sched& s) const { return round < s.dp || u < uend; }
 };
 
-// The next piece of the walk (more() must hold), for query tiles of BM rows
-// and input rows of ROWB bytes (one head); `slot` receives the workspace slot
-// a cut piece writes.
-template <int BM, int ROWB>
+// The next piece of the walk (more() must hold), for query tiles of BM rows,
+// input rows of ROWB bytes (one head) and key blocks of BN keys (nblk blocks
+// in all); `slot` receives the workspace slot a cut piece writes.
+template <int BM, int ROWB, int BN>
 __device__ __forceinline__ PieceAddr next_piece(ShareWalk& w, const Sched& sch, const AttnArgs& a,
                                                 int nblk, uint32_t row_stride, int& slot) {
   const int npair = sch.npair, mtiles = (a.S + BM - 1) / BM;
@@ -59,8 +59,10 @@ __device__ __forceinline__ PieceAddr next_piece(ShareWalk& w, const Sched& sch, 
   pa.m0 = (tile - pa.bh * mtiles) * BM;
   pa.h = pa.bh % a.H;
   pa.b = pa.bh / a.H;
-  pa.jb = 2 * p0;
-  pa.je = 2 * p1 < nblk ? 2 * p1 : nblk;
+  static_assert(kUnitKeys % (2 * BN) == 0, "a unit holds an even number of blocks");
+  constexpr int BPU = kUnitKeys / BN;  // key blocks per unit
+  pa.jb = BPU * p0;
+  pa.je = BPU * p1 < nblk ? BPU * p1 : nblk;
   pa.whole = p0 == 0 && p1 == npair;
   pa.head_off = ((size_t)pa.b * a.batch_rows * a.H + pa.h) * ROWB;
   pa.kcur.init(pa.jb, a.chunk_rows, a.jump_rows, row_stride);
