@@ -5,9 +5,9 @@
 // Same operation as the bf16 kernel (X-Stage paper, catalyzex.com abstract;
 // gist.science explainer, "Zentrale Beitraege", "FlashAttention-A2A
 // (Piggybacking)"): per workgroup 8 waves x 32 query rows of one (b, h), K/V
-// blocks of 64 keys double buffered in LDS via direct-to-LDS loads, a software
-// pipeline of pinned micro-steps inside each wave.  What differs for 8-bit
-// operands:
+// blocks of 64 keys in a four-stage LDS ring filled by direct-to-LDS loads
+// (one barrier per two blocks), a software pipeline of pinned micro-steps
+// inside each wave.  What differs for 8-bit operands:
 //  * Both contractions use v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3 -> fp32):
 //    S^T = K Q^T takes D/64 k-steps; O^T += V^T P^T takes one k-step of all 64
 //    keys of the block per 32-row d tile.
@@ -18,16 +18,22 @@
 //    {8g + 4h + i}; the V tile is stored in LDS with its rows permuted so that
 //    those keys are 32 consecutive rows, which ds_read_b64_tr_b8 turns into
 //    the V^T operand in the same order.
-//  * Row sums add the fp32 probabilities before quantisation.
+//  * The row sums that normalise O are those of the quantised P, computed on
+//    the matrix core: one more MFMA per block with an all-ones A operand
+//    (the vector ALU, not the matrix core, bounds this kernel).  When the
+//    log-sum-exp output is requested, a second instantiation instead adds the
+//    fp32 probabilities before quantisation and normalises with that sum,
+//    which the log-sum-exp is defined by.
 #include "attn_launch.h"
 #include "device_common.h"
 #include "piece.h"
 
 namespace xs {
 
-template <int D_>
+template <int D_, bool LSE_>
 struct Fp8Cfg {
   static constexpr int D = D_;
+  static constexpr bool LSE = LSE_;       // also keep fp32 row sums for the log-sum-exp output
   static constexpr int NW = 8;            // waves per workgroup, 32 query rows each
   static constexpr int BN = 64;           // keys per K/V block
   static constexpr int QW = 32;
@@ -41,6 +47,7 @@ struct Fp8Cfg {
   static constexpr int DT = D / 32;       // 32-row d tiles of O^T
   static constexpr int NT = BN / 32;      // 32-key score tiles per block
   static constexpr int THREADS = 64 * NW;
+  static constexpr int STAGES = 4;        // LDS ring depth for K and for V
   static constexpr float TAU = 8.0f;      // lazy-rescale threshold (log2 units)
   static_assert(LOADS <= NW, "one direct load per wave at most");
   static_assert(NT == 2, "the P^T operand layout assumes 64-key blocks");
@@ -77,11 +84,21 @@ struct Scores8 {
 template <class C>
 struct Fp8State {
   f32x16 o[C::DT];
+  f32x16 lt;         // row sums of the quantised P (each register holds the lane's row sum)
   i32x8 qf[C::KS];
   u32x4 p0, p1;      // P^T operand: e4m3 probabilities of keys 0..31 and 32..63
-  float m, l, alpha;
+  float m, alpha;
+  float l32;         // lane-local fp32 sum of the unquantised p (kept only when C::LSE)
   bool rescale;
 };
+
+// The A operand of the row-sum MFMA: every element e4m3 1.0 (0x38), so
+// lt += ONES P^T adds each query's sum of quantised probabilities to all 32
+// rows of its column.
+__device__ __forceinline__ i32x8 ones_e4m3() {
+  const int w = 0x38383838;
+  return i32x8{w, w, w, w, w, w, w, w};
+}
 
 template <class C>
 __device__ __forceinline__ void qk_block8(Scores8<C>& sc, const Fp8State<C>& st,
@@ -128,10 +145,32 @@ __device__ __forceinline__ void softmax_max8(Fp8State<C>& st, const Scores8<C>& 
   if (__builtin_amdgcn_ballot_w64(need)) {
     const float a = need ? fast_exp2(st.m - mnew) : 1.0f;
     st.m = need ? mnew : st.m;
-    st.l *= a;
     st.alpha *= a;
+    if (C::LSE) st.l32 *= a;
     st.rescale = true;
   }
+}
+
+// The row sum that normalises O: without the log-sum-exp output, the sum of
+// the quantised probabilities that entered P V (from the row-sum MFMA; every
+// register of lt holds it); with it, the fp32 sum of the unquantised
+// probabilities (the sum the log-sum-exp is defined by).
+template <class C>
+__device__ __forceinline__ float row_sum(const Fp8State<C>& st) {
+  return C::LSE ? sum_halves(st.l32) : st.lt[0];
+}
+
+// O^T and the row sums *= alpha (rare: only when the running max moved).
+template <class C>
+__device__ __forceinline__ void rescale_o8(Fp8State<C>& st) {
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+    st.o[dt] *= st.alpha;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (!C::LSE) st.lt *= st.alpha;
+  st.alpha = 1.0f;
+  st.rescale = false;
 }
 
 #ifndef XS_LEAD8
@@ -176,21 +215,28 @@ __device__ __forceinline__ LdsOffs8<C> lds_offsets8(int lane) {
   return o;
 }
 
-// p = 2^(s c - m) of scores 4q..4q+3 of 32-key tile nt, packed to four e4m3
-// bytes, fp32 values added to the row sum; pinned to the current micro-step.
+// The probabilities of scores 4q..4q+3 of 32-key tile nt in two halves, a
+// micro-step apart, so the conversion never waits on the transcendental
+// unit's latency: exp4 computes p = 2^(s c - m), pack4 rounds them to four
+// e4m3 bytes.  Both are pinned to the micro-step they are issued in.
 template <class C>
-__device__ __forceinline__ void exp_quad(const Scores8<C>& sc, int nt, int q, float c, float neg_m,
-                                         float& lsum, uint32_t& w) {
+__device__ __forceinline__ f32x4 exp4(const Scores8<C>& sc, int nt, int q, float c, float neg_m,
+                                      float& lsum) {
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     p[i] = fast_exp2(__builtin_fmaf(sc.s[nt][4 * q + i], c, neg_m));
-    lsum += p[i];
+    if (C::LSE) lsum += p[i];
+    pin(p[i]);
   }
+  if (C::LSE) pin(lsum);
+  return f32x4{p[0], p[1], p[2], p[3]};
+}
+
+__device__ __forceinline__ uint32_t pack4(f32x4 p) {
   uint32_t pk = pack_fp8x4(p[0], p[1], p[2], p[3]);
   pin(pk);
-  pin(lsum);
-  w = pk;
+  return pk;
 }
 
 // Step A: S^T of the next block from K stage KST || keys 32..63 of the current
@@ -210,8 +256,9 @@ __device__ __forceinline__ void step_a8(Scores8<C>& nxt, const Scores8<C>& cur, 
     return __builtin_bit_cast(i32x8, (u32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}));
   };
   const float neg_m = -st.m;
-  float lsum = st.l;
+  float lsum = st.l32;
   uint32_t w[4];
+  f32x4 pe[4];
   i32x8 kf[R];
 #pragma unroll
   for (int f = 0; f < LEAD; ++f) kf[f] = kread(f);
@@ -222,10 +269,16 @@ __device__ __forceinline__ void step_a8(Scores8<C>& nxt, const Scores8<C>& cur, 
     nxt.s[nt] = mfma_fp8(kf[f % R], st.qf[t], t == 0 ? f32x16{} : nxt.s[nt]);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      if (q * NF / 4 == f) exp_quad<C>(cur, 1, q, c, neg_m, lsum, w[q]);
+      if (f > 0 && q * NF / 4 == f - 1) w[q] = pack4(pe[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q * NF / 4 == f) pe[q] = exp4<C>(cur, 1, q, c, neg_m, lsum);
     __builtin_amdgcn_sched_barrier(0);
   }
-  st.l = lsum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q * NF / 4 == NF - 1) w[q] = pack4(pe[q]);
+  st.l32 = lsum;
   st.p1 = u32x4{w[0], w[1], w[2], w[3]};
   keep(st.p1);
 }
@@ -240,15 +293,10 @@ __device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
   constexpr int HALF = NF / 2;
   constexpr int LEAD = XS_LEAD8 < NF ? XS_LEAD8 : NF;
   constexpr int R = LEAD + 1;
-  if (st.rescale) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st.o[dt] *= st.alpha;
-    st.alpha = 1.0f;
-    st.rescale = false;
-  }
+  if (st.rescale) rescale_o8<C>(st);
   const i32x8 pf = __builtin_bit_cast(
       i32x8, (u32x8{st.p0[0], st.p0[1], st.p0[2], st.p0[3], st.p1[0], st.p1[1], st.p1[2], st.p1[3]}));
-  const uint8_t XS_LDS* vb = lds + (2 + VST) * C::TILE;
+  const uint8_t XS_LDS* vb = lds + (C::STAGES + VST) * C::TILE;
   auto vread = [&](int f) {
     u32x2 r[4];
 #pragma unroll
@@ -259,6 +307,7 @@ __device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
   float mx = nxt.s[0][0];
   float neg_m = 0.0f, lsum = 0.0f;
   uint32_t w[4];
+  f32x4 pe[4];
   i32x8 vf[R];
 #pragma unroll
   for (int f = 0; f < LEAD; ++f) vf[f] = vread(f);
@@ -266,6 +315,7 @@ __device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
   for (int f = 0; f < NF; ++f) {
     if (f + LEAD < NF) vf[(f + LEAD) % R] = vread(f + LEAD);
     st.o[f] = mfma_fp8(vf[f % R], pf, st.o[f]);
+    if (!C::LSE && f == NF - 1) st.lt = mfma_fp8(ones_e4m3(), pf, st.lt);
     if (f < HALF) {
       constexpr int EPS = 32 / HALF;  // max over the 32 scores of the next block
 #pragma unroll
@@ -281,21 +331,27 @@ __device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
         if (__builtin_amdgcn_ballot_w64(need)) {
           const float a = need ? fast_exp2(st.m - mnew) : 1.0f;
           st.m = need ? mnew : st.m;
-          st.l *= a;
           st.alpha *= a;
+          if (C::LSE) st.l32 *= a;
           st.rescale = true;
         }
         neg_m = -st.m;
-        lsum = st.l;
+        lsum = st.l32;
       }
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (q * HALF / 4 == f - HALF) exp_quad<C>(nxt, 0, q, c, neg_m, lsum, w[q]);
+        if (f > HALF && q * HALF / 4 == f - 1 - HALF) w[q] = pack4(pe[q]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q * HALF / 4 == f - HALF) pe[q] = exp4<C>(nxt, 0, q, c, neg_m, lsum);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  st.l = lsum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q * HALF / 4 == NF - 1 - HALF) w[q] = pack4(pe[q]);
+  st.l32 = lsum;
   st.p0 = u32x4{w[0], w[1], w[2], w[3]};
   keep(st.p0);
 }
@@ -305,27 +361,23 @@ template <class C>
 __device__ __forceinline__ void exp_tile8(Fp8State<C>& st, const Scores8<C>& sc, int nt, float c,
                                           u32x4& out) {
   const float neg_m = -st.m;
-  float lsum = st.l;
+  float lsum = st.l32;
   uint32_t w[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) exp_quad<C>(sc, nt, q, c, neg_m, lsum, w[q]);
-  st.l = lsum;
+  for (int q = 0; q < 4; ++q) w[q] = pack4(exp4<C>(sc, nt, q, c, neg_m, lsum));
+  st.l32 = lsum;
   out = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// O^T = alpha O^T + V^T P^T of one block from V stage VST (tail, not pipelined).
-template <class C, int VST>
+// O^T = alpha O^T + V^T P^T (and the row sums) of the last block of a piece,
+// from the V stage at byte offset stage_off of the V region (not pipelined).
+template <class C>
 __device__ __forceinline__ void pv_only8(Fp8State<C>& st, const uint8_t XS_LDS* lds,
-                                         const LdsOffs8<C>& off) {
-  if (st.rescale) {
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) st.o[dt] *= st.alpha;
-    st.alpha = 1.0f;
-    st.rescale = false;
-  }
+                                         const LdsOffs8<C>& off, uint32_t stage_off) {
+  if (st.rescale) rescale_o8<C>(st);
   const i32x8 pf = __builtin_bit_cast(
       i32x8, (u32x8{st.p0[0], st.p0[1], st.p0[2], st.p0[3], st.p1[0], st.p1[1], st.p1[2], st.p1[3]}));
-  const uint8_t XS_LDS* vb = lds + (2 + VST) * C::TILE;
+  const uint8_t XS_LDS* vb = lds + C::STAGES * C::TILE + stage_off;
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) {
     u32x2 r[4];
@@ -334,11 +386,14 @@ __device__ __forceinline__ void pv_only8(Fp8State<C>& st, const uint8_t XS_LDS* 
     const i32x8 vf = __builtin_bit_cast(
         i32x8, (u32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]}));
     st.o[dt] = mfma_fp8(vf, pf, st.o[dt]);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (!C::LSE) st.lt = mfma_fp8(ones_e4m3(), pf, st.lt);
 }
 
-// Takes the next piece of the walk and issues its first loads (K and V of
-// block jb into stage 0, K of jb+1 into stage 1).
+// Takes the next piece of the walk and issues its first loads: K of blocks jb,
+// jb+1, jb+2 and V of blocks jb, jb+1 into ring stages 0, 1, 2 (stage of block
+// i = (i - jb) % 4).
 template <class C>
 __device__ __forceinline__ PieceAddr begin_piece8(ShareWalk& walk, const Sched& sch,
                                                   const AttnArgs& a, int nblk, uint32_t row_stride,
@@ -347,12 +402,18 @@ __device__ __forceinline__ PieceAddr begin_piece8(ShareWalk& walk, const Sched& 
   PieceAddr pa = next_piece<C::BM, C::ROWB, C::BN>(walk, sch, a, nblk, row_stride, slot);
   const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
   const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
+  uint8_t XS_LDS* const vlds = lds + C::STAGES * C::TILE;
   load_tile8<C>(kbase, row_stride, pa.jb * C::BN, pa.kcur.at(pa.jb), a.S, lds, koff, wave);
-  load_tile8<C>(vbase, row_stride, pa.jb * C::BN, pa.vcur.at(pa.jb), a.S, lds + 2 * C::TILE, voff,
-                wave);
-  if (pa.jb + 1 < pa.je)
+  load_tile8<C>(vbase, row_stride, pa.jb * C::BN, pa.vcur.at(pa.jb), a.S, vlds, voff, wave);
+  if (pa.jb + 1 < pa.je) {
     load_tile8<C>(kbase, row_stride, (pa.jb + 1) * C::BN, pa.kcur.at(pa.jb + 1), a.S,
                   lds + C::TILE, koff, wave);
+    load_tile8<C>(vbase, row_stride, (pa.jb + 1) * C::BN, pa.vcur.at(pa.jb + 1), a.S,
+                  vlds + C::TILE, voff, wave);
+  }
+  if (pa.jb + 2 < pa.je)
+    load_tile8<C>(kbase, row_stride, (pa.jb + 2) * C::BN, pa.kcur.at(pa.jb + 2), a.S,
+                  lds + 2 * C::TILE, koff, wave);
   return pa;
 }
 
@@ -378,10 +439,11 @@ __device__ __forceinline__ void load_q8(i32x8 (&qf)[C::KS], const AttnArgs& a, c
 template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a) {
   constexpr int BN = C::BN;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];
+  // K stages 0..3 | V stages 0..3
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGES * C::TILE];
   uint8_t XS_LDS* const lds = (uint8_t XS_LDS*)smem;
-  auto kbuf = [&](int i) { return lds + (i & 1) * C::TILE; };
-  auto vbuf = [&](int i) { return lds + (2 + (i & 1)) * C::TILE; };
+  auto kbuf = [&](int s) { return lds + s * C::TILE; };
+  auto vbuf = [&](int s) { return lds + (C::STAGES + s) * C::TILE; };
 
   const int S = a.S, H = a.H, T = a.T, B = a.B;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -416,7 +478,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
     const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
 
     st.m = -INFINITY;
-    st.l = 0.0f;
+    st.lt = f32x16{};
+    st.l32 = 0.0f;
     st.alpha = 1.0f;
     st.rescale = false;
 #pragma unroll
@@ -427,51 +490,82 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
 
     // prologue: score block jb, take its max, probabilities of its keys 0..31
     Scores8<C> sa, sb;
-    qk_block8<C>(sa, st, kbuf(jb), lane);
+    qk_block8<C>(sa, st, kbuf(0), lane);
     if (jb >= nfull) mask_tail8<C>(sa, jb * BN, S, lane);
     softmax_max8<C>(st, sa, c);
     exp_tile8<C>(st, sa, 0, c, st.p0);
 
-    // Steady state, two blocks per trip so the score buffers swap statically.
-    // Entering the trip for block i: its scores are in one buffer with their max
-    // taken and the probabilities of keys 0..31 in st.p0; K_{i+1} and V_i are
-    // loaded or in flight.  (jb is even: K_i and V_i live in stage i % 2.)
+    // K/V blocks stream through a four-stage LDS ring with one barrier per two
+    // blocks, as in the bf16 kernel: at the barrier before blocks i, i+1
+    // (i - jb even) the loads of K_{i+1}, K_{i+2}, V_i, V_{i+1} are complete
+    // and blocks i-2, i-1 are done, so K_{i+3}, K_{i+4}, V_{i+2}, V_{i+3} go
+    // into their stages.  Entering a step for block i: its scores are in one
+    // buffer with their max taken and the probabilities of keys 0..31 in st.p0.
+    auto ld_k = [&](int i, int stage) {
+      load_tile8<C>(kbase, row_stride, i * BN, pa.kcur.at(i), S, kbuf(stage), koff, wave);
+    };
+    auto ld_v = [&](int i, int stage) {
+      load_tile8<C>(vbase, row_stride, i * BN, pa.vcur.at(i), S, vbuf(stage), voff, wave);
+    };
     int j = jb;
-    for (; j + 2 < je; j += 2) {
+    for (; j + 4 < je; j += 4) {
       wait_vmcnt<0>();
       __syncthreads();
-      load_tile8<C>(kbase, row_stride, (j + 2) * BN, pa.kcur.at(j + 2), S, kbuf(0), koff, wave);
-      load_tile8<C>(vbase, row_stride, (j + 1) * BN, pa.vcur.at(j + 1), S, vbuf(1), voff, wave);
-      step_a8<C, 1>(sb, sa, st, lds, off, c);
+      ld_k(j + 3, 3);
+      ld_k(j + 4, 0);
+      ld_v(j + 2, 2);
+      ld_v(j + 3, 3);
+      step_a8<C, 1>(sb, sa, st, lds, off, c);  // block j
       if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
       step_b8<C, 0>(st, sb, lds, off, c);
+      step_a8<C, 2>(sa, sb, st, lds, off, c);  // block j+1
+      if (j + 2 >= nfull) mask_tail8<C>(sa, (j + 2) * BN, S, lane);
+      step_b8<C, 1>(st, sa, lds, off, c);
 
       wait_vmcnt<0>();
       __syncthreads();
-      if (j + 3 < je)
-        load_tile8<C>(kbase, row_stride, (j + 3) * BN, pa.kcur.at(j + 3), S, kbuf(1), koff, wave);
-      load_tile8<C>(vbase, row_stride, (j + 2) * BN, pa.vcur.at(j + 2), S, vbuf(0), voff, wave);
-      step_a8<C, 0>(sa, sb, st, lds, off, c);
-      if (j + 2 >= nfull) mask_tail8<C>(sa, (j + 2) * BN, S, lane);
-      step_b8<C, 1>(st, sa, lds, off, c);
+      if (j + 5 < je) ld_k(j + 5, 1);
+      if (j + 6 < je) ld_k(j + 6, 2);
+      ld_v(j + 4, 0);
+      if (j + 5 < je) ld_v(j + 5, 1);
+      step_a8<C, 3>(sb, sa, st, lds, off, c);  // block j+2
+      if (j + 3 >= nfull) mask_tail8<C>(sb, (j + 3) * BN, S, lane);
+      step_b8<C, 2>(st, sb, lds, off, c);
+      step_a8<C, 0>(sa, sb, st, lds, off, c);  // block j+3
+      if (j + 4 >= nfull) mask_tail8<C>(sa, (j + 4) * BN, S, lane);
+      step_b8<C, 3>(st, sa, lds, off, c);
     }
-    // the last one or two blocks (j is even; scores of block j in sa)
-    if (j + 1 < je) {
+    // the last one to four blocks j .. je-1 (stages 0..3, scores of block j in sa)
+    {
+      const int r = je - j;
       wait_vmcnt<0>();
       __syncthreads();
-      load_tile8<C>(vbase, row_stride, (j + 1) * BN, pa.vcur.at(j + 1), S, vbuf(1), voff, wave);
-      step_a8<C, 1>(sb, sa, st, lds, off, c);
-      if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
-      step_b8<C, 0>(st, sb, lds, off, c);
-      wait_vmcnt<0>();
-      __syncthreads();
-      exp_tile8<C>(st, sb, 1, c, st.p1);
-      pv_only8<C, 1>(st, lds, off);
-    } else {
-      wait_vmcnt<0>();  // V_j may have been issued by the last loop trip
-      __syncthreads();
-      exp_tile8<C>(st, sa, 1, c, st.p1);
-      pv_only8<C, 0>(st, lds, off);
+      if (r > 3) ld_k(j + 3, 3);
+      if (r > 2) ld_v(j + 2, 2);
+      if (r > 3) ld_v(j + 3, 3);
+      if (r > 1) {
+        step_a8<C, 1>(sb, sa, st, lds, off, c);  // block j
+        if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
+        step_b8<C, 0>(st, sb, lds, off, c);
+      }
+      if (r > 2) {
+        step_a8<C, 2>(sa, sb, st, lds, off, c);  // block j+1
+        if (j + 2 >= nfull) mask_tail8<C>(sa, (j + 2) * BN, S, lane);
+        step_b8<C, 1>(st, sa, lds, off, c);
+        wait_vmcnt<0>();
+        __syncthreads();
+      }
+      if (r > 3) {
+        step_a8<C, 3>(sb, sa, st, lds, off, c);  // block j+2
+        if (j + 3 >= nfull) mask_tail8<C>(sb, (j + 3) * BN, S, lane);
+        step_b8<C, 2>(st, sb, lds, off, c);
+      }
+      // the last block, j + r - 1: scores in sa when r is odd, keys 0..31 done
+      if (r & 1)
+        exp_tile8<C>(st, sa, 1, c, st.p1);
+      else
+        exp_tile8<C>(st, sb, 1, c, st.p1);
+      pv_only8<C>(st, lds, off, (uint32_t)(r - 1) * C::TILE);
     }
 
     // ---- next piece: request its first K/V blocks and its queries before
@@ -489,9 +583,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
     const int srow = m0 + wave * C::QW + (lane & 31);
     if (cur.whole) {
       // O * dv / l, rounded to bf16, stored into the destination slice
-      const float lrow = sum_halves(st.l);
+      const float lrow = row_sum(st);
       const float inv = a.o_scale / lrow;
-      if (a.lse && lane < 32 && srow < S) a.lse[(size_t)cur.bh * S + srow] = row_lse(st.m, lrow);
+      if (C::LSE && lane < 32 && srow < S) a.lse[(size_t)cur.bh * S + srow] = row_lse(st.m, lrow);
       if (srow < S) {
         const int p = srow / T;
         const int sp = srow - p * T;
@@ -509,7 +603,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
       }
     } else {
       // a tile cut between shares: fp32 partials into this share's slot
-      const float lsum = sum_halves(st.l);
+      const float lsum = row_sum(st);
       const int r = srow - m0;
       if (srow < S) {
         const size_t sr = (size_t)cur_slot * C::BM + r;
@@ -529,9 +623,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
   }
 }
 
-template <int D>
+template <int D, bool LSE>
 static hipError_t launch_d8(const AttnArgs& a, hipStream_t stream) {
-  using C = Fp8Cfg<D>;
+  using C = Fp8Cfg<D, LSE>;
   static_assert(C::BM == kBlockM && C::BN == kBlockN, "tile geometry");
   if (a.groups < 1) return hipErrorInvalidValue;
   AttnArgs args = a;
@@ -543,9 +637,9 @@ static hipError_t launch_d8(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream) {
   switch (a.D) {
     case 64:
-      return launch_d8<64>(a, stream);
+      return a.lse ? launch_d8<64, true>(a, stream) : launch_d8<64, false>(a, stream);
     case 128:
-      return launch_d8<128>(a, stream);
+      return a.lse ? launch_d8<128, true>(a, stream) : launch_d8<128, false>(a, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -319,10 +319,13 @@ def test_fp8_negative_scale(gpu):
 
 def test_fp8_peaked_softmax_within_rounding_bound(gpu):
     # At scale 0.25, D=64 a few keys dominate each row and the e4m3 rounding of P
-    # (unit roundoff 2^-4 for normal values, absolute 2^-10 below 2^-6) no longer
-    # averages out.  Bound per element: 2^-4 (1 + 2^-8) sum_j w_ij |v_j| for P,
-    # 2^-8 |O_i| for the bf16 output, and 2^-9 max|v| for weights in the
-    # subnormal range; the relative-L2 gate of the fp8 workloads still applies.
+    # (unit roundoff u = 2^-4 for normal values, absolute 2^-10 below 2^-6) no
+    # longer averages out.  O is normalised by the sum of the same quantised
+    # probabilities, p^_j = p_j (1 + d_j): O' - O = (sum_j w_j d_j v_j - d O) /
+    # (1 + d) with d = sum_j w_j d_j, so per element |O' - O| <= u / (1 - u)
+    # (sum_j w_ij |v_j| + |O_i|); plus 2^-8 |O_i| for the bf16 output and
+    # 2^-9 max|v| for weights in the subnormal range.  The relative-L2 gate of
+    # the fp8 workloads still applies.
     w = workloads.custom(2, 333, 2, 64, 3, dtype="fp8", index=4200)
     inp = workloads.make_inputs(w)
     ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], 3, 0.25, inp["descales"])
@@ -334,11 +337,30 @@ def test_fp8_peaked_softmax_within_rounding_bound(gpu):
     ref_abs = oracle.attention_packed(qf, kf, vabs * dv, 3, 0.25)
     got = f64(run(inp, 3, gpu, scale=0.25))
     vmax = float(vabs.max()) * dv
-    bound = 2.0 ** -4 * (1 + 2.0 ** -8) * ref_abs + 2.0 ** -8 * np.abs(ref) + 2.0 ** -9 * vmax
+    u = 2.0 ** -4
+    bound = u / (1 - u) * (ref_abs + np.abs(ref)) + 2.0 ** -8 * np.abs(ref) + 2.0 ** -9 * vmax
     worst = float((np.abs(got - ref) / bound).max())
     print(f"  fp8 scale=0.25 worst error / bound = {worst:.3f}", flush=True)
     assert worst <= 1.0
     assert gate(got, ref, "fp8")[1] <= TOL["fp8"][1]
+
+
+def test_fp8_constant_v_gives_constant_output(gpu):
+    # Without the log-sum-exp output O is normalised by the sum of the same
+    # quantised probabilities that weight V, so a constant V comes back exactly
+    # (1.5 * 0.5 = 0.75 is exact in bf16).  With it, O is normalised by the fp32
+    # sum of the unquantised probabilities, within the e4m3 rounding of P.
+    w = workloads.custom(2, 1000, 2, 128, 8, dtype="fp8", index=4300)
+    inp = workloads.make_inputs(w)
+    q, k, _ = to_gpu(inp, gpu)
+    v = torch.full_like(q, 1.5)
+    dq, dk, _ = inp["descales"]
+    _say("fp8 constant V")
+    out = xs.fwd_fp8(q, k, v, (dq, dk, 0.5), 8, inp["scale"])
+    out_l, _ = xs.fwd_fp8(q, k, v, (dq, dk, 0.5), 8, inp["scale"], lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 0.75)
+    assert float((out_l.float() - 0.75).abs().max()) <= 0.75 * 2.0 ** -4
 
 
 def test_fp8_canaries_and_full_write(gpu):
