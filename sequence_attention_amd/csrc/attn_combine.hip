@@ -43,16 +43,37 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const size_t first = 2 * (size_t)c_lo + (sch.start(c_lo) < u0 ? 1 : 0);
   auto slot_of = [&](int c) { return c == c_lo ? first : 2 * (size_t)c; };
 
-  float M = -INFINITY;
-  for (int c = c_lo; c <= c_hi; ++c) M = fmaxf(M, a.ws_ml[2 * (slot_of(c) * kBlockM + r)]);
-  float L = 0.0f;
+  // Pieces in groups of up to four: all loads of a group are issued before any
+  // is used (the merge is bound by memory latency, not bandwidth).  Each group
+  // is folded into the running (M, L, acc) with the online-softmax rescale,
+  // in key order.
+  float M = -INFINITY, L = 0.0f;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int c = c_lo; c <= c_hi; ++c) {
-    const size_t sr = slot_of(c) * kBlockM + r;
-    const f32x2 ml = *(const f32x2*)(a.ws_ml + 2 * sr);
-    const float w = fast_exp2(ml[0] - M);
-    L += w * ml[1];
-    acc += w * *(const f32x4*)(a.ws_o + sr * D + d0);
+  for (int c0 = c_lo; c0 <= c_hi; c0 += 4) {
+    f32x2 ml[4];
+    f32x4 o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = c0 + i <= c_hi ? c0 + i : c_hi;  // clamped: a repeated load, not used
+      const size_t sr = slot_of(c) * kBlockM + r;
+      ml[i] = *(const f32x2*)(a.ws_ml + 2 * sr);
+      o[i] = *(const f32x4*)(a.ws_o + sr * D + d0);
+    }
+    float Mg = M;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (c0 + i <= c_hi) Mg = fmaxf(Mg, ml[i][0]);
+    const float a0 = fast_exp2(M - Mg);  // 0 for the first group (M = -inf)
+    L *= a0;
+    acc *= a0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (c0 + i <= c_hi) {
+        const float w = fast_exp2(ml[i][0] - Mg);
+        L += w * ml[i][1];
+        acc += w * o[i];
+      }
+    M = Mg;
   }
   const float inv = a.o_scale / L;
   if (a.lse && d0 == 0) a.lse[(size_t)bh * a.S + srow] = row_lse(M, L);
