@@ -142,6 +142,42 @@ def test_lse_closed_forms(gpu):
     np.testing.assert_allclose(_f64(lse1), s.permute(0, 2, 1).numpy(), rtol=0, atol=2e-5)
 
 
+def test_score_accumulation_precision(gpu):
+    # With one key the row log-sum-exp is the score itself, so lse - scale * q.k
+    # (exact, fp64) is the error of the score MFMAs' dot product.  Pinned here
+    # because the log-sum-exp bars rest on it: the bf16 matrix core sums the
+    # exact products as fp32 does (D * 2^-24 of scale * sum_d |q_d k_d| is the
+    # fp32 bound; 2^-20 is checked), the e4m3 one much more coarsely (measured up
+    # to 2^-12.8; 2^-11 is checked).  One dominant product per dot (|q_0 k_0|
+    # about 999 times the rest) is the hard case for the e4m3 sum.
+    g = torch.Generator().manual_seed(3)
+    for dtype, eps in (("bf16", 2.0 ** -20), ("fp8", 2.0 ** -11)):
+        for mag in (1.0, 30.0):
+            B, H, D = 64, 8, 128
+            qf = torch.randn(B, 1, H, D, generator=g) * mag
+            kf = torch.randn(B, 1, H, D, generator=g) * mag
+            qf[..., 0] = mag
+            kf[..., 0] = 999.0
+            _say(f"score accumulation {dtype} magnitude {mag}")
+            if dtype == "fp8":
+                dq, dk = float(qf.abs().max()) / 448.0, float(kf.abs().max()) / 448.0
+                q8, k8 = (qf / dq).to(torch.float8_e4m3fn), (kf / dk).to(torch.float8_e4m3fn)
+                qe, ke = q8.to(torch.float64) * dq, k8.to(torch.float64) * dk
+                _, lse = xs.fwd_fp8(q8.to(gpu), k8.to(gpu), torch.ones_like(q8).to(gpu),
+                                    (dq, dk, 1.0), 1, 0.0883883476, lse=True)
+            else:
+                q, k = qf.to(torch.bfloat16), kf.to(torch.bfloat16)
+                qe, ke = q.to(torch.float64), k.to(torch.float64)
+                _, lse = xs.fwd(q.to(gpu), k.to(gpu), torch.ones_like(q).to(gpu), 1, 0.0883883476,
+                                lse=True)
+            torch.cuda.synchronize()
+            exact = ((qe * ke).sum(-1) * 0.0883883476).permute(0, 2, 1).numpy()  # [B][H][1]
+            absdot = ((qe * ke).abs().sum(-1) * 0.0883883476).permute(0, 2, 1).numpy()
+            rel = float((np.abs(_f64(lse) - exact) / absdot).max())
+            print(f"  max error / (scale sum|q k|) = 2^{np.log2(max(rel, 1e-30)):.1f}", flush=True)
+            assert rel <= eps
+
+
 # ------------------------------------------------------------------ chunk-layout inputs
 CHUNKED = [
     # (B, S, H, D, P, dtype): T = S/P a multiple of 64 whenever B > 1 and P > 1

@@ -258,6 +258,79 @@ def test_peaked_softmax_within_rounding_bound(gpu):
     assert gate(got, ref, "bf16")[1] <= 1e-2
 
 
+def _rising_scores(B, S, H, D, dtype, index):
+    """Inputs whose scores rise along the keys: q[..., 0] = 1 and k[:, j, :, 0] = j, so
+    with scale 1/sqrt(D) every 64-key block's max exceeds the previous one by about
+    64 * scale * log2(e) > 8 (log2 units) and the running max moves (and O, l are
+    rescaled) in nearly every block, including the ragged last one."""
+    w = workloads.custom(B, S, H, D, 1, dtype=dtype, index=index)
+    inp = workloads.make_inputs(w)
+    if dtype == "fp8":
+        dq, dk, dv = inp["descales"]
+        q = inp["q"].to(torch.float32) * dq
+        k = inp["k"].to(torch.float32) * dk
+        q[..., 0] = 1.0
+        k[..., 0] = torch.arange(S, dtype=torch.float32).view(1, S, 1)
+        dq, dk = float(q.abs().max()) / 448.0, float(k.abs().max()) / 448.0
+        inp["q"] = (q / dq).to(torch.float8_e4m3fn)
+        inp["k"] = (k / dk).to(torch.float8_e4m3fn)
+        inp["descales"] = (dq, dk, dv)
+    else:
+        inp["q"][..., 0] = 1.0
+        inp["k"][..., 0] = torch.arange(S, dtype=torch.float32).view(1, S, 1).to(torch.bfloat16)
+    return w, inp
+
+
+@pytest.mark.parametrize("dtype,B,S,H,D,P", [("bf16", 2, 1000, 2, 64, 4), ("bf16", 1, 777, 3, 128, 7),
+                                             ("fp8", 2, 1000, 2, 128, 8)])
+def test_running_max_moves_every_block(gpu, dtype, B, S, H, D, P):
+    # Rounding bound as in the peaked-softmax tests (a few keys dominate each
+    # row); with the log-sum-exp checked against the oracle's at the usual bar.
+    w, inp = _rising_scores(B, S, H, D, dtype, 4400 + S + D)
+    scale = inp["scale"]
+    _say(f"rising scores {dtype} B={B} S={S} H={H} D={D} P={P}")
+    ref, ref_l = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, scale, inp["descales"],
+                                         with_lse=True)
+    if dtype == "fp8":
+        dq, dk, dv = inp["descales"]
+        vabs = inp["v"].to(torch.float64).abs() * dv
+        qf, kf = inp["q"].to(torch.float64) * dq, inp["k"].to(torch.float64) * dk
+        ref_abs = oracle.attention_packed(qf, kf, vabs, P, scale)
+        u = 2.0 ** -4
+        bound = u / (1 - u) * (ref_abs + np.abs(ref)) + 2.0 ** -8 * np.abs(ref) \
+            + 2.0 ** -9 * float(vabs.max())
+        q, k, v = to_gpu(inp, gpu)
+        out = xs.fwd_fp8(q, k, v, inp["descales"], P, scale)
+        out_l, lse = xs.fwd_fp8(q, k, v, inp["descales"], P, scale, lse=True)
+    else:
+        ref_abs = oracle.attention_packed(inp["q"], inp["k"], inp["v"].abs(), P, scale)
+        u = 2.0 ** -8
+        bound = u * np.abs(ref) + u * (1 + u) * ref_abs + 1e-5
+        q, k, v = to_gpu(inp, gpu)
+        out = xs.fwd(q, k, v, P, scale)
+        out_l, lse = xs.fwd(q, k, v, P, scale, lse=True)
+    torch.cuda.synchronize()
+    for name, o in (("O", out), ("O with lse", out_l)):
+        got = f64(o)
+        worst = float((np.abs(got - ref) / bound).max())
+        print(f"  {name}: worst error / bound = {worst:.3f}", flush=True)
+        assert worst <= 1.0 and np.isfinite(got).all(), name
+    d = np.abs(f64(lse) - ref_l)
+    print(f"  lse max_abs={d.max():.3e}", flush=True)
+    # bf16: the 5e-3 bar of the log-sum-exp tests.  fp8: the e4m3 matrix core sums
+    # its products less precisely than fp32 (measured: up to 2^-12.8 of
+    # scale * sum_d |q_d k_d|, test_score_accumulation_precision), and the scores
+    # here reach 90: the bar adds 2^-11 scale * max_j sum_d |q_d k_jd| per row.
+    bar = 5e-3
+    if dtype == "fp8":
+        dq, dk, _ = inp["descales"]
+        qa = inp["q"].to(torch.float64).abs() * dq
+        ka = inp["k"].to(torch.float64).abs() * dk
+        sabs = torch.einsum("bqhd,bkhd->bhqk", qa, ka).amax(-1).numpy() * scale  # [B][H][S]
+        bar = 5e-3 + 2.0 ** -11 * sabs
+    assert (d <= bar).all()
+
+
 # ------------------------------------------------------------------ the gate rejects wrong answers
 def test_negative_controls_fail_the_gate(gpu):
     w = workloads.WORKLOADS["video"].with_(S=8192)  # same statistics, cheaper oracle
