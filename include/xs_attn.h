@@ -65,9 +65,13 @@ int xs_attn_fwd(const void *q, const void *k, const void *v, void *out_packed, i
                 int H_local, int D, int P, float scale, void *stream);
 
 /* The same operation over OCP fp8 e4m3 (e4m3fn) inputs with per-tensor fp32
- * descales: the value of element x is x8 * x_descale.  Accumulation is fp32
- * and the output is bf16 [P][B][S/P][H_local][D] as above.  Descales must be
- * finite. */
+ * descales: the value of element x is x8 * x_descale.  The e4m3 matrix cores
+ * accumulate into fp32, though a dot product's terms are not summed to full
+ * fp32 precision (measured: up to about 2^-12.8 of scale * sum_d |q_d k_d| when
+ * one product dominates); the probabilities enter the second contraction as
+ * e4m3, and O is normalised by the sum of those quantised probabilities (a
+ * constant V comes back exactly).  The output is bf16 [P][B][S/P][H_local][D]
+ * as above.  Descales must be finite. */
 int xs_attn_fwd_fp8(const void *q8, const void *k8, const void *v8, float q_descale,
                     float k_descale, float v_descale, void *out_packed, int B, int S, int H_local,
                     int D, int P, float scale, void *stream);
@@ -126,8 +130,10 @@ int xs_attn_fwd_fp8_ws(const void *q8, const void *k8, const void *v8, float q_d
  *              the quantity an online-softmax merge of partial attention needs
  *              ("Move the Query, Not the Cache", gist.science explainer, Methodik:
  *              the Route primitive).  It is the running max plus log of the row sum
- *              of the kernel's own softmax (the bf16-rounded probabilities for bf16,
- *              fp32 ones for fp8).
+ *              of the kernel's own softmax: the bf16-rounded probabilities for bf16;
+ *              for fp8 the unquantised fp32 ones, and then O too is normalised by
+ *              that fp32 sum (it differs from the call without lse within the
+ *              e4m3 rounding of P).
  * Every other argument, the workspace rules and the error behaviour are those of
  * xs_attn_fwd_ws / xs_attn_fwd_fp8_ws, which equal these calls with in_layout =
  * XS_LAYOUT_BSHD and lse = NULL. */
