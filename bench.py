@@ -191,7 +191,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no cross-GPU step in this build).", file=sys.stderr)
+              "(the path has no cross-GPU step).", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
