@@ -50,7 +50,7 @@ extern "C" {
                                    and S/P not a multiple of 64 */
 #define XS_ERR_ALIGN (-4)       /* a pointer is not 16-byte aligned */
 #define XS_ERR_LAUNCH (-5)      /* the HIP launch reported an error */
-#define XS_ERR_OVERLAP (-6)     /* out_packed overlaps q, k or v */
+#define XS_ERR_OVERLAP (-6)     /* out_packed, lse or the workspace overlaps another buffer */
 #define XS_ERR_WORKSPACE (-7)   /* workspace smaller than xs_attn_workspace_size() */
 /* (XS_ERR_UNSUPPORTED also when B*H_local*ceil(S/256) exceeds 2^31 - 1 query tiles.) */
 
@@ -95,7 +95,9 @@ int xs_attn_fwd_fp8(const void *q8, const void *k8, const void *v8, float q_desc
  *                    xs_attn_workspace_size(B, S, H_local, D) bytes; owned by the
  *                    caller, not retained after the call; its contents are
  *                    scratch (overwritten, never read before written).  Calls
- *                    that overlap in time must not share a workspace.
+ *                    that overlap in time must not share a workspace.  When the
+ *                    schedule cuts tiles, the workspace_size bytes it uses may
+ *                    not overlap q, k, v, out_packed or lse (XS_ERR_OVERLAP).
  *   workspace NULL   no tile is cut (identical to xs_attn_fwd).
  * Results differ from the uncut schedule only by rounding (pieces are merged in
  * key order, so they are deterministic); they do not depend on P.

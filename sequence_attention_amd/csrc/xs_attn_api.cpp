@@ -190,12 +190,22 @@ size_t workspace_bytes(const Plan& pl, int D) {
 }
 
 // Attaches the schedule and, when it cuts tiles, the workspace to validated
-// arguments.  Without a workspace the schedule never cuts.
-int attach_workspace(xs::AttnArgs* a, void* ws, size_t ws_bytes) {
+// arguments (inputs of in_elem_bytes per element).  Without a workspace the
+// schedule never cuts.
+int attach_workspace(xs::AttnArgs* a, void* ws, size_t ws_bytes, size_t in_elem_bytes) {
   if (ws != nullptr && ((uintptr_t)ws & 15u) != 0) return XS_ERR_ALIGN;
   const Plan pl = plan_for(a->B, a->S, a->H, a->D, ws != nullptr);
   const size_t need = workspace_bytes(pl, a->D);
   if (need > 0 && ws_bytes < need) return XS_ERR_WORKSPACE;
+  if (need > 0) {
+    // the partials must not land in an input or an output
+    const size_t n = (size_t)a->B * a->S * a->H * a->D;
+    const size_t in_bytes = n * in_elem_bytes;
+    if (overlaps(ws, need, a->q, in_bytes) || overlaps(ws, need, a->k, in_bytes) ||
+        overlaps(ws, need, a->v, in_bytes) || overlaps(ws, need, a->out, n * 2) ||
+        (a->lse && overlaps(ws, need, a->lse, (size_t)a->B * a->H * a->S * sizeof(float))))
+      return XS_ERR_OVERLAP;
+  }
   a->groups = pl.groups;
   a->npair = pl.npair;
   a->dp = pl.dp;
@@ -226,7 +236,7 @@ int xs_attn_fwd_ex(const void* q, const void* k, const void* v, int in_layout, v
   if (rc != XS_OK) return rc;
   rc = apply_layout_and_lse(&a, in_layout, lse, 2);
   if (rc != XS_OK) return rc;
-  rc = attach_workspace(&a, workspace, workspace_bytes);
+  rc = attach_workspace(&a, workspace, workspace_bytes, 2);
   if (rc != XS_OK) return rc;
   return launch(a, false, (hipStream_t)stream);
 }
@@ -262,7 +272,7 @@ int xs_attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v8, int in_la
   a.neg = qk < 0.0f;
   a.c = scores_factor(qk);
   a.o_scale = v_descale;
-  rc = attach_workspace(&a, workspace, workspace_bytes);
+  rc = attach_workspace(&a, workspace, workspace_bytes, 1);
   if (rc != XS_OK) return rc;
   return launch(a, true, (hipStream_t)stream);
 }
@@ -317,7 +327,7 @@ const char* xs_attn_strerror(int status) {
     case XS_ERR_LAUNCH:
       return "the HIP kernel launch failed";
     case XS_ERR_OVERLAP:
-      return "out_packed overlaps q, k or v";
+      return "buffers overlap: out_packed, lse or the workspace shares memory with another buffer";
     case XS_ERR_WORKSPACE:
       return "workspace smaller than xs_attn_workspace_size()";
     default:

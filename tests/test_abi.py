@@ -164,6 +164,11 @@ def test_workspace_errors_before_any_launch():
     assert _fwd_ws(W + 8, need) == XS_ERR_ALIGN
     assert _fwd_ws(W, need - 16) == XS_ERR_WORKSPACE
     assert _fwd_ws(W, need, D=96) == XS_ERR_UNSUPPORTED
+    # the partials may not land in an input or the output
+    nbytes = 1 * 4608 * 3 * 128 * 2
+    assert _fwd_ws(O + 16, need) == XS_ERR_OVERLAP
+    assert _fwd_ws(Q - need + 16, need) == XS_ERR_OVERLAP      # runs into q
+    assert _fwd_ws(V + nbytes - 16, need) == XS_ERR_OVERLAP    # starts inside v
 
 
 def _fwd_ex(**kw):
