@@ -74,10 +74,6 @@ struct Bf16Cfg {
   static_assert(LOADS % NW == 0 && LOADS >= NW, "tile loads must split evenly over waves");
 };
 
-#ifndef XS_VSWZ
-#define XS_VSWZ 1
-#endif
-
 // XOR swizzle of the 16-byte chunk index of V row `row`.  A ds_read_b64_tr_b16
 // of a V^T fragment touches 8 rows x 4 chunks and is served one half-wave at a
 // time (4 rows x 4 chunks = 256 bytes): XOR-ing the chunk with 4*(row%4) (D=128,
@@ -85,12 +81,8 @@ struct Bf16Cfg {
 // puts the 16 chunks of each half-wave on 16 different bank groups.
 template <class C>
 __device__ __forceinline__ int vswz(int row) {
-#if XS_VSWZ == 0
-  return (2 * row) & (C::CH - 1);
-#else
   constexpr int RPL = 256 / C::ROWB;  // rows per 256-byte bank line
   return 4 * ((row / RPL) & (C::CH / 4 - 1));
-#endif
 }
 
 // Per-lane byte offsets (relative to the block's first key row) of the
