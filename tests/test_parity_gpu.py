@@ -121,6 +121,31 @@ def test_full_size_workload_sampled_rows(gpu, name, nrows):
     _sampled_parity(gpu, name, nrows)
 
 
+@pytest.mark.parametrize("B,S,H,D,P,dtype,nrows", [
+    (1, 262144, 1, 128, 8, "bf16", 32),   # twice the long share's sequence, one head
+    (8, 2048, 2, 64, 8, "bf16", 64),      # many batches: the relayout interleaves 8 of them
+    (4, 65536, 1, 128, 16, "fp8", 32),
+])
+def test_large_shapes_sampled_rows(gpu, B, S, H, D, P, dtype, nrows):
+    w = workloads.custom(B, S, H, D, P, dtype=dtype, index=7000 + B + H)
+    inp = workloads.make_inputs(w)
+    for split in ("auto", None):
+        _say(f"large B={B} S={S} H={H} D={D} P={P} {dtype} split={split}")
+        q, k, v = to_gpu(inp, gpu)
+        if dtype == "fp8":
+            out = xs.fwd_fp8(q, k, v, inp["descales"], P, inp["scale"], workspace=split)
+        else:
+            out = xs.fwd(q, k, v, P, inp["scale"], workspace=split)
+        torch.cuda.synchronize()
+        rows = workloads.sample_rows(w, nrows)
+        ref = oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, inp["scale"],
+                                    inp["descales"])
+        o = xs.unpack(out, S)
+        idx = torch.as_tensor(rows, device=out.device)
+        assert_gate(f64(o[idx[:, 0], idx[:, 1], idx[:, 2]]), ref, dtype, f"split={split}")
+        assert torch.isfinite(out.float()).all()
+
+
 def test_image_workload_every_element(gpu):
     # 4608 x 3 rows of 4608 keys: affordable for the oracle on the host
     w = workloads.WORKLOADS["image"]
