@@ -12,6 +12,7 @@ answers.  Each pin is chosen so a plausible mistake in the oracle fails it:
   pack layout                        -> hand-derived golden layouts, numpy split/stack
   log-sum-exp: dropped max / log     -> golden values, score-shift invariance, torch.logsumexp
   chunk-layout inputs (index math)   -> numpy reshape/transpose of [B][S][H][D] inputs
+  anything in the core formula       -> Python-loop brute force (S <= 64), rows sum to 1
 """
 import json
 import math
@@ -194,6 +195,45 @@ def test_query_row_permutation_permutes_output_rows():
     a = _unpacked(q, k, v, 0.25)
     b = _unpacked(q[:, perm], k, v, 0.25)
     np.testing.assert_array_equal(a[:, perm.numpy()], b)
+
+
+def _brute_force(q, k, v, scale):
+    """softmax(scale q k^T) v written out with Python loops and math.exp."""
+    B, S, H, D = q.shape
+    q, k, v = q.tolist(), k.tolist(), v.tolist()
+    out = [[[[0.0] * D for _ in range(H)] for _ in range(S)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            for i in range(S):
+                s = [scale * sum(q[b][i][h][d] * k[b][j][h][d] for d in range(D)) for j in range(S)]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                tot = sum(e)
+                for d in range(D):
+                    out[b][i][h][d] = sum(e[j] * v[b][j][h][d] for j in range(S)) / tot
+    return np.array(out)
+
+
+@pytest.mark.parametrize("S", [1, 5, 33, 64])
+def test_brute_force_small_sequences(S):
+    B, H, D = 2, 2, 16
+    q, k, v = _rand((B, S, H, D), 40 + S, 1.5), _rand((B, S, H, D), 41 + S), _rand((B, S, H, D), 42 + S)
+    np.testing.assert_allclose(_unpacked(q, k, v, 0.4), _brute_force(q, k, v, 0.4), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("S", [3, 64])
+def test_softmax_rows_sum_to_one(S):
+    # with V the identity (value row j = e_j) O is the weight matrix itself: each
+    # row must be a probability vector equal to the brute-force softmax row
+    B, H, D = 1, 2, 64
+    q, k = _rand((B, S, H, D), 50 + S), _rand((B, S, H, D), 51 + S)
+    v = torch.zeros((B, S, H, D), dtype=torch.float64)
+    for j in range(S):
+        v[:, j, :, j] = 1.0
+    w = _unpacked(q, k, v, 0.3)
+    np.testing.assert_allclose(w[..., :S].sum(-1), 1.0, rtol=0, atol=1e-14)
+    assert (w[..., :S] > 0).all() and (w[..., S:] == 0).all()
+    np.testing.assert_allclose(w, _brute_force(q, k, v, 0.3), rtol=0, atol=1e-14)
 
 
 @pytest.mark.parametrize("B,S,H,D", [(1, 1, 1, 8), (2, 17, 3, 64), (1, 64, 2, 128), (2, 130, 1, 32)])
