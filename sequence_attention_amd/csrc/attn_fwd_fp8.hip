@@ -215,6 +215,17 @@ __device__ __forceinline__ LdsOffs8<C> lds_offsets8(int lane) {
   return o;
 }
 
+// Four fp32 values -> four OCP e4m3 bytes (round to nearest even), first value
+// in the low byte.  Inputs must stay below 464 (larger values become NaN).  The
+// first conversion writes the low half and keeps the high half of its `old`
+// operand, which the second conversion overwrites: any register will do as
+// `old`, so a's own bits are passed and no zeroed register is needed.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 // The probabilities of scores 4q..4q+3 of 32-key tile nt in two halves, a
 // micro-step apart, so the conversion never waits on the transcendental
 // unit's latency: exp4 computes p = 2^(s c - m), pack4 rounds them to four
@@ -234,7 +245,7 @@ __device__ __forceinline__ f32x4 exp4(const Scores8<C>& sc, int nt, int q, float
 }
 
 __device__ __forceinline__ uint32_t pack4(f32x4 p) {
-  uint32_t pk = pack_fp8x4(p[0], p[1], p[2], p[3]);
+  uint32_t pk = pack_e4m3x4(p[0], p[1], p[2], p[3]);
   pin(pk);
   return pk;
 }
@@ -287,7 +298,8 @@ __device__ __forceinline__ void step_a8(Scores8<C>& nxt, const Scores8<C>& cur, 
 // block (first half), then the probabilities of its keys 0..31 (second half).
 template <class C, int VST>
 __device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
-                                        const uint8_t XS_LDS* lds, const LdsOffs8<C>& off, float c) {
+                                        const uint8_t XS_LDS* lds, const LdsOffs8<C>& off, float c,
+                                        const i32x8& ones) {
   constexpr int DT = C::DT, ROWB = C::ROWB;
   constexpr int NF = DT;
   constexpr int HALF = NF / 2;
@@ -315,7 +327,7 @@ __device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
   for (int f = 0; f < NF; ++f) {
     if (f + LEAD < NF) vf[(f + LEAD) % R] = vread(f + LEAD);
     st.o[f] = mfma_fp8(vf[f % R], pf, st.o[f]);
-    if (!C::LSE && f == NF - 1) st.lt = mfma_fp8(ones_e4m3(), pf, st.lt);
+    if (!C::LSE && f == NF - 1) st.lt = mfma_fp8(ones, pf, st.lt);
     if (f < HALF) {
       constexpr int EPS = 32 / HALF;  // max over the 32 scores of the next block
 #pragma unroll
@@ -373,7 +385,8 @@ __device__ __forceinline__ void exp_tile8(Fp8State<C>& st, const Scores8<C>& sc,
 // from the V stage at byte offset stage_off of the V region (not pipelined).
 template <class C>
 __device__ __forceinline__ void pv_only8(Fp8State<C>& st, const uint8_t XS_LDS* lds,
-                                         const LdsOffs8<C>& off, uint32_t stage_off) {
+                                         const LdsOffs8<C>& off, uint32_t stage_off,
+                                         const i32x8& ones) {
   if (st.rescale) rescale_o8<C>(st);
   const i32x8 pf = __builtin_bit_cast(
       i32x8, (u32x8{st.p0[0], st.p0[1], st.p0[2], st.p0[3], st.p1[0], st.p1[1], st.p1[2], st.p1[3]}));
@@ -388,7 +401,7 @@ __device__ __forceinline__ void pv_only8(Fp8State<C>& st, const uint8_t XS_LDS* 
     st.o[dt] = mfma_fp8(vf, pf, st.o[dt]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (!C::LSE) st.lt = mfma_fp8(ones_e4m3(), pf, st.lt);
+  if (!C::LSE) st.lt = mfma_fp8(ones, pf, st.lt);
 }
 
 // Takes the next piece of the walk and issues its first loads: K of blocks jb,
@@ -462,6 +475,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
   const uint32_t qflip = a.neg ? 0x80808080u : 0u;
   const float c = a.c;
   const LdsOffs8<C> off = lds_offsets8<C>(lane);
+  // the row-sum MFMA's constant operand, held in registers for the whole kernel
+  // (opaque, so the compiler does not rebuild it before every use)
+  i32x8 ones = ones_e4m3();
+  asm volatile("" : "+v"(ones));
 
   const Sched sch{a.units, a.groups, a.npair, a.dp};
   ShareWalk walk;
@@ -517,10 +534,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
       ld_v(j + 3, 3);
       step_a8<C, 1>(sb, sa, st, lds, off, c);  // block j
       if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
-      step_b8<C, 0>(st, sb, lds, off, c);
+      step_b8<C, 0>(st, sb, lds, off, c, ones);
       step_a8<C, 2>(sa, sb, st, lds, off, c);  // block j+1
       if (j + 2 >= nfull) mask_tail8<C>(sa, (j + 2) * BN, S, lane);
-      step_b8<C, 1>(st, sa, lds, off, c);
+      step_b8<C, 1>(st, sa, lds, off, c, ones);
 
       wait_vmcnt<0>();
       __syncthreads();
@@ -530,10 +547,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
       if (j + 5 < je) ld_v(j + 5, 1);
       step_a8<C, 3>(sb, sa, st, lds, off, c);  // block j+2
       if (j + 3 >= nfull) mask_tail8<C>(sb, (j + 3) * BN, S, lane);
-      step_b8<C, 2>(st, sb, lds, off, c);
+      step_b8<C, 2>(st, sb, lds, off, c, ones);
       step_a8<C, 0>(sa, sb, st, lds, off, c);  // block j+3
       if (j + 4 >= nfull) mask_tail8<C>(sa, (j + 4) * BN, S, lane);
-      step_b8<C, 3>(st, sa, lds, off, c);
+      step_b8<C, 3>(st, sa, lds, off, c, ones);
     }
     // the last one to four blocks j .. je-1 (stages 0..3, scores of block j in sa)
     {
@@ -546,26 +563,26 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
       if (r > 1) {
         step_a8<C, 1>(sb, sa, st, lds, off, c);  // block j
         if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
-        step_b8<C, 0>(st, sb, lds, off, c);
+        step_b8<C, 0>(st, sb, lds, off, c, ones);
       }
       if (r > 2) {
         step_a8<C, 2>(sa, sb, st, lds, off, c);  // block j+1
         if (j + 2 >= nfull) mask_tail8<C>(sa, (j + 2) * BN, S, lane);
-        step_b8<C, 1>(st, sa, lds, off, c);
+        step_b8<C, 1>(st, sa, lds, off, c, ones);
         wait_vmcnt<0>();
         __syncthreads();
       }
       if (r > 3) {
         step_a8<C, 3>(sb, sa, st, lds, off, c);  // block j+2
         if (j + 3 >= nfull) mask_tail8<C>(sb, (j + 3) * BN, S, lane);
-        step_b8<C, 2>(st, sb, lds, off, c);
+        step_b8<C, 2>(st, sb, lds, off, c, ones);
       }
       // the last block, j + r - 1: scores in sa when r is odd, keys 0..31 done
       if (r & 1)
         exp_tile8<C>(st, sa, 1, c, st.p1);
       else
         exp_tile8<C>(st, sb, 1, c, st.p1);
-      pv_only8<C>(st, lds, off, (uint32_t)(r - 1) * C::TILE);
+      pv_only8<C>(st, lds, off, (uint32_t)(r - 1) * C::TILE, ones);
     }
 
     // ---- next piece: request its first K/V blocks and its queries before
