@@ -54,6 +54,46 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def resource_usage() -> str:
+    """Markdown table of every kernel's register, LDS and spill usage, from the
+    compiler's kernel-resource-usage remarks (same flags as the build)."""
+    import re
+
+    rows = []
+    for src in SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
+               "-o", os.devnull]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        cur = None
+        for line in r.stderr.splitlines():
+            m = re.search(r"remark: (?:\s*)([A-Za-z][^:\[]*?)(?: \[[^\]]*\])?: (.*?) \[-Rpass", line)
+            if not m:
+                continue
+            key, val = m.group(1).strip(), m.group(2).strip()
+            if key == "Function Name":
+                cur = {"kernel": val, "source": src}
+                rows.append(cur)
+            elif cur is not None:
+                cur[key] = val
+    demangle = subprocess.run(["c++filt"], input="\n".join(r["kernel"] for r in rows),
+                              capture_output=True, text=True).stdout.splitlines()
+    cols = [("VGPRs", "VGPRs"), ("AGPRs", "AGPRs"), ("TotalSGPRs", "SGPRs"),
+            ("VGPRs Spill", "VGPR spills"), ("ScratchSize", "scratch B/lane"),
+            ("LDS Size", "LDS B/block"), ("Occupancy", "waves/SIMD")]
+    out = ["| kernel | " + " | ".join(c[1] for c in cols) + " |",
+           "|---|" + "---|" * len(cols)]
+    for r, name in zip(rows, demangle):
+        out.append(f"| `{name}` | " + " | ".join(r.get(c[0], "") for c in cols) + " |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--resources" in sys.argv:
+        print(resource_usage())
+    else:
+        build(verbose=True)
     sys.exit(0)
