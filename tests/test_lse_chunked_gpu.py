@@ -181,6 +181,34 @@ def test_score_accumulation_precision(gpu):
             assert rel <= eps
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_lse_and_workspace_stay_in_bounds(gpu, dtype):
+    # lse is written on every row and nowhere else; the kernels touch only the
+    # workspace_size bytes of a larger workspace
+    B, S, H, D, P = 1, 4608, 3, 128, 8          # the image share: a cut schedule
+    w = workloads.custom(B, S, H, D, P, dtype=dtype, index=3700)
+    inp = workloads.make_inputs(w)
+    q, k, v = [inp[n].to(gpu) for n in "qkv"]
+    nl, pad = B * H * S, 1024
+    lbig = torch.full((nl + 2 * pad,), float("nan"), dtype=torch.float32, device=gpu)
+    lbig[:pad] = 5.0
+    lbig[pad + nl:] = -9.0
+    lse = lbig[pad:pad + nl].view(B, H, S)
+    need = xs.workspace_size(B, S, H, D)
+    assert need > 0
+    wbig = torch.full((need + 2 * 4096,), 0xA5, dtype=torch.uint8, device=gpu)
+    ws = wbig[4096:4096 + need]
+    _say(f"bounds {dtype}: lse {nl} floats, workspace {need} bytes")
+    if dtype == "fp8":
+        xs.fwd_fp8(q, k, v, inp["descales"], P, inp["scale"], workspace=ws, lse=lse)
+    else:
+        xs.fwd(q, k, v, P, inp["scale"], workspace=ws, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(lse).any()
+    assert torch.all(lbig[:pad] == 5.0) and torch.all(lbig[pad + nl:] == -9.0)
+    assert torch.all(wbig[:4096] == 0xA5) and torch.all(wbig[4096 + need:] == 0xA5)
+
+
 # ------------------------------------------------------------------ chunk-layout inputs
 CHUNKED = [
     # (B, S, H, D, P, dtype): T = S/P a multiple of 64 whenever B > 1 and P > 1
