@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   }
   const float inv = a.o_scale / L;
   if (a.lse && d0 == 0) a.lse[(size_t)bh * a.S + srow] = row_lse(M, L);
-  const int S = a.S, H = a.H, T = a.T;
+  const int H = a.H, T = a.T;
   const int h = bh % H, b = bh / H;
   const int p = srow / T;
   const int sp = srow - p * T;
