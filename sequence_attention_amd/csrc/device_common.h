@@ -75,13 +75,14 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
 // wait_vmcnt + a workgroup barrier before the tile is read.  The instruction
 // has no VGPR result, and its address VGPR is consumed at issue.
 __device__ __forceinline__ void load_lds_b128(u32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
+  // M0 holds the LDS destination base; the compiler writes it (the "{m0}"
+  // operand), the s_nop covers the M0-write to LDS-DMA distance.
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %0, %1, 0 offen lds"
       :
-      : "v"(voff), "s"(rsrc), "s"(lds_addr)
-      : "memory", "m0");
+      : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+      : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t XS_LDS* p) {
