@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--in-layout", default="bshd", choices=["bshd", "chunked"],
+                    help="input layout: [B][S][H][D] or the pre-attention All-to-All chunk layout "
+                         "[P][B][S/P][H][D] (converted once, before timing)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step (the attention kernel and, when the plan splits, the "
                          "merge kernel) in a HIP graph and replay it per step: removes the host "
@@ -213,6 +216,8 @@ def main():
     dev = torch.device("cuda:0")
     inp = workloads.make_inputs(w)
     q, k, v = (inp[n].to(dev) for n in "qkv")
+    if args.in_layout == "chunked":
+        q, k, v = (xs.chunk(t, w.P) for t in (q, k, v))
     out = torch.empty((w.P, w.B, w.S // w.P, w.H, w.D), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
     # split-key workspace (fp32 partials), allocated once outside the timed region
@@ -223,9 +228,10 @@ def main():
     def step():
         if w.dtype == "fp8":
             xs.fwd_fp8(q, k, v, inp["descales"], w.P, inp["scale"], out=out, stream=stream,
-                       workspace=ws)
+                       workspace=ws, in_layout=args.in_layout)
         else:
-            xs.fwd(q, k, v, w.P, inp["scale"], out=out, stream=stream, workspace=ws)
+            xs.fwd(q, k, v, w.P, inp["scale"], out=out, stream=stream, workspace=ws,
+                   in_layout=args.in_layout)
 
     for _ in range(args.warmup):
         step()
@@ -239,9 +245,11 @@ def main():
         with torch.cuda.stream(side):
             with torch.cuda.graph(graph, stream=side):
                 if w.dtype == "fp8":
-                    xs.fwd_fp8(q, k, v, inp["descales"], w.P, inp["scale"], out=out, workspace=ws)
+                    xs.fwd_fp8(q, k, v, inp["descales"], w.P, inp["scale"], out=out, workspace=ws,
+                               in_layout=args.in_layout)
                 else:
-                    xs.fwd(q, k, v, w.P, inp["scale"], out=out, workspace=ws)
+                    xs.fwd(q, k, v, w.P, inp["scale"], out=out, workspace=ws,
+                           in_layout=args.in_layout)
         torch.cuda.synchronize()
         step = lambda: graph.replay()  # noqa: E731
         for _ in range(3):
@@ -301,7 +309,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "S": w.S, "H_local": w.H, "D": w.D, "P": w.P,
                    "causal": False, "key_splits": nsplit, "workspace_bytes": ws_bytes,
                    "caches": "evicted before every call (--cold)" if args.cold else "warm",
-                   "launch": "hip graph replay" if args.graph else "direct"},
+                   "launch": "hip graph replay" if args.graph else "direct",
+                   "in_layout": args.in_layout},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "pct_of_bf16_peak": round(100.0 * value / PEAK_TFLOPS["bf16"], 2),
         "launch_ms": {"mean": round(float(launch_ms.mean()), 4), "min": round(float(launch_ms.min()), 4),
