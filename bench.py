@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--epilogue-overhead", action="store_true",
                     help="time the fused destination-ordered epilogue against a plain [B][S][H][D] "
                          "epilogue and against attention followed by a separate relayout")
+    ap.add_argument("--torch-sdpa", action="store_true",
+                    help="context: time torch's own fused attention (scaled_dot_product_attention, "
+                         "flash backend only) on the same inputs next to this library's call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -190,6 +193,86 @@ def epilogue_overhead(args):
                       "warmup": args.warmup, "results": results}), flush=True)
 
 
+def torch_sdpa(args):
+    """Context, not part of the path: torch's own fused attention kernel
+    (scaled_dot_product_attention restricted to its flash backend, so it raises
+    instead of falling back to the unfused math path) against this library's
+    call, on the same resident bf16 inputs, interleaved per call (medians).
+    Torch writes [B][S][H][D]; for B = 1 that is byte-identical to the P-way
+    destination-ordered buffer, for B > 1 a separate relayout copy follows and
+    is timed with it.  The two outputs are compared element by element."""
+    import sequence_attention_amd as xs
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sdpa = torch.nn.functional.scaled_dot_product_attention
+    cases = [workloads.WORKLOADS[n] for n in ("image", "video", "long")]
+    cases.append(workloads.custom(2, 32768, 4, 128, 8, index=4, name="video_b2"))
+    results = []
+    for w in cases:
+        inp = workloads.make_inputs(w)
+        q, k, v = (inp[n].to(dev) for n in "qkv")
+        qt, kt, vt = (t.transpose(1, 2) for t in (q, k, v))  # [B][H][S][D] views, no copy
+        ws_bytes = xs.workspace_size(w.B, w.S, w.H, w.D)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+        out = torch.empty((w.P, w.B, w.S // w.P, w.H, w.D), dtype=torch.bfloat16, device=dev)
+        ref = torch.empty_like(out)
+        T = w.S // w.P
+
+        def run_xs():
+            xs.fwd(q, k, v, w.P, inp["scale"], out=out, stream=stream, workspace=ws)
+
+        def run_torch():
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                o = sdpa(qt, kt, vt, scale=inp["scale"])
+            if w.B > 1:  # [B][S][H][D] -> [P][B][S/P][H][D]
+                ref.copy_(o.transpose(1, 2).view(w.B, w.P, T, w.H, w.D).permute(1, 0, 2, 3, 4))
+            return o
+
+        fns = (("xs", run_xs), ("torch", run_torch))
+        for _ in range(3):
+            for _, fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _, fn in fns:
+            fn()
+        torch.cuda.synchronize()
+        # about 3 s of timed calls per workload, at most --steps
+        steps = int(min(args.steps, max(5, 3.0 / (time.perf_counter() - t0))))
+        for _ in range(min(args.warmup, steps)):
+            for _, fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        samples = {name: [] for name, _ in fns}
+        for _ in range(steps):
+            for name, fn in fns:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                samples[name].append(e0.elapsed_time(e1))
+        o = run_torch()
+        run_xs()
+        torch.cuda.synchronize()
+        if w.B == 1:
+            assert o.transpose(1, 2).is_contiguous(), "torch output is not [B][S][H][D]"
+            ref.view(-1).copy_(o.transpose(1, 2).reshape(-1))
+        t = {name: float(np.median(s)) for name, s in samples.items()}
+        results.append({"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D, "P": w.P,
+                        "steps": steps, "xs_ms": round(t["xs"], 4), "torch_ms": round(t["torch"], 4),
+                        "xs_tflops": round(w.flops / t["xs"] / 1e9, 1),
+                        "torch_tflops": round(w.flops / t["torch"] / 1e9, 1),
+                        "torch_includes_relayout": w.B > 1,
+                        "speedup": round(t["torch"] / t["xs"], 3),
+                        "max_abs_diff": float((out.float() - ref.float()).abs().max())})
+    print(json.dumps({"metric": "torch_sdpa_comparison", "n_gpus": 1, "torch": torch.__version__,
+                      "backend": "flash (scaled_dot_product_attention)", "results": results}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -201,6 +284,9 @@ def main():
         return
     if args.epilogue_overhead:
         epilogue_overhead(args)
+        return
+    if args.torch_sdpa:
+        torch_sdpa(args)
         return
     if args.burst_gap:
         from sequence_attention_amd import burst_gap
