@@ -132,10 +132,11 @@ int xs_attn_fwd_fp8_ws(const void *q8, const void *k8, const void *v8, float q_d
  *              the quantity an online-softmax merge of partial attention needs
  *              ("Move the Query, Not the Cache", gist.science explainer, Methodik:
  *              the Route primitive).  It is the running max plus log of the row sum
- *              of the kernel's own softmax: the bf16-rounded probabilities for bf16;
- *              for fp8 the unquantised fp32 ones, and then O too is normalised by
- *              that fp32 sum (it differs from the call without lse within the
- *              e4m3 rounding of P).
+ *              of the kernel's own softmax, taken over the fp32 probabilities
+ *              before their rounding to bf16 / e4m3.  For fp8, O is then
+ *              normalised by that fp32 sum too (it differs from the call without
+ *              lse within the e4m3 rounding of P); for bf16, O is the same with
+ *              or without lse.
  * Every other argument, the workspace rules and the error behaviour are those of
  * xs_attn_fwd_ws / xs_attn_fwd_fp8_ws, which equal these calls with in_layout =
  * XS_LAYOUT_BSHD and lse = NULL. */

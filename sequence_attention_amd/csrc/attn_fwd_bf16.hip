@@ -32,7 +32,8 @@
 //  * Online softmax in base 2: p = 2^(s*c - m), c = scale*log2(e) folded into
 //    one FMA per score.  The running max is moved only when a block's max
 //    exceeds it by more than 2^TAU (p <= 2^TAU), so rescaling O is a rare
-//    wave-uniform branch.  The row sum adds the bf16-rounded p that enter P V.
+//    wave-uniform branch.  The row sum adds the fp32 p before their rounding
+//    to bf16 (plain adds: the vector ALU is the scarce unit here).
 //  * Epilogue: O/l rounded to bf16 and stored per query row at its
 //    destination-slice offset (p = s / T, s' = s - p*T).  Tile shapes and the
 //    reduction order never depend on P; only the store address does.
@@ -217,7 +218,6 @@ __device__ __forceinline__ void softmax_max(Bf16State<C>& st, const Scores<C>& s
 template <class C>
 __device__ __forceinline__ void softmax_exp(Bf16State<C>& st, const Scores<C>& sc, float c) {
   constexpr int QT = C::QT, NT = C::NT;
-  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float neg_m = -st.m[qt];
@@ -232,7 +232,8 @@ __device__ __forceinline__ void softmax_exp(Bf16State<C>& st, const Scores<C>& s
           const float p0 = fast_exp2(__builtin_fmaf(sc.s[nt][qt][8 * h + 2 * i], c, neg_m));
           const float p1 = fast_exp2(__builtin_fmaf(sc.s[nt][qt][8 * h + 2 * i + 1], c, neg_m));
           w[i] = pack_bf16(p0, p1);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]), ones, lsum, false);
+          lsum += p0;
+          lsum += p1;
         }
         st.pb[qt][2 * nt + h] = u32x4{w[0], w[1], w[2], w[3]};
       }
@@ -284,8 +285,8 @@ __device__ __forceinline__ LdsOffs<C> lds_offsets(int lane) {
 // the conversion never waits on the transcendental unit's latency:
 //  exp_pair2: p = 2^(s c - m) of pair idx (0 .. 8 NT - 1: registers 2(idx%8),
 //             2(idx%8)+1 of 32-key tile idx/8) of query sub-tile qt;
-//  pack_sum:  the pair rounded to bf16 (word idx%4 of P^T fragment idx/4) and
-//             added to the row sum.
+//  pack_sum:  the pair rounded to bf16 (word idx%4 of P^T fragment idx/4);
+//             its fp32 values added to the row sum.
 // Both are pinned to the micro-step they are issued in.
 template <class C>
 __device__ __forceinline__ f32x2 exp_pair2(const Scores<C>& cur, int qt, int idx, float c,
@@ -299,9 +300,9 @@ __device__ __forceinline__ f32x2 exp_pair2(const Scores<C>& cur, int qt, int idx
 }
 
 __device__ __forceinline__ uint32_t pack_sum(f32x2 p, float& lsum) {
-  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
   uint32_t pk = pack_bf16(p[0], p[1]);
-  lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, lsum, false);
+  lsum += p[0];
+  lsum += p[1];
   pin(pk);
   pin(lsum);
   return pk;
