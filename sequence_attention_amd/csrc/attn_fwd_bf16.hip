@@ -24,8 +24,8 @@
 //    V rows are swizzled for ds_read_b64_tr_b16, which delivers V^T fragments
 //    directly.
 //  * Software pipeline inside the wave:
-//      step 1: QK^T of block j+1 (MFMA)  ||  exp/sum/convert of keys 0-31 of block j
-//      step 2: P V of block j (MFMA)     ||  exp/sum/convert of keys 32-63 of block j,
+//      step 1: QK^T of block j+1 (MFMA)  ||  exp/sum/convert of most keys of block j
+//      step 2: P V of block j (MFMA)     ||  exp/sum/convert of its other keys,
 //                                            then the row max of block j+1
 //    so the matrix core and the vector ALU work on different blocks at once;
 //    each pair's conversion runs one micro-step after its exponentials.
@@ -72,6 +72,7 @@ struct Bf16Cfg {
   static constexpr int THREADS = 64 * NW;
   static constexpr int STAGES = 4;       // LDS ring depth for K and for V
   static constexpr float TAU = 8.0f;     // lazy-rescale threshold (log2 units)
+  static constexpr float PMAX = 256.0f;  // 2^TAU: the largest probability kept
   static_assert(LOADS % NW == 0 && LOADS >= NW, "tile loads must split evenly over waves");
 };
 
@@ -129,6 +130,7 @@ struct Bf16State {
   u32x4 pb[C::QT][2 * C::NT]; // bf16 probabilities, P^T B-operand fragment F = keys 16F..16F+15
   float m[C::QT];             // running max of s*c (log2 units), shared by both half-waves
   float l[C::QT];             // lane-local part of the running sum of p
+  float lh[C::QT];            // l through the probabilities of the first half of a block's keys
   float alpha[C::QT];         // pending rescale of O (applied before the next P V)
   bool rescale;               // wave-uniform: alpha differs from 1 somewhere
 };
@@ -187,7 +189,7 @@ __device__ __forceinline__ void mask_tail(Scores<C>& sc, int kv0, int S, int lan
 
 // ---- step-2 VALU work: row max of a scored block, lazy move of the running max
 template <class C>
-__device__ __forceinline__ void softmax_max(Bf16State<C>& st, const Scores<C>& sc, float c) {
+__device__ __forceinline__ bool softmax_max(Bf16State<C>& st, const Scores<C>& sc, float c) {
   constexpr int QT = C::QT, NT = C::NT;
   bool need[QT], any = false;
   float mnew[QT];
@@ -211,7 +213,9 @@ __device__ __forceinline__ void softmax_max(Bf16State<C>& st, const Scores<C>& s
       st.alpha[qt] *= a;
     }
     st.rescale = true;
+    return true;
   }
+  return false;
 }
 
 // ---- step-1 VALU work: p = 2^(s c - m) -> bf16 P^T fragments, row sums
@@ -250,11 +254,11 @@ __device__ __forceinline__ void softmax_exp(Bf16State<C>& st, const Scores<C>& s
 // fragment LEAD positions ahead, issues the MFMA that uses the fragment read
 // LEAD micro-steps earlier, and does a slice of the softmax work, so LDS
 // latency and vector work hide under the matrix core.  The exponentials of a
-// block are split between the two steps (keys 0-31 under the next block's
-// QK^T, keys 32-63 under the first half of this block's P V) so that neither
-// step is bound by the vector ALU.  LDS addresses are per-lane offsets
-// computed once plus immediates (the double-buffer stage is a template
-// argument: splits start on even blocks).
+// block are split between the two steps (those the first half of its P V
+// needs, and at D = 128 some more, under the next block's QK^T; the rest under
+// the first half of this block's P V) so that neither step is bound by the
+// vector ALU.  LDS addresses are per-lane offsets computed once plus
+// immediates (the ring stage is a template argument).
 
 // Per-lane LDS byte offsets of the fragments, relative to a tile's start.
 template <class C>
@@ -328,6 +332,8 @@ struct PairOrder {
                                                                           : HP;
   static constexpr int qt(int k) { return (k % HP) / (4 * C::NT); }
   static constexpr int idx(int k) { return (k / HP) * 4 * C::NT + k % (4 * C::NT); }
+  // pair k is sub-tile qt(k)'s last pair of the first half of the keys
+  static constexpr bool last_of_first_half(int k) { return k < HP && (k + 1) % (4 * C::NT) == 0; }
 };
 
 // Step 1: S^T of the next block from K stage KST || the first NE1 probability
@@ -367,6 +373,7 @@ __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16
       if (f > 0 && k * NF / NE == f - 1) {
         const int qt = PO::qt(k), idx = PO::idx(k);
         st.pb[qt][idx / 4][idx % 4] = pack_sum(pe[k], lsum[qt]);
+        if (PO::last_of_first_half(k)) st.lh[qt] = lsum[qt];
       }
 #pragma unroll
     for (int k = 0; k < NE; ++k)
@@ -378,7 +385,29 @@ __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16
     if (k * NF / NE == NF - 1) {
       const int qt = PO::qt(k), idx = PO::idx(k);
       st.pb[qt][idx / 4][idx % 4] = pack_sum(pe[k], lsum[qt]);
+      if (PO::last_of_first_half(k)) st.lh[qt] = lsum[qt];
     }
+  // Overflow check of the pairs just computed (the running max was not taken
+  // for this block): a lane whose new probabilities sum to more than 2^TAU may
+  // hold one above 2^TAU (any one above it makes the sum exceed it).  Then the
+  // block's exact max is taken; if the running max moves, the O rescale is left
+  // pending for step 2 and these pairs are recomputed with the new max.
+  bool over = false;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) over |= !(lsum[qt] - st.l[qt] <= C::PMAX);
+  if (__builtin_amdgcn_ballot_w64(over)) {
+    if (softmax_max<C>(st, cur, c)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) lsum[qt] = st.l[qt];
+#pragma unroll
+      for (int k = 0; k < NE; ++k) {
+        const int qt = PO::qt(k), idx = PO::idx(k);
+        const f32x2 p = exp_pair2<C>(cur, qt, idx, c, -st.m[qt]);
+        st.pb[qt][idx / 4][idx % 4] = pack_sum(p, lsum[qt]);
+        if (PO::last_of_first_half(k)) st.lh[qt] = lsum[qt];
+      }
+    }
+  }
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     st.l[qt] = lsum[qt];
@@ -388,11 +417,10 @@ __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16
 }
 
 // Step 2: O^T = alpha O^T + V^T P^T from V stage VST; under the first half
-// (the first half of the block's keys) the remaining probability pairs, under
-// the second half the row max of the next block (lazy move of the running max;
-// the O rescale it may ask for is applied at the start of the next step 2).
+// (the first half of the block's keys) the remaining probability pairs, then
+// their overflow check before the second half uses them.
 template <class C, int VST>
-__device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, const Scores<C>& cur,
+__device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& cur,
                                       const uint8_t XS_LDS* lds, const LdsOffs<C>& off, float c) {
   using PO = PairOrder<C>;
   constexpr int QT = C::QT, NT = C::NT, DT = C::DT, ROWB = C::ROWB;
@@ -401,16 +429,14 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, co
   constexpr int LEAD = XS_LEAD < NF ? XS_LEAD : NF;
   constexpr int R = LEAD + 1;
   constexpr int NE = PO::NP - PO::NE1;     // pairs left for this step
-  constexpr int NM = 16 * NT * QT;         // scores of the next block per lane
   if (st.rescale) rescale_o<C>(st);
   const uint8_t XS_LDS* vb = lds + VST * C::TILE;  // off.v holds the V region's base
   auto vaddr = [&](int f) { return vb + off.v[f % DT] + (f / DT) * 16 * ROWB; };
-  float neg_m[QT], lsum[QT], mx[QT];
+  float neg_m[QT], lsum[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     neg_m[qt] = -st.m[qt];
     lsum[qt] = st.l[qt];
-    mx[qt] = nxt.s[0][qt][0];
   }
   u32x2 vlo[R], vhi[R];
   f32x2 pe[NE > 0 ? NE : 1];
@@ -433,6 +459,30 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, co
         const int qt = PO::qt(PO::NE1 + k), idx = PO::idx(PO::NE1 + k);
         st.pb[qt][idx / 4][idx % 4] = pack_sum(pe[k], lsum[qt]);
       }
+    if (f == HALF) {
+      // Overflow check of this step's pairs, as in step 1.  The first half of
+      // the block is already weighted into O: if the running max moves, O and
+      // the sum through that half are rescaled now and the second half's pairs
+      // (those of step 1 too) are recomputed with the new max.
+      bool over = false;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) over |= !(lsum[qt] - st.l[qt] <= C::PMAX);
+      if (__builtin_amdgcn_ballot_w64(over)) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) st.l[qt] = st.lh[qt];  // the sum O holds
+        if (softmax_max<C>(st, cur, c)) {
+          rescale_o<C>(st);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) lsum[qt] = st.l[qt];
+#pragma unroll
+          for (int k = PO::HP; k < PO::NP; ++k) {
+            const int qt = PO::qt(k), idx = PO::idx(k);
+            const f32x2 p = exp_pair2<C>(cur, qt, idx, c, -st.m[qt]);
+            st.pb[qt][idx / 4][idx % 4] = pack_sum(p, lsum[qt]);
+          }
+        }
+      }
+    }
     const int F = f / DT, dt = f % DT;
     const u32x4 vf = u32x4{vlo[f % R][0], vlo[f % R][1], vhi[f % R][0], vhi[f % R][1]};
 #pragma unroll
@@ -444,38 +494,11 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& nxt, co
           const int qt = PO::qt(PO::NE1 + k), idx = PO::idx(PO::NE1 + k);
           pe[k] = exp_pair2<C>(cur, qt, idx, c, neg_m[qt]);
         }
-    } else {
-      constexpr int EPS = NM / HALF;  // max over the scores of the next block
-#pragma unroll
-      for (int ee = 0; ee < EPS; ++ee) {
-        const int e = (f - HALF) * EPS + ee;  // 0 .. NM-1
-        const int qt = e / (16 * NT), r = e % (16 * NT);
-        mx[qt] = fmaxf(mx[qt], nxt.s[r / 16][qt][r % 16]);
-      }
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) pin(mx[qt]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  bool need[QT], any = false;
-  float mnew[QT];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    st.l[qt] = lsum[qt];
-    mnew[qt] = max_halves(mx[qt]) * c;
-    need[qt] = mnew[qt] > st.m[qt] + C::TAU;
-    any |= need[qt];
-  }
-  if (__builtin_amdgcn_ballot_w64(any)) {
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float a = need[qt] ? fast_exp2(st.m[qt] - mnew[qt]) : 1.0f;
-      st.m[qt] = need[qt] ? mnew[qt] : st.m[qt];
-      st.l[qt] *= a;
-      st.alpha[qt] *= a;
-    }
-    st.rescale = true;
-  }
+  for (int qt = 0; qt < QT; ++qt) st.l[qt] = lsum[qt];
 }
 
 // O^T = alpha O^T + V^T P^T of the last block of a piece from the V stage at
@@ -639,10 +662,10 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
       ld_v(j + 3, 3);
       step1<C, 1>(sb, sa, st, lds, off, c);  // block j
       if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
-      step2<C, 0>(st, sb, sa, lds, off, c);
+      step2<C, 0>(st, sa, lds, off, c);
       step1<C, 2>(sa, sb, st, lds, off, c);  // block j+1
       if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
-      step2<C, 1>(st, sa, sb, lds, off, c);
+      step2<C, 1>(st, sb, lds, off, c);
 
       wait_vmcnt<0>();
       __syncthreads();
@@ -652,10 +675,10 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
       if (j + 5 < je) ld_v(j + 5, 1);
       step1<C, 3>(sb, sa, st, lds, off, c);  // block j+2
       if (j + 3 >= nfull) mask_tail<C>(sb, (j + 3) * BN, S, lane);
-      step2<C, 2>(st, sb, sa, lds, off, c);
+      step2<C, 2>(st, sa, lds, off, c);
       step1<C, 0>(sa, sb, st, lds, off, c);  // block j+3
       if (j + 4 >= nfull) mask_tail<C>(sa, (j + 4) * BN, S, lane);
-      step2<C, 3>(st, sa, sb, lds, off, c);
+      step2<C, 3>(st, sb, lds, off, c);
     }
     // the last one to four blocks j .. je-1 (stages 0..3, scores of block j in sa)
     {
@@ -668,25 +691,29 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
       if (r > 1) {
         step1<C, 1>(sb, sa, st, lds, off, c);  // block j
         if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
-        step2<C, 0>(st, sb, sa, lds, off, c);
+        step2<C, 0>(st, sa, lds, off, c);
       }
       if (r > 2) {
         step1<C, 2>(sa, sb, st, lds, off, c);  // block j+1
         if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
-        step2<C, 1>(st, sa, sb, lds, off, c);
+        step2<C, 1>(st, sb, lds, off, c);
         wait_vmcnt<0>();
         __syncthreads();
       }
       if (r > 3) {
         step1<C, 3>(sb, sa, st, lds, off, c);  // block j+2
         if (j + 3 >= nfull) mask_tail<C>(sb, (j + 3) * BN, S, lane);
-        step2<C, 2>(st, sb, sa, lds, off, c);
+        step2<C, 2>(st, sa, lds, off, c);
       }
-      // the last block, j + r - 1: scores in sa when r is odd
-      if (r & 1)
+      // the last block, j + r - 1: scores in sa when r is odd (its max not yet
+      // taken)
+      if (r & 1) {
+        softmax_max<C>(st, sa, c);
         softmax_exp<C>(st, sa, c);
-      else
+      } else {
+        softmax_max<C>(st, sb, c);
         softmax_exp<C>(st, sb, c);
+      }
       pv_only<C>(st, lds, off, (uint32_t)(r - 1) * C::TILE);
     }
 
