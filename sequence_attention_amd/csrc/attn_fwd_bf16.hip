@@ -25,15 +25,20 @@
 //    directly.
 //  * Software pipeline inside the wave:
 //      step 1: QK^T of block j+1 (MFMA)  ||  exp/sum/convert of most keys of block j
-//      step 2: P V of block j (MFMA)     ||  exp/sum/convert of its other keys,
-//                                            then the row max of block j+1
+//      step 2: P V of block j (MFMA)     ||  exp/sum/convert of its other keys
 //    so the matrix core and the vector ALU work on different blocks at once;
 //    each pair's conversion runs one micro-step after its exponentials.
 //  * Online softmax in base 2: p = 2^(s*c - m), c = scale*log2(e) folded into
-//    one FMA per score.  The running max is moved only when a block's max
-//    exceeds it by more than 2^TAU (p <= 2^TAU), so rescaling O is a rare
-//    wave-uniform branch.  The row sum adds the fp32 p before their rounding
-//    to bf16 (plain adds: the vector ALU is the scarce unit here).
+//    one FMA per score.  The running max m is taken exactly for a piece's
+//    first and last blocks only; the other blocks' probabilities are computed
+//    with the current m and checked: when a lane's sum of a block's new p
+//    exceeds 2^TAU (as any single p above 2^TAU makes it), the block's exact
+//    max is taken, m moves if that max exceeds it by more than TAU (log2
+//    units), O is rescaled (a rare wave-uniform branch) and the block's p are
+//    recomputed.  So p <= 2^TAU always holds where p is used, as with a
+//    per-block max, without the max's vector work.  The row sum adds the
+//    fp32 p before their rounding to bf16 (plain adds: the vector ALU is the
+//    scarce unit here).
 //  * Epilogue: O/l rounded to bf16 and stored per query row at its
 //    destination-slice offset (p = s / T, s' = s - p*T).  Tile shapes and the
 //    reduction order never depend on P; only the store address does.
@@ -187,7 +192,8 @@ __device__ __forceinline__ void mask_tail(Scores<C>& sc, int kv0, int S, int lan
     }
 }
 
-// ---- step-2 VALU work: row max of a scored block, lazy move of the running max
+// ---- row max of a scored block, lazy move of the running max (piece ends and
+// the rare overflow path); returns whether the max moved
 template <class C>
 __device__ __forceinline__ bool softmax_max(Bf16State<C>& st, const Scores<C>& sc, float c) {
   constexpr int QT = C::QT, NT = C::NT;

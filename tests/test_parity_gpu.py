@@ -308,6 +308,47 @@ def _rising_scores(B, S, H, D, dtype, index):
     return w, inp
 
 
+def _mid_block_spikes(B, S, H, D, index):
+    """bf16 inputs whose large scores sit only in the last 16 keys of every 64-key
+    block: q[..., 0] = 1 and k[:, j, :, 0] = (j // 64) * 16 sqrt(D) for j % 64 >= 48,
+    else 0.  Each block's spike exceeds the previous block's max by 16 * 1.44 = 23
+    (log2 units) while its first 48 keys score far below it, so the kernel's
+    probabilities of those 48 keys pass and the overflow is found among the last
+    keys, computed under the first half of P V: the running max moves after half
+    the block is already weighted into O."""
+    w = workloads.custom(B, S, H, D, 1, index=index)
+    inp = workloads.make_inputs(w)
+    j = torch.arange(S)
+    spike = torch.where(j % 64 >= 48, (j // 64).to(torch.float32) * 16.0 * D ** 0.5, 0.0)
+    inp["q"][..., 0] = 1.0
+    inp["k"][..., 0] = spike.view(1, S, 1).to(torch.bfloat16)
+    return w, inp
+
+
+@pytest.mark.parametrize("B,S,H,D,P", [(2, 1000, 2, 64, 4), (1, 777, 3, 128, 7), (1, 4608, 2, 128, 8)])
+def test_running_max_moves_mid_block(gpu, B, S, H, D, P):
+    w, inp = _mid_block_spikes(B, S, H, D, 4600 + S + D)
+    scale = inp["scale"]
+    _say(f"mid-block spikes B={B} S={S} H={H} D={D} P={P}")
+    ref, ref_l = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, scale, with_lse=True)
+    ref_abs = oracle.attention_packed(inp["q"], inp["k"], inp["v"].abs(), P, scale)
+    u = 2.0 ** -8
+    bound = u * np.abs(ref) + u * (1 + u) * ref_abs + 1e-5
+    q, k, v = to_gpu(inp, gpu)
+    for ws in (None, "auto"):
+        out = xs.fwd(q, k, v, P, scale, workspace=ws)
+        out_l, lse = xs.fwd(q, k, v, P, scale, lse=True, workspace=ws)
+        torch.cuda.synchronize()
+        for name, o in (("O", out), ("O with lse", out_l)):
+            got = f64(o)
+            worst = float((np.abs(got - ref) / bound).max())
+            print(f"  workspace={ws} {name}: worst error / bound = {worst:.3f}", flush=True)
+            assert worst <= 1.0 and np.isfinite(got).all(), name
+        d = np.abs(f64(lse) - ref_l)
+        print(f"  workspace={ws} lse max_abs={d.max():.3e}", flush=True)
+        assert d.max() <= 5e-3
+
+
 @pytest.mark.parametrize("dtype,B,S,H,D,P", [("bf16", 2, 1000, 2, 64, 4), ("bf16", 1, 777, 3, 128, 7),
                                              ("fp8", 2, 1000, 2, 128, 8)])
 def test_running_max_moves_every_block(gpu, dtype, B, S, H, D, P):
