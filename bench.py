@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=25.0,
                     help="target wall time of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--samples", type=int, default=20,
+                    help="timed launches also bracketed by their own events (roofline launch time)")
     ap.add_argument("--in-layout", default="bshd", choices=["bshd", "chunked"],
                     help="input layout: [B][S][H][D] or the pre-attention All-to-All chunk layout "
                          "[P][B][S/P][H][D] (converted once, before timing)")
@@ -342,24 +344,32 @@ def main():
             step()
         torch.cuda.synchronize()
 
-    # timed region: K back-to-back launches, each bracketed by events on the launch stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # Timed region: K back-to-back launches on the launch stream, bracketed by two
+    # events.  A sample of the launches (every launch with --cold) is also
+    # bracketed by its own pair of events, for the kernel's mean launch duration
+    # in the roofline: each event between launches adds queue time of its own, so
+    # instrumenting every launch would slow the back-to-back steps being timed.
+    every = 1 if args.cold else max(1, args.steps // args.samples)
+    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for i in range(0, args.steps, every)}
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
     t_start.record(stream)
-    for i, (e0, e1) in enumerate(ev):
+    for i in range(args.steps):
         if flush is not None:
             flush.fill_(i & 0xFF)
-        e0.record(stream)
+        pair = ev.get(i)
+        if pair is not None:
+            pair[0].record(stream)
         step()
-        e1.record(stream)
+        if pair is not None:
+            pair[1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    launch_ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    launch_ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev.values()])
     ms_per_step = total_ms / args.steps
 
     flops = w.flops
@@ -400,7 +410,7 @@ def main():
         "pct_of_peak": round(100.0 * value / peak, 2),
         "pct_of_bf16_peak": round(100.0 * value / PEAK_TFLOPS["bf16"], 2),
         "launch_ms": {"mean": round(float(launch_ms.mean()), 4), "min": round(float(launch_ms.min()), 4),
-                      "median": round(float(np.median(launch_ms)), 4)},
+                      "median": round(float(np.median(launch_ms)), 4), "sampled_launches": len(launch_ms)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
                      "traffic": recorded_traffic(
