@@ -14,6 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libxs_attn.so")
+DEMO = os.path.join(PKG, "c_api_demo")  # host program using the C ABI alone
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["xs_attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "attn_combine.hip",
            "burst_gap.hip"]
@@ -49,8 +50,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the C-ABI demo links the library by name and finds it next to itself
+    cmd = [HIPCC, "-O2", "-std=c++17", f"-I{INCLUDE}", os.path.join(CSRC, "c_api_demo.cpp"),
+           f"-L{PKG}", "-lxs_attn", "-Wl,-rpath,$ORIGIN", "-o", DEMO + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"c_api_demo build failed:\n{r.stderr}")
+    os.replace(DEMO + ".tmp", DEMO)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {DEMO}")
     return LIB
 
 
