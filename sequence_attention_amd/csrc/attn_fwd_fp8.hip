@@ -23,7 +23,11 @@
 //    (the vector ALU, not the matrix core, bounds this kernel).  When the
 //    log-sum-exp output is requested, a second instantiation instead adds the
 //    fp32 probabilities before quantisation and normalises with that sum,
-//    which the log-sum-exp is defined by.
+//    which the log-sum-exp is defined by.  Having those sums at hand, it also
+//    skips the per-block row max: a lane whose sum of a block's new
+//    probabilities exceeds 2^TAU (as any single one above 2^TAU makes it)
+//    triggers the block's exact max, the lazy move and a recomputation, before
+//    P V uses the block.
 #include "attn_launch.h"
 #include "device_common.h"
 #include "piece.h"
@@ -49,6 +53,7 @@ struct Fp8Cfg {
   static constexpr int THREADS = 64 * NW;
   static constexpr int STAGES = 4;        // LDS ring depth for K and for V
   static constexpr float TAU = 8.0f;      // lazy-rescale threshold (log2 units)
+  static constexpr float PMAX = 256.0f;   // 2^TAU: the largest probability kept
   static_assert(LOADS <= NW, "one direct load per wave at most");
   static_assert(NT == 2, "the P^T operand layout assumes 64-key blocks");
 };
@@ -89,6 +94,7 @@ struct Fp8State {
   u32x4 p0, p1;      // P^T operand: e4m3 probabilities of keys 0..31 and 32..63
   float m, alpha;
   float l32;         // lane-local fp32 sum of the unquantised p (kept only when C::LSE)
+  float lb;          // l32 before the current block's probabilities (C::LSE)
   bool rescale;
 };
 
@@ -134,7 +140,7 @@ __device__ __forceinline__ void mask_tail8(Scores8<C>& sc, int kv0, int S, int l
 }
 
 template <class C>
-__device__ __forceinline__ void softmax_max8(Fp8State<C>& st, const Scores8<C>& sc, float c) {
+__device__ __forceinline__ bool softmax_max8(Fp8State<C>& st, const Scores8<C>& sc, float c) {
   float mx = sc.s[0][0];
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt)
@@ -148,7 +154,9 @@ __device__ __forceinline__ void softmax_max8(Fp8State<C>& st, const Scores8<C>& 
     st.alpha *= a;
     if (C::LSE) st.l32 *= a;
     st.rescale = true;
+    return true;
   }
+  return false;
 }
 
 // The row sum that normalises O: without the log-sum-exp output, the sum of
@@ -250,6 +258,19 @@ __device__ __forceinline__ uint32_t pack4(f32x4 p) {
   return pk;
 }
 
+// Probabilities of all 32 keys of tile nt (prologue and tail, not pipelined).
+template <class C>
+__device__ __forceinline__ void exp_tile8(Fp8State<C>& st, const Scores8<C>& sc, int nt, float c,
+                                          u32x4& out) {
+  const float neg_m = -st.m;
+  float lsum = st.l32;
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w[q] = pack4(exp4<C>(sc, nt, q, c, neg_m, lsum));
+  st.l32 = lsum;
+  out = u32x4{w[0], w[1], w[2], w[3]};
+}
+
 // Step A: S^T of the next block from K stage KST || keys 32..63 of the current
 // block (its keys 0..31 were done in the previous step B).
 template <class C, int KST>
@@ -292,6 +313,22 @@ __device__ __forceinline__ void step_a8(Scores8<C>& nxt, const Scores8<C>& cur, 
   st.l32 = lsum;
   st.p1 = u32x4{w[0], w[1], w[2], w[3]};
   keep(st.p1);
+  if (C::LSE) {
+    // Overflow check of the block's probabilities (keys 0..31 from the step B
+    // before, 32..63 here; none has entered P V yet): a lane whose sum of them
+    // exceeds 2^TAU may hold one above 2^TAU.  Then the block's exact max is
+    // taken and, if the running max moves, all 64 are recomputed with it (the
+    // O rescale waits for step B).
+    if (__builtin_amdgcn_ballot_w64(!(st.l32 - st.lb <= C::PMAX))) {
+      st.l32 = st.lb;
+      if (softmax_max8<C>(st, cur, c)) {
+        exp_tile8<C>(st, cur, 0, c, st.p0);
+        exp_tile8<C>(st, cur, 1, c, st.p1);
+      } else {
+        st.l32 = lsum;
+      }
+    }
+  }
 }
 
 // Step B: O^T = alpha O^T + V^T P^T from V stage VST || row max of the next
@@ -329,26 +366,33 @@ __device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
     st.o[f] = mfma_fp8(vf[f % R], pf, st.o[f]);
     if (!C::LSE && f == NF - 1) st.lt = mfma_fp8(ones, pf, st.lt);
     if (f < HALF) {
-      constexpr int EPS = 32 / HALF;  // max over the 32 scores of the next block
+      // Without the log-sum-exp: the next block's row max and the lazy move of
+      // the running max.  With it, the max is not taken here: the fp32 row sums
+      // detect a probability above 2^TAU at the end of the next step A.
+      if (!C::LSE) {
+        constexpr int EPS = 32 / HALF;  // max over the 32 scores of the next block
 #pragma unroll
-      for (int ee = 0; ee < EPS; ++ee) {
-        const int e = f * EPS + ee;
-        mx = fmaxf(mx, nxt.s[e / 16][e % 16]);
+        for (int ee = 0; ee < EPS; ++ee) {
+          const int e = f * EPS + ee;
+          mx = fmaxf(mx, nxt.s[e / 16][e % 16]);
+        }
+        pin(mx);
       }
-      pin(mx);
       if (f == HALF - 1) {
-        // lazy move of the running max (the O rescale waits for the next step B)
-        const float mnew = max_halves(mx) * c;
-        const bool need = mnew > st.m + C::TAU;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-          const float a = need ? fast_exp2(st.m - mnew) : 1.0f;
-          st.m = need ? mnew : st.m;
-          st.alpha *= a;
-          if (C::LSE) st.l32 *= a;
-          st.rescale = true;
+        if (!C::LSE) {
+          // lazy move of the running max (the O rescale waits for the next step B)
+          const float mnew = max_halves(mx) * c;
+          const bool need = mnew > st.m + C::TAU;
+          if (__builtin_amdgcn_ballot_w64(need)) {
+            const float a = need ? fast_exp2(st.m - mnew) : 1.0f;
+            st.m = need ? mnew : st.m;
+            st.alpha *= a;
+            st.rescale = true;
+          }
         }
         neg_m = -st.m;
         lsum = st.l32;
+        if (C::LSE) st.lb = st.l32;
       }
     } else {
 #pragma unroll
@@ -368,18 +412,6 @@ __device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
   keep(st.p0);
 }
 
-// Probabilities of all 32 keys of tile nt (prologue and tail, not pipelined).
-template <class C>
-__device__ __forceinline__ void exp_tile8(Fp8State<C>& st, const Scores8<C>& sc, int nt, float c,
-                                          u32x4& out) {
-  const float neg_m = -st.m;
-  float lsum = st.l32;
-  uint32_t w[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) w[q] = pack4(exp4<C>(sc, nt, q, c, neg_m, lsum));
-  st.l32 = lsum;
-  out = u32x4{w[0], w[1], w[2], w[3]};
-}
 
 // O^T = alpha O^T + V^T P^T (and the row sums) of the last block of a piece,
 // from the V stage at byte offset stage_off of the V region (not pipelined).
@@ -510,6 +542,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
     qk_block8<C>(sa, st, kbuf(0), lane);
     if (jb >= nfull) mask_tail8<C>(sa, jb * BN, S, lane);
     softmax_max8<C>(st, sa, c);
+    st.lb = st.l32;
     exp_tile8<C>(st, sa, 0, c, st.p0);
 
     // K/V blocks stream through a four-stage LDS ring with one barrier per two
@@ -578,10 +611,23 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
         step_b8<C, 2>(st, sb, lds, off, c, ones);
       }
       // the last block, j + r - 1: scores in sa when r is odd, keys 0..31 done
-      if (r & 1)
+      if (C::LSE) {
+        // its max not yet taken: take it, then recompute all its probabilities
+        st.l32 = st.lb;
+        if (r & 1) {
+          softmax_max8<C>(st, sa, c);
+          exp_tile8<C>(st, sa, 0, c, st.p0);
+          exp_tile8<C>(st, sa, 1, c, st.p1);
+        } else {
+          softmax_max8<C>(st, sb, c);
+          exp_tile8<C>(st, sb, 0, c, st.p0);
+          exp_tile8<C>(st, sb, 1, c, st.p1);
+        }
+      } else if (r & 1) {
         exp_tile8<C>(st, sa, 1, c, st.p1);
-      else
+      } else {
         exp_tile8<C>(st, sb, 1, c, st.p1);
+      }
       pv_only8<C>(st, lds, off, (uint32_t)(r - 1) * C::TILE, ones);
     }
 
