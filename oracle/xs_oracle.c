@@ -21,7 +21,10 @@
  *        m    = max_j s_j                      (exact row max, first pass)
  *        w_j  = exp(s_j - m),  l = sum_j w_j   (second pass)
  *        O[b,i,h,:] = (sum_j w_j * v[b,j,h,:]) / l
- *    There is no online rescaling and no blocking: one query row at a time.
+ *    There is no online rescaling and no blocking: one query row at a time
+ *    (the score pass walks eight keys side by side, each dot product still
+ *    summed over d in index order, so every value is the one the plain loop
+ *    gives).
  *  - The destination-ordered buffer is the layout an All-to-All over P ranks
  *    delivers when the sequence is cut into P contiguous slices of T = S/P
  *    rows: out_packed[p][b][s'][h][d] = O[b][p*T + s'][h][d].
@@ -34,9 +37,10 @@
  *    (((p*B + b)*T + s')*H + h)*D + d with p = floor(s/T), s' = s - p*T.
  *
  * Inputs are stored as fp64, bf16 (bit patterns) or OCP fp8 e4m3fn codes with
- * a per-tensor fp64 descale; every element is decoded exactly to fp64 before
- * any arithmetic.  All arithmetic is fp64 with libm exp().  Build without
- * -ffast-math.
+ * a per-tensor fp64 descale; every element is decoded exactly to fp64 once per
+ * call, into [B][S][H][D] arrays, before any arithmetic.  All arithmetic is
+ * fp64 with libm exp(); each dot product and sum runs in index order.  Build
+ * without -ffast-math.
  */
 #include <math.h>
 #include <pthread.h>
@@ -73,55 +77,86 @@ double xs_oracle_decode_e4m3(uint8_t code) {
   return sign ? -mag : mag;
 }
 
+/* The problem after decoding: q, k, v as fp64 [B][H][S][D] arrays, each
+ * element the exact value of the input element (x8 * descale for e4m3). */
 typedef struct {
-  int dtype;
-  const void *q, *k, *v;
-  double q_descale, k_descale, v_descale;
+  const double *q, *k, *v;
   int64_t B, S, H, D;
   double scale;
-  int64_t in_P; /* 0: inputs are [B][S][H][D]; >= 1: [in_P][B][S/in_P][H][D] */
 } xso_problem;
 
-/* Element x[b][s][h][d] of an input tensor in the problem's layout, decoded to
- * fp64. */
-static double load(const xso_problem *pr, const void *base, double descale, int64_t b, int64_t s,
-                   int64_t h, int64_t d) {
-  int64_t idx;
-  if (pr->in_P > 0) {
-    const int64_t T = pr->S / pr->in_P, p = s / T, sp = s - p * T;
-    idx = (((p * pr->B + b) * T + sp) * pr->H + h) * pr->D + d;
-  } else {
-    idx = ((b * pr->S + s) * pr->H + h) * pr->D + d;
-  }
-  switch (pr->dtype) {
-    case XSO_BF16:
-      return xs_oracle_decode_bf16(((const uint16_t *)base)[idx]);
-    case XSO_E4M3:
-      return xs_oracle_decode_e4m3(((const uint8_t *)base)[idx]) * descale;
-    default:
-      return ((const double *)base)[idx];
-  }
+/* Decodes one input tensor, stored as fp64, bf16 bit patterns or e4m3 codes
+ * (times descale) in [B][S][H][D] (in_P = 0) or in the chunk layout
+ * [in_P][B][S/in_P][H][D], into a new fp64 array ordered [B][H][S][D], so that
+ * the rows of one (batch, head) are contiguous (NULL when the allocation
+ * fails).  Every element is decoded exactly, once per call. */
+static double *decode_input(int dtype, const void *base, double descale, int64_t in_P, int64_t B,
+                            int64_t S, int64_t H, int64_t D) {
+  double *x = (double *)malloc((size_t)(B * S * H * D) * sizeof(double));
+  if (!x) return NULL;
+  double e4m3[256];
+  for (int c = 0; c < 256; ++c) e4m3[c] = xs_oracle_decode_e4m3((uint8_t)c) * descale;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t s = 0; s < S; ++s)
+      for (int64_t h = 0; h < H; ++h)
+        for (int64_t d = 0; d < D; ++d) {
+          int64_t idx; /* position of element (b, s, h, d) in the input's layout */
+          if (in_P > 0) {
+            const int64_t T = S / in_P, p = s / T, sp = s - p * T;
+            idx = (((p * B + b) * T + sp) * H + h) * D + d;
+          } else {
+            idx = ((b * S + s) * H + h) * D + d;
+          }
+          double val;
+          switch (dtype) {
+            case XSO_BF16:
+              val = xs_oracle_decode_bf16(((const uint16_t *)base)[idx]);
+              break;
+            case XSO_E4M3:
+              val = e4m3[((const uint8_t *)base)[idx]];
+              break;
+            default:
+              val = ((const double *)base)[idx];
+          }
+          x[((b * H + h) * S + s) * D + d] = val;
+        }
+  return x;
 }
 
 /* One output row O[b,i,h,:] by the two-pass definition above, and the row's
  * log-sum-exp.  `s` is a scratch row of S doubles and `acc` one of D doubles. */
 static double attention_row(const xso_problem *pr, int64_t b, int64_t i, int64_t h, double *s,
                             double *acc, double *out_row) {
-  const int64_t S = pr->S, D = pr->D;
-  double m = -INFINITY;
-  for (int64_t j = 0; j < S; ++j) {
-    double dot = 0.0;
+  const int64_t S = pr->S, H = pr->H, D = pr->D;
+  const size_t head = (size_t)((b * H + h) * S) * D; /* row 0 of (b, h) */
+  const double *qi = pr->q + head + i * D, *K = pr->k + head, *V = pr->v + head;
+  /* pass 1: the scores.  Keys are taken eight at a time only so that the
+   * eight dot products -- each summed over d in index order -- proceed side
+   * by side; the remaining keys one at a time. */
+  int64_t j = 0;
+  for (; j + 8 <= S; j += 8) {
+    const double *k0 = K + j * D;
+    double dot[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     for (int64_t d = 0; d < D; ++d)
-      dot += load(pr, pr->q, pr->q_descale, b, i, h, d) * load(pr, pr->k, pr->k_descale, b, j, h, d);
-    s[j] = pr->scale * dot;
-    if (s[j] > m) m = s[j];
+      for (int u = 0; u < 8; ++u) dot[u] += qi[d] * k0[u * D + d];
+    for (int u = 0; u < 8; ++u) s[j + u] = pr->scale * dot[u];
   }
+  for (; j < S; ++j) {
+    double dot = 0.0;
+    for (int64_t d = 0; d < D; ++d) dot += qi[d] * K[j * D + d];
+    s[j] = pr->scale * dot;
+  }
+  double m = -INFINITY;
+  for (j = 0; j < S; ++j)
+    if (s[j] > m) m = s[j];
+  /* pass 2 */
   double l = 0.0;
   for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
-  for (int64_t j = 0; j < S; ++j) {
+  for (j = 0; j < S; ++j) {
+    const double *vj = V + j * D;
     double w = exp(s[j] - m);
     l += w;
-    for (int64_t d = 0; d < D; ++d) acc[d] += w * load(pr, pr->v, pr->v_descale, b, j, h, d);
+    for (int64_t d = 0; d < D; ++d) acc[d] += w * vj[d];
   }
   for (int64_t d = 0; d < D; ++d) out_row[d] = acc[d] / l;
   return m + log(l);
@@ -210,6 +245,24 @@ static int run_rows(const xso_problem *pr, const int64_t *rows, int64_t nrows, d
   return status;
 }
 
+/* Decodes q, k, v (see decode_input) and computes the given rows; the decoded
+ * copies are freed before returning.  Returns 0 or -1 (allocation). */
+static int solve(int dtype, const void *q, const void *k, const void *v, double q_descale,
+                 double k_descale, double v_descale, int64_t in_P, int64_t B, int64_t S,
+                 int64_t H, int64_t D, double scale, const int64_t *rows, int64_t nrows,
+                 double *out, int64_t P, double *lse, int nthreads) {
+  double *qd = decode_input(dtype, q, q_descale, in_P, B, S, H, D);
+  double *kd = decode_input(dtype, k, k_descale, in_P, B, S, H, D);
+  double *vd = decode_input(dtype, v, v_descale, in_P, B, S, H, D);
+  int rc = -1;
+  if (qd && kd && vd) {
+    xso_problem pr = {qd, kd, vd, B, S, H, D, scale};
+    rc = run_rows(&pr, rows, nrows, out, P, lse, nthreads);
+  }
+  free(qd), free(kd), free(vd);
+  return rc;
+}
+
 static int check(int dtype, const void *q, const void *k, const void *v, int64_t B, int64_t S,
                  int64_t H, int64_t D) {
   if (!q || !k || !v) return -1;
@@ -235,8 +288,8 @@ int xs_oracle_attention_rows_ex(int dtype, const void *q, const void *k, const v
     if (rows[3 * r] < 0 || rows[3 * r] >= B || rows[3 * r + 1] < 0 || rows[3 * r + 1] >= S ||
         rows[3 * r + 2] < 0 || rows[3 * r + 2] >= H)
       return -2;
-  xso_problem pr = {dtype, q, k, v, q_descale, k_descale, v_descale, B, S, H, D, scale, in_P};
-  return run_rows(&pr, rows, nrows, out, 0, lse, nthreads);
+  return solve(dtype, q, k, v, q_descale, k_descale, v_descale, in_P, B, S, H, D, scale, rows,
+               nrows, out, 0, lse, nthreads);
 }
 
 int xs_oracle_attention_rows(int dtype, const void *q, const void *k, const void *v,
@@ -264,15 +317,15 @@ int xs_oracle_attention_packed_ex(int dtype, const void *q, const void *k, const
   int64_t nrows = B * S * H;
   int64_t *rows = (int64_t *)malloc((size_t)nrows * 3 * sizeof(int64_t));
   if (!rows) return -1;
-  int64_t r = 0;
+  int64_t r = 0; /* ordered by (b, h, s): threads work on the rows of one head together */
   for (int64_t b = 0; b < B; ++b)
-    for (int64_t s = 0; s < S; ++s)
-      for (int64_t h = 0; h < H; ++h) {
+    for (int64_t h = 0; h < H; ++h)
+      for (int64_t s = 0; s < S; ++s) {
         rows[3 * r] = b, rows[3 * r + 1] = s, rows[3 * r + 2] = h;
         ++r;
       }
-  xso_problem pr = {dtype, q, k, v, q_descale, k_descale, v_descale, B, S, H, D, scale, in_P};
-  rc = run_rows(&pr, rows, nrows, out_packed, P, lse, nthreads);
+  rc = solve(dtype, q, k, v, q_descale, k_descale, v_descale, in_P, B, S, H, D, scale, rows, nrows,
+             out_packed, P, lse, nthreads);
   free(rows);
   return rc;
 }
