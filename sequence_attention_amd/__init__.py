@@ -15,10 +15,14 @@ the calls raise.
 By default the calls use the split-key schedule when it fills the GPU better,
 with a workspace allocated from torch's caching allocator (pass a tensor of
 at least workspace_size(...) bytes to reuse one, or workspace=None to run
-unsplit).
+unsplit).  The call runs on `stream` (a torch stream or a raw hipStream_t
+handle; default the current stream), and the buffers it allocates come from
+that stream's pool.  A caller-provided out, lse or workspace that another
+stream uses must be ordered by the caller (events or record_stream).
 """
 from __future__ import annotations
 
+import contextlib
 import math
 
 import numpy as np
@@ -40,10 +44,22 @@ def default_scale(D: int) -> float:
     return float(np.float32(1.0 / math.sqrt(D)))
 
 
-def _stream_ptr(t: torch.Tensor, stream) -> int:
+def _alloc_on(s, out, lse, workspace):
+    """Context in which the call's own buffers are allocated: the call's stream
+    when anything is to be allocated (nothing to switch otherwise)."""
+    if out is None or lse is True or isinstance(workspace, str):
+        return torch.cuda.stream(s)
+    return contextlib.nullcontext()
+
+
+def _stream(t: torch.Tensor, stream) -> torch.cuda.Stream:
+    """The stream the call runs on, as a torch stream: the current one by
+    default; a raw hipStream_t handle (int) is wrapped, not copied."""
     if stream is None:
-        stream = torch.cuda.current_stream(t.device)
-    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream(t.device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=t.device)
 
 
 def _check_inputs(q, k, v, dtype, P, in_layout):
@@ -185,12 +201,17 @@ def fwd(q, k, v, P: int, scale: float | None = None, out=None, stream=None,
     lse=True (or a [B][H][S] float32 tensor) the rows' natural-log log-sum-exp is
     written too and (out_packed, lse) is returned."""
     B, S, H, D, code = _check_inputs(q, k, v, torch.bfloat16, P, in_layout)
-    out = _out(q, B, S, H, D, P, out)
-    lse_t = _lse(q, B, S, H, lse)
+    s = _stream(q, stream)
+    # Buffers allocated here come from the caching allocator's pool of the stream
+    # the kernels run on, so a block freed on return is not handed to another
+    # stream's allocation while those kernels may still write it.
+    with _alloc_on(s, out, lse, workspace):
+        out = _out(q, B, S, H, D, P, out)
+        lse_t = _lse(q, B, S, H, lse)
+        ws, nbytes = _workspace(q, B, S, H, D, workspace)
     scale = default_scale(D) if scale is None else float(scale)
-    ws, nbytes = _workspace(q, B, S, H, D, workspace)
     check(xs_attn_fwd_ex(q, k, v, code, out, lse_t, B, S, H, D, P, scale, ws, nbytes,
-                         _stream_ptr(q, stream)))
+                         s.cuda_stream))
     return (out, lse_t) if lse_t is not None else out
 
 
@@ -199,13 +220,15 @@ def fwd_fp8(q8, k8, v8, descales, P: int, scale: float | None = None, out=None,
     """Attention over e4m3 inputs with per-tensor descales (x = x8 * d); layouts,
     lse and the return value as for fwd."""
     B, S, H, D, code = _check_inputs(q8, k8, v8, torch.float8_e4m3fn, P, in_layout)
-    out = _out(q8, B, S, H, D, P, out)
-    lse_t = _lse(q8, B, S, H, lse)
+    s = _stream(q8, stream)
+    with _alloc_on(s, out, lse, workspace):  # the pool of the call's stream (see fwd)
+        out = _out(q8, B, S, H, D, P, out)
+        lse_t = _lse(q8, B, S, H, lse)
+        ws, nbytes = _workspace(q8, B, S, H, D, workspace)
     scale = default_scale(D) if scale is None else float(scale)
     dq, dk, dv = (float(d) for d in descales)
-    ws, nbytes = _workspace(q8, B, S, H, D, workspace)
     check(xs_attn_fwd_fp8_ex(q8, k8, v8, code, dq, dk, dv, out, lse_t, B, S, H, D, P, scale, ws,
-                             nbytes, _stream_ptr(q8, stream)))
+                             nbytes, s.cuda_stream))
     return (out, lse_t) if lse_t is not None else out
 
 

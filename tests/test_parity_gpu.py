@@ -4,9 +4,11 @@ Bar: every element of out_packed within max-abs 1e-2 (bf16 inputs) or 5e-2
 (fp8 inputs) of the oracle on the same seeded bytes, plus a relative-L2 gate
 (1e-2 bf16, 8e-2 fp8) that a zero or badly scaled output cannot pass; the
 relayout is bit-exact (P = k equals the pack of P = 1 bit for bit).  Small
-shapes are checked on every element; the full-size workloads are checked on
-sampled rows (which touch every destination slice) that the oracle computes
-one by one, and by properties that hold at any size.
+shapes and the image share are checked on every element here, the full-size
+workloads additionally on sampled rows (which touch every destination slice)
+and by properties that hold at any size; tests/test_parity_full_gpu.py checks
+the video and fp8 shares on every element and the long share on three rows of
+every query tile.
 """
 import numpy as np
 import pytest
@@ -588,3 +590,104 @@ def test_persistent_schedule_cut_tiles(gpu, B, S, H, D):
     assert_gate(f64(cut), ref, "bf16", "cut schedule")
     assert_gate(f64(whole), ref, "bf16", "uncut schedule")
     assert float((cut.float() - whole.float()).abs().max()) <= 2e-3
+
+
+# ------------------------------------------------------------------ a call on a stream other than the current one
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_side_stream_with_auto_workspace(gpu, dtype):
+    # The image share (its plan cuts every tile, so the call allocates a
+    # workspace, the output and the log-sum-exp itself) on a side stream, while
+    # the current stream allocates and overwrites memory of the same sizes right
+    # after the call is enqueued: the call's buffers must come from the side
+    # stream's pool, so that nothing freed on return is reused before the side
+    # stream's kernels are done with it.
+    w = workloads.WORKLOADS["image"].with_(dtype=dtype, index=8300 + (dtype == "fp8"))
+    inp = workloads.make_inputs(w)
+    assert xs.split_count(w.B, w.S, w.H, w.D) > 1
+    q, k, v = to_gpu(inp, gpu)
+    ref, ref_l = oracle.attention_packed(inp["q"], inp["k"], inp["v"], w.P, inp["scale"],
+                                         inp["descales"], with_lse=True)
+    side = torch.cuda.Stream(gpu)
+    side.wait_stream(torch.cuda.current_stream(gpu))
+    ws_bytes = xs.workspace_size(w.B, w.S, w.H, w.D)
+    results = []
+    _say(f"side stream {dtype} image share, workspace {ws_bytes} B")
+    for _ in range(3):
+        if dtype == "fp8":
+            out, lse = xs.fwd_fp8(q, k, v, inp["descales"], w.P, inp["scale"], stream=side,
+                                  workspace="auto", lse=True)
+        else:
+            out, lse = xs.fwd(q, k, v, w.P, inp["scale"], stream=side, workspace="auto", lse=True)
+        # the current stream allocates and fills blocks of the workspace's size
+        junk = [torch.full((ws_bytes // 4,), -7.0, device=gpu) for _ in range(2)]
+        results.append((out, lse))
+        del junk
+    torch.cuda.current_stream(gpu).wait_stream(side)
+    torch.cuda.synchronize()
+    for out, lse in results:
+        assert_gate(f64(out), ref, dtype, f"{dtype} side stream")
+        assert float(np.abs(f64(lse) - ref_l).max()) <= 5e-3
+
+
+# ------------------------------------------------------------------ fp8: running max moving inside a block (lse path)
+def _fp8_block_spikes(B, S, H, D, lo, hi, index):
+    """fp8 inputs whose large scores sit only in keys lo..hi-1 of every 64-key
+    block: q[..., 0] = 1 and k[:, j, :, 0] = (j // 64) * 16 sqrt(D) there, else 0,
+    then requantised to e4m3 with fresh per-tensor descales.  Each block's spike
+    exceeds the previous block's max by about 16 * 1.44 = 23 (log2 units), so the
+    kernel's probabilities computed with the running max overflow in exactly
+    those keys and the max moves every block."""
+    w = workloads.custom(B, S, H, D, 1, dtype="fp8", index=index)
+    inp = workloads.make_inputs(w)
+    dq, dk, dv = inp["descales"]
+    q = inp["q"].to(torch.float32) * dq
+    k = inp["k"].to(torch.float32) * dk
+    j = torch.arange(S)
+    inb = (j % 64 >= lo) & (j % 64 < hi)
+    spike = torch.where(inb, (j // 64).to(torch.float32) * 16.0 * D ** 0.5, 0.0)
+    q[..., 0] = 1.0
+    k[..., 0] = spike.view(1, S, 1)
+    dq, dk = float(q.abs().max()) / 448.0, float(k.abs().max()) / 448.0
+    inp["q"] = (q / dq).to(torch.float8_e4m3fn)
+    inp["k"] = (k / dk).to(torch.float8_e4m3fn)
+    inp["descales"] = (dq, dk, dv)
+    return w, inp
+
+
+@pytest.mark.parametrize("lo,hi", [(16, 32), (48, 64)])
+def test_fp8_running_max_moves_mid_block_with_lse(gpu, lo, hi):
+    # Keys 0..31 of a block have their probabilities computed under the P V of
+    # the block before, keys 32..63 under the block's own QK^T; with the
+    # log-sum-exp requested the kernel takes no per-block max and finds the
+    # overflow from the lane's sum of the new probabilities.  Spikes in either
+    # half must move the running max before any of the block enters P V.
+    B, S, H, D, P = 2, 1000, 2, 128, 8
+    w, inp = _fp8_block_spikes(B, S, H, D, lo, hi, 4700 + lo)
+    scale = inp["scale"]
+    _say(f"fp8 spikes in keys {lo}..{hi - 1} of every block B={B} S={S} H={H} D={D} P={P}")
+    ref, ref_l = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, scale, inp["descales"],
+                                         with_lse=True)
+    dq, dk, dv = inp["descales"]
+    vabs = inp["v"].to(torch.float64).abs() * dv
+    qf, kf = inp["q"].to(torch.float64) * dq, inp["k"].to(torch.float64) * dk
+    ref_abs = oracle.attention_packed(qf, kf, vabs, P, scale)
+    # rounding bound of the e4m3 probabilities (as in the rising-scores test)
+    u = 2.0 ** -4
+    bound = u / (1 - u) * (ref_abs + np.abs(ref)) + 2.0 ** -8 * np.abs(ref) \
+        + 2.0 ** -9 * float(vabs.max())
+    # log-sum-exp bar: 5e-3 plus the e4m3 matrix core's score accumulation
+    sabs = torch.einsum("bqhd,bkhd->bhqk", qf.abs(), kf.abs()).amax(-1).numpy() * scale
+    bar = 5e-3 + 2.0 ** -11 * sabs
+    q, k, v = to_gpu(inp, gpu)
+    for ws in (None, "auto"):
+        out, lse = xs.fwd_fp8(q, k, v, inp["descales"], P, scale, lse=True, workspace=ws)
+        plain = xs.fwd_fp8(q, k, v, inp["descales"], P, scale, workspace=ws)
+        torch.cuda.synchronize()
+        for name, o in (("O with lse", out), ("O", plain)):
+            got = f64(o)
+            worst = float((np.abs(got - ref) / bound).max())
+            print(f"  workspace={ws} {name}: worst error / bound = {worst:.3f}", flush=True)
+            assert np.isfinite(got).all() and worst <= 1.0, name
+        d = np.abs(f64(lse) - ref_l)
+        print(f"  workspace={ws} lse max_abs={d.max():.3e}", flush=True)
+        assert np.isfinite(d).all() and (d <= bar).all()
