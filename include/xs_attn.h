@@ -52,6 +52,7 @@ extern "C" {
 #define XS_ERR_LAUNCH (-5)      /* the HIP launch reported an error */
 #define XS_ERR_OVERLAP (-6)     /* out_packed, lse or the workspace overlaps another buffer */
 #define XS_ERR_WORKSPACE (-7)   /* workspace smaller than xs_attn_workspace_size() */
+#define XS_ERR_SCRATCH (-8)     /* xs_attn_fwd_noalloc: partials exceed its static scratch */
 /* (XS_ERR_UNSUPPORTED also when B*H_local*ceil(S/256) exceeds 2^31 - 1 query tiles.) */
 
 /* Attention forward over bf16 inputs with the destination-ordered epilogue.
@@ -109,6 +110,26 @@ int xs_attn_fwd_fp8_ws(const void *q8, const void *k8, const void *v8, float q_d
                        float k_descale, float v_descale, void *out_packed, int B, int S,
                        int H_local, int D, int P, float scale, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate (code under HIP-graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): xs_attn_fwd_ws without the
+ * workspace arguments.  The split-key partials go to a static device array of
+ * the library, XS_NOALLOC_SCRATCH_BYTES bytes (65 MiB) that every GPU the
+ * library runs on holds until the process ends; the call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).  The first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress) and
+ * keeps its address.  65 MiB holds the partials of every shape on a device of
+ * up to 256 compute units (at most one workgroup per compute unit writes two
+ * 256-row slots of fp32 O, max and sum); a larger need returns XS_ERR_SCRATCH
+ * before any launch.  The partials are always written before they are read,
+ * so nothing has to start at zero.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (on different streams, or from
+ * different threads without ordering) race and give wrong results; calls
+ * ordered on one stream do not.  Arguments, results and status codes are
+ * those of xs_attn_fwd_ws (bit-identical output for the same inputs). */
+#define XS_NOALLOC_SCRATCH_BYTES 68157440
+int xs_attn_fwd_noalloc(const void *q, const void *k, const void *v, void *out_packed, int B,
+                        int S, int H_local, int D, int P, float scale, void *stream);
 
 /* Input layouts of q, k, v for the _ex entry points. */
 #define XS_LAYOUT_BSHD 0    /* [B][S][H_local][D] */

@@ -42,6 +42,8 @@ def lib() -> ctypes.CDLL:
         L.xs_attn_fwd_fp8_ex.argtypes = [vp, vp, vp, ci, cf, cf, cf, vp, vp, ci, ci, ci, ci, ci, cf,
                                          vp, sz, vp]
         L.xs_attn_fwd_fp8_ex.restype = ci
+        L.xs_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp]
+        L.xs_attn_fwd_noalloc.restype = ci
         L.xs_attn_workspace_size.argtypes = [ci, ci, ci, ci]
         L.xs_attn_workspace_size.restype = sz
         L.xs_attn_split_count.argtypes = [ci, ci, ci, ci]

@@ -5,8 +5,18 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "attn_launch.h"
 #include "xs_attn.h"
+
+// Device memory of xs_attn_fwd_noalloc: the split-key partials of one call
+// (fp32 partial O, then per-row running max and row sum), the same contents a
+// caller workspace holds.  Every GPU the library runs on holds its own copy
+// from the time the library's code is loaded onto it until the process ends.
+// Host code never passes `scratch` itself (in host code the name is only a
+// stand-in): it uses the per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[XS_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -217,6 +227,27 @@ int attach_workspace(xs::AttnArgs* a, void* ws, size_t ws_bytes, size_t in_elem_
   return XS_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return XS_ERR_LAUNCH;
+  if (dev >= kMaxDevices) return XS_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return XS_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return XS_OK;
+}
+
 int launch(const xs::AttnArgs& a, bool fp8, hipStream_t stream) {
   const hipError_t e = fp8 ? xs::launch_attn_fp8(a, stream) : xs::launch_attn_bf16(a, stream);
   if (e != hipSuccess) return XS_ERR_LAUNCH;
@@ -293,6 +324,23 @@ int xs_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_desc
                             out_packed, nullptr, B, S, H_local, D, P, scale, nullptr, 0, stream);
 }
 
+int xs_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out_packed, int B,
+                        int S, int H_local, int D, int P, float scale, void* stream) {
+  xs::AttnArgs a;
+  int rc = validate(q, k, v, out_packed, B, S, H_local, D, P, scale, 2, &a);
+  if (rc != XS_OK) return rc;
+  const size_t need = workspace_bytes(plan_for(B, S, H_local, D, true), D);
+  if (need > (size_t)XS_NOALLOC_SCRATCH_BYTES) return XS_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    rc = scratch_address(&ws);
+    if (rc != XS_OK) return rc;
+  }
+  rc = attach_workspace(&a, ws, (size_t)XS_NOALLOC_SCRATCH_BYTES, 2);
+  if (rc != XS_OK) return rc;
+  return launch(a, false, (hipStream_t)stream);
+}
+
 size_t xs_attn_workspace_size(int B, int S, int H_local, int D) {
   if (B < 1 || S < 1 || H_local < 1 || (D != 64 && D != 128)) return 0;
   return workspace_bytes(plan_for(B, S, H_local, D, true), D);
@@ -330,6 +378,9 @@ const char* xs_attn_strerror(int status) {
       return "buffers overlap: out_packed, lse or the workspace shares memory with another buffer";
     case XS_ERR_WORKSPACE:
       return "workspace smaller than xs_attn_workspace_size()";
+    case XS_ERR_SCRATCH:
+      return "xs_attn_fwd_noalloc: the shape's split-key partials need more than the library's "
+             "static scratch of XS_NOALLOC_SCRATCH_BYTES bytes (use xs_attn_fwd_ws)";
     default:
       return "unknown status code";
   }

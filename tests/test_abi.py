@@ -12,6 +12,7 @@ from sequence_attention_amd import _lib
 XS_OK, XS_ERR_NULL, XS_ERR_SHAPE, XS_ERR_UNSUPPORTED, XS_ERR_ALIGN, XS_ERR_LAUNCH, XS_ERR_OVERLAP = (
     0, -1, -2, -3, -4, -5, -6)
 XS_ERR_WORKSPACE = -7
+XS_ERR_SCRATCH = -8
 
 # distinct, 16-byte aligned, far-apart fake device addresses (never dereferenced)
 Q, K, V, O = 0x10000000, 0x20000000, 0x30000000, 0x40000000
@@ -22,7 +23,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == {"xs_attn_fwd", "xs_attn_fwd_fp8", "xs_attn_fwd_ws", "xs_attn_fwd_fp8_ws",
                           "xs_attn_fwd_ex", "xs_attn_fwd_fp8_ex", "xs_attn_workspace_size",
                           "xs_attn_split_count", "xs_attn_strerror", "xs_attn_version",
-                          "xs_burst_gap"}
+                          "xs_attn_fwd_noalloc", "xs_burst_gap"}
     L = _lib.lib()
     for n in names:
         assert getattr(L, n) is not None
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_function():
 def test_version_and_strerror():
     assert xs.xs_attn_version() == 10200
     for code in (XS_OK, XS_ERR_NULL, XS_ERR_SHAPE, XS_ERR_UNSUPPORTED, XS_ERR_ALIGN, XS_ERR_LAUNCH,
-                 XS_ERR_OVERLAP, XS_ERR_WORKSPACE, 12345):
+                 XS_ERR_OVERLAP, XS_ERR_WORKSPACE, XS_ERR_SCRATCH, 12345):
         s = xs.xs_attn_strerror(code)
         assert isinstance(s, str) and s
     assert xs.xs_attn_strerror(12345) == "unknown status code"
@@ -231,3 +232,23 @@ def test_burst_gap_validates_before_any_launch():
         assert L.xs_burst_gap(D, 1 << 20, producers, nbytes, nburst, gap, T, None) == -2
     assert L.xs_burst_gap(D + 8, 1 << 20, 4, 4096, 2, 0, T, None) == -4
     assert L.xs_burst_gap(D, 1 << 20, 4, 4096, 2, 0, T + 4, None) == -4
+
+
+def test_noalloc_entry_validates_before_any_hip_call():
+    L = _lib.lib()
+    f = L.xs_attn_fwd_noalloc
+    assert f(None, K, V, O, 1, 64, 1, 64, 1, 0.125, None) == XS_ERR_NULL
+    assert f(Q, K, V, O, 1, 64, 1, 64, 3, 0.125, None) == XS_ERR_SHAPE
+    assert f(Q, K, V, O, 1, 64, 1, 96, 1, 0.125, None) == XS_ERR_UNSUPPORTED
+    assert f(Q, K, V, O, 1, 64, 1, 64, 1, math.inf, None) == XS_ERR_UNSUPPORTED
+    assert f(Q + 8, K, V, O, 1, 64, 1, 64, 1, 0.125, None) == XS_ERR_ALIGN
+    assert f(Q, K, V, Q, 1, 64, 1, 64, 1, 0.125, None) == XS_ERR_OVERLAP
+    assert "static scratch" in xs.xs_attn_strerror(XS_ERR_SCRATCH)
+
+
+def test_noalloc_scratch_covers_every_schedule_of_a_256_cu_device():
+    # the largest cut schedule: one workgroup per compute unit, two 256-row
+    # slots of fp32 O (D = 128) plus max and sum per row
+    text = open(_lib.HEADER_PATH).read()
+    size = int(text.split("#define XS_NOALLOC_SCRATCH_BYTES")[1].split()[0])
+    assert size == 2 * 256 * 256 * (4 * 128 + 8) == 65 * 2 ** 20
