@@ -123,15 +123,45 @@ def cpu_baseline(w, inp, target_s):
     t0 = time.perf_counter()
     oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, inp["scale"], inp["descales"], threads)
     dt = time.perf_counter() - t0
+    total = w.B * w.S * w.H
     return {
         "value": per_row * len(rows) / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "cpu_model": cpu_model(),
         "kind": "oracle",
-        "sample": f"{len(rows)} of {w.B * w.S * w.H} query rows of the {w.name} workload "
-                  f"(all {w.S} keys each), {dt:.1f} s wall, fp64",
+        "extrapolated": len(rows) < total,
+        "sample": f"{len(rows)} of {total} query rows ({100.0 * len(rows) / total:.2f} %) of the "
+                  f"{w.name} workload (all {w.S} keys each), {dt:.1f} s wall, fp64; the rate is "
+                  f"extrapolated linearly to the whole workload (rows are independent)",
     }
+
+
+def clock_stamp(stream):
+    """Enqueue one xs_clock_stamp on `stream`; returns (device tensor, wall-clock kHz)."""
+    import ctypes
+
+    from sequence_attention_amd import _lib
+
+    buf = torch.zeros(256, dtype=torch.int64, device="cuda:0")
+    khz = ctypes.c_int(0)
+    rc = _lib.lib().xs_clock_stamp(buf.data_ptr(), ctypes.byref(khz), stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"xs_clock_stamp failed: {rc}")
+    return buf, khz.value
+
+
+def average_sclk(a, b, khz):
+    """Average shader clock (GHz) between two stamps, per XCD and the mean."""
+    a, b = a.cpu().numpy().reshape(-1, 4), b.cpu().numpy().reshape(-1, 4)
+    per = {}
+    for x in sorted(set(a[:, 2].tolist()) & set(b[:, 2].tolist())):
+        ra, rb = a[a[:, 2] == x][0], b[b[:, 2] == x][0]
+        dt, dr = float(rb[0] - ra[0]), float(rb[1] - ra[1])
+        if dr > 0:
+            per[int(x)] = dt / dr * khz * 1e3 / 1e9
+    vals = list(per.values())
+    return (float(np.mean(vals)) if vals else None), per
 
 
 def epilogue_overhead(args):
@@ -356,6 +386,9 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+    # shader-clock stamps on the launch stream just outside the timed region: the
+    # average clock the box held over the timed steps
+    stamp_a, wall_khz = clock_stamp(stream)
     t_start.record(stream)
     for i in range(args.steps):
         if flush is not None:
@@ -367,8 +400,10 @@ def main():
         if pair is not None:
             pair[1].record(stream)
     t_end.record(stream)
+    stamp_b, _ = clock_stamp(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
+    sclk, sclk_per_xcd = average_sclk(stamp_a, stamp_b, wall_khz)
     launch_ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev.values()])
     ms_per_step = total_ms / args.steps
 
@@ -378,6 +413,41 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     achieved = flops / (float(launch_ms.mean()) * 1e-3) / 1e12
+
+    # The spec signature itself (xs_attn_fwd / xs_attn_fwd_fp8 by name: no
+    # workspace, so the schedule never cuts a tile), timed the same way after the
+    # product path's timed steps, on the same inputs.
+    out_ns = torch.empty_like(out)
+    sched_ns = xs.xs_attn_schedule(w.B, w.S, w.H, w.D, with_workspace=False)
+
+    def step_ns():
+        if w.dtype == "fp8":
+            dq, dk, dv = inp["descales"]
+            rc = xs.xs_attn_fwd_fp8(q, k, v, dq, dk, dv, out_ns, w.B, w.S, w.H, w.D, w.P,
+                                    inp["scale"], stream.cuda_stream)
+        else:
+            rc = xs.xs_attn_fwd(q, k, v, out_ns, w.B, w.S, w.H, w.D, w.P, inp["scale"],
+                                stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(xs.xs_attn_strerror(rc))
+
+    north_star = None
+    if args.in_layout == "bshd" and not args.cold:
+        for _ in range(min(args.warmup, 3)):
+            step_ns()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step_ns()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_ns = e0.elapsed_time(e1) / args.steps
+        north_star = {"entry": "xs_attn_fwd_fp8" if w.dtype == "fp8" else "xs_attn_fwd",
+                      "workspace_bytes": 0, "schedule": sched_ns, "steps": args.steps,
+                      "ms_per_call": round(ms_ns, 4),
+                      "value": round(flops / (ms_ns * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                      "equals_product_path_within": float((out_ns.float() - out.float()).abs().max())}
 
     check = None
     if not args.no_check:
@@ -403,7 +473,11 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0, sigma^2) inputs, shapes of the workload)",
         "config": {"workload": w.name, "B": w.B, "S": w.S, "H_local": w.H, "D": w.D, "P": w.P,
-                   "causal": False, "key_splits": nsplit, "workspace_bytes": ws_bytes,
+                   "causal": False,
+                   "entry": ("xs_attn_fwd_fp8_ex" if w.dtype == "fp8" else "xs_attn_fwd_ex")
+                            + (" with a caller workspace" if ws_bytes else " (no workspace)"),
+                   "schedule": xs.xs_attn_schedule(w.B, w.S, w.H, w.D, with_workspace=True),
+                   "key_splits": nsplit, "workspace_bytes": ws_bytes,
                    "caches": "evicted before every call (--cold)" if args.cold else "warm",
                    "launch": "hip graph replay" if args.graph else "direct",
                    "in_layout": args.in_layout},
@@ -418,6 +492,14 @@ def main():
                      "kernel": ("attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_fp8_kernel")
                                + (" + attn_combine_kernel" if nsplit > 1 else ""),
                      "flops_per_launch": flops},
+        "clock": {"sclk_ghz": None if sclk is None else round(sclk, 4),
+                  "per_xcd_ghz": {str(x): round(g, 4) for x, g in sclk_per_xcd.items()},
+                  "method": "s_memtime against s_memrealtime, stamped on the launch stream "
+                            "before and after the timed steps (xs_clock_stamp)",
+                  "peak_at_this_clock": None if sclk is None else round(peak * sclk / 2.4, 1),
+                  "frac_at_this_clock": None if sclk is None
+                  else round(achieved / (peak * sclk / 2.4), 4)},
+        "north_star_entry": north_star,
         "check": check,
     }
     if not args.no_cpu_baseline:

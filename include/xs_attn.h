@@ -178,6 +178,14 @@ size_t xs_attn_workspace_size(int B, int S, int H_local, int D);
  * on the current device (1 = no tile is cut); 0 for invalid sizes. */
 int xs_attn_split_count(int B, int S, int H_local, int D);
 
+/* The schedule the library runs for this shape on the current device, with
+ * (with_workspace != 0) or without a workspace: the number of workgroups, the
+ * rounds of whole tiles each takes first, and the most pieces any remainder
+ * tile is cut into (1 = none is cut).  Any output pointer may be NULL.  Returns
+ * XS_OK or XS_ERR_SHAPE (sizes < 1, D not 64 or 128).  No launch. */
+int xs_attn_schedule(int B, int S, int H_local, int D, int with_workspace, int *groups,
+                     int *whole_rounds, int *pieces);
+
 /* Static, never-NULL description of a status code. */
 const char *xs_attn_strerror(int status);
 

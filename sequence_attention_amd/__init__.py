@@ -33,6 +33,7 @@ from ._lib import XsAttnError, check, declared_functions, lib, strerror
 __all__ = ["fwd", "fwd_fp8", "unpack", "chunk", "workspace_size", "split_count", "xs_attn_fwd",
            "xs_attn_fwd_fp8", "xs_attn_fwd_ws", "xs_attn_fwd_fp8_ws", "xs_attn_fwd_ex",
            "xs_attn_fwd_fp8_ex", "xs_attn_workspace_size", "xs_attn_split_count",
+           "xs_attn_schedule", "xs_attn_fwd_noalloc",
            "xs_attn_strerror", "xs_attn_version", "XsAttnError", "default_scale",
            "LAYOUT_BSHD", "LAYOUT_CHUNKED"]
 
@@ -156,12 +157,29 @@ def xs_attn_fwd_fp8_ex(q8, k8, v8, in_layout, q_descale, k_descale, v_descale, o
                                     int(workspace_bytes), stream)
 
 
+def xs_attn_fwd_noalloc(q, k, v, out_packed, B, S, H_local, D, P, scale, stream) -> int:
+    ptr = lambda x: x.data_ptr() if isinstance(x, torch.Tensor) else x
+    return lib().xs_attn_fwd_noalloc(ptr(q), ptr(k), ptr(v), ptr(out_packed), B, S, H_local, D,
+                                     P, float(scale), stream)
+
+
 def xs_attn_workspace_size(B, S, H_local, D) -> int:
     return int(lib().xs_attn_workspace_size(B, S, H_local, D))
 
 
 def xs_attn_split_count(B, S, H_local, D) -> int:
     return int(lib().xs_attn_split_count(B, S, H_local, D))
+
+
+def xs_attn_schedule(B, S, H_local, D, with_workspace=True) -> dict:
+    """The schedule the library runs for this shape on the current device:
+    {"groups", "whole_rounds", "pieces"} (pieces = most pieces a tile is cut into)."""
+    import ctypes
+
+    g, r, p = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    check(lib().xs_attn_schedule(B, S, H_local, D, int(bool(with_workspace)), ctypes.byref(g),
+                                 ctypes.byref(r), ctypes.byref(p)))
+    return {"groups": g.value, "whole_rounds": r.value, "pieces": p.value}
 
 
 workspace_size = xs_attn_workspace_size

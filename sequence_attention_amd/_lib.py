@@ -8,7 +8,8 @@ import re
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libxs_attn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "xs_attn.h")
-HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_PKG), "include", "xs_burst_gap.h")]
+HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_PKG), "include", "xs_burst_gap.h"),
+                os.path.join(os.path.dirname(_PKG), "include", "xs_probe.h")]
 
 _lib = None
 
@@ -46,6 +47,9 @@ def lib() -> ctypes.CDLL:
         L.xs_attn_fwd_noalloc.restype = ci
         L.xs_attn_workspace_size.argtypes = [ci, ci, ci, ci]
         L.xs_attn_workspace_size.restype = sz
+        ip = ctypes.POINTER(ci)
+        L.xs_attn_schedule.argtypes = [ci, ci, ci, ci, ci, ip, ip, ip]
+        L.xs_attn_schedule.restype = ci
         L.xs_attn_split_count.argtypes = [ci, ci, ci, ci]
         L.xs_attn_split_count.restype = ci
         L.xs_attn_strerror.argtypes = [ci]
@@ -54,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.xs_attn_version.restype = ci
         L.xs_burst_gap.argtypes = [vp, sz, ci, sz, ci, ctypes.c_longlong, vp, vp]
         L.xs_burst_gap.restype = ci
+        L.xs_clock_stamp.argtypes = [vp, ctypes.POINTER(ci), vp]
+        L.xs_clock_stamp.restype = ci
         _lib = L
     return _lib
 

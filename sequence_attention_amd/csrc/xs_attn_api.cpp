@@ -346,6 +346,26 @@ size_t xs_attn_workspace_size(int B, int S, int H_local, int D) {
   return workspace_bytes(plan_for(B, S, H_local, D, true), D);
 }
 
+int xs_attn_schedule(int B, int S, int H_local, int D, int with_workspace, int* groups,
+                     int* whole_rounds, int* pieces) {
+  if (B < 1 || S < 1 || H_local < 1 || (D != 64 && D != 128)) return XS_ERR_SHAPE;
+  const Plan p = plan_for(B, S, H_local, D, with_workspace != 0);
+  if (groups) *groups = p.groups;
+  if (whole_rounds) *whole_rounds = p.dp;
+  if (pieces) {
+    int most = 1;
+    if (p.cut) {
+      const xs::Sched sch{p.units, p.groups, p.npair, p.dp};
+      for (long long t = 0; t < p.units / p.npair; ++t) {  // remainder tiles
+        const int n = sch.owner((t + 1) * p.npair - 1) - sch.owner(t * p.npair) + 1;
+        most = n > most ? n : most;
+      }
+    }
+    *pieces = most;
+  }
+  return XS_OK;
+}
+
 int xs_attn_split_count(int B, int S, int H_local, int D) {
   if (B < 1 || S < 1 || H_local < 1 || (D != 64 && D != 128)) return 0;
   const Plan p = plan_for(B, S, H_local, D, true);

@@ -23,7 +23,8 @@ def test_library_exports_every_declared_function():
     assert set(names) == {"xs_attn_fwd", "xs_attn_fwd_fp8", "xs_attn_fwd_ws", "xs_attn_fwd_fp8_ws",
                           "xs_attn_fwd_ex", "xs_attn_fwd_fp8_ex", "xs_attn_workspace_size",
                           "xs_attn_split_count", "xs_attn_strerror", "xs_attn_version",
-                          "xs_attn_fwd_noalloc", "xs_burst_gap"}
+                          "xs_attn_fwd_noalloc", "xs_attn_schedule", "xs_burst_gap",
+                          "xs_clock_stamp"}
     L = _lib.lib()
     for n in names:
         assert getattr(L, n) is not None
@@ -252,3 +253,19 @@ def test_noalloc_scratch_covers_every_schedule_of_a_256_cu_device():
     text = open(_lib.HEADER_PATH).read()
     size = int(text.split("#define XS_NOALLOC_SCRATCH_BYTES")[1].split()[0])
     assert size == 2 * 256 * 256 * (4 * 128 + 8) == 65 * 2 ** 20
+
+
+def test_schedule_query_is_consistent_with_split_count():
+    for shape in [(1, 4608, 3, 128), (1, 32768, 5, 128), (2, 1000, 3, 64), (1, 131072, 3, 128)]:
+        s = xs.xs_attn_schedule(*shape)
+        assert s["pieces"] == xs.split_count(*shape)
+        assert xs.xs_attn_schedule(*shape, with_workspace=False)["pieces"] == 1
+        assert s["groups"] >= 1 and s["whole_rounds"] >= 0
+    with pytest.raises(xs.XsAttnError):
+        xs.xs_attn_schedule(1, 64, 1, 96)
+
+
+def test_clock_stamp_validates_before_launch():
+    L = _lib.lib()
+    assert L.xs_clock_stamp(None, None, None) == -1
+    assert L.xs_clock_stamp(0x10000004, None, None) == -4
