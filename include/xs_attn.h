@@ -70,9 +70,11 @@ int xs_attn_fwd(const void *q, const void *k, const void *v, void *out_packed, i
  * accumulate into fp32, though a dot product's terms are not summed to full
  * fp32 precision (measured: up to about 2^-12.8 of scale * sum_d |q_d k_d| when
  * one product dominates); the probabilities enter the second contraction as
- * e4m3, and O is normalised by the sum of those quantised probabilities (a
- * constant V comes back exactly).  The output is bf16 [P][B][S/P][H_local][D]
- * as above.  Descales must be finite. */
+ * e4m3 codes read off their exponents (for p = 2^y, the code of 2^e (1 + f) with
+ * e + f = y, rounded to e4m3's three mantissa bits: within 12.8 % of a common
+ * multiple of p, no exponential is evaluated), and O is normalised by the sum of
+ * those quantised probabilities (a constant V comes back exactly).  The output
+ * is bf16 [P][B][S/P][H_local][D] as above.  Descales must be finite. */
 int xs_attn_fwd_fp8(const void *q8, const void *k8, const void *v8, float q_descale,
                     float k_descale, float v_descale, void *out_packed, int B, int S, int H_local,
                     int D, int P, float scale, void *stream);
@@ -154,10 +156,11 @@ int xs_attn_fwd_noalloc(const void *q, const void *k, const void *v, void *out_p
  *              ("Move the Query, Not the Cache", gist.science explainer, Methodik:
  *              the Route primitive).  It is the running max plus log of the row sum
  *              of the kernel's own softmax, taken over the fp32 probabilities
- *              before their rounding to bf16 / e4m3.  For fp8, O is then
- *              normalised by that fp32 sum too (it differs from the call without
- *              lse within the e4m3 rounding of P); for bf16, O is the same with
- *              or without lse.
+ *              before their rounding to bf16 / e4m3.  For fp8 with lse, P is
+ *              2^(s c - m) rounded to the nearest e4m3 and O is normalised by
+ *              that fp32 sum too (it differs from the call without lse within
+ *              the two encodings of P); for bf16, O is the same with or without
+ *              lse.
  * Every other argument, the workspace rules and the error behaviour are those of
  * xs_attn_fwd_ws / xs_attn_fwd_fp8_ws, which equal these calls with in_layout =
  * XS_LAYOUT_BSHD and lse = NULL. */

@@ -13,14 +13,18 @@
 //    keys of the block per 32-row d tile.
 //  * The descales fold into the exponent factor (c = scale*dq*dk*log2 e) and
 //    the epilogue (O * dv / l); the MFMAs see the raw e4m3 codes.
-//  * P is quantised to e4m3 (p <= 2^TAU = 256 < 448, so nothing saturates).
-//    Its accumulator registers already hold, per half-wave, the 32 keys
+//  * P enters P V as e4m3.  With the log-sum-exp output it is p = 2^(s c - m)
+//    rounded to e4m3 (p <= 2^TAU = 256 < 448, so nothing saturates); without
+//    it, the e4m3 code of each probability is read off its exponent by one FMA
+//    and one integer conversion, with no exponential (code4).
+//    The accumulator registers of the scores already hold, per half-wave, the
+//    32 keys
 //    {8g + 4h + i}; the V tile is stored in LDS with its rows permuted so that
 //    those keys are 32 consecutive rows, which ds_read_b64_tr_b8 turns into
 //    the V^T operand in the same order.
 //  * The row sums that normalise O are those of the quantised P, computed on
-//    the matrix core: one more MFMA per block with an all-ones A operand
-//    (the vector ALU, not the matrix core, bounds this kernel).  When the
+//    the matrix core: one more (16x16x128) MFMA per block with a selector A
+//    operand (the vector ALU, not the matrix core, bounds this kernel).  When the
 //    log-sum-exp output is requested, a second instantiation instead adds the
 //    fp32 probabilities before quantisation and normalises with that sum,
 //    which the log-sum-exp is defined by.  Having those sums at hand, it also
@@ -52,8 +56,14 @@ struct Fp8Cfg {
   static constexpr int NT = BN / 32;      // 32-key score tiles per block
   static constexpr int THREADS = 64 * NW;
   static constexpr int STAGES = 4;        // LDS ring depth for K and for V
-  static constexpr float TAU = 8.0f;      // lazy-rescale threshold (log2 units)
-  static constexpr float PMAX = 256.0f;   // 2^TAU: the largest probability kept
+  // lazy-rescale threshold (log2 units): every x = s c - m stays <= TAU
+  static constexpr float TAU = LSE_ ? 8.0f : 4.0f;
+  static constexpr float PMAX = LSE_ ? 256.0f : 16.0f;  // 2^TAU
+  // Without the log-sum-exp: P = 2^(x + SHIFT) as e4m3 codes (code4); the codes
+  // of x in [-6 - SHIFT, TAU] are normal e4m3 numbers and the largest, x = TAU,
+  // is code 126 (448), one below the NaN code.
+  static constexpr float SHIFT = 4.75f;
+  static constexpr float CODE_BIAS = 8.0f * (SHIFT + 7.0f);
   static_assert(LOADS <= NW, "one direct load per wave at most");
   static_assert(NT == 2, "the P^T operand layout assumes 64-key blocks");
 };
@@ -89,7 +99,8 @@ struct Scores8 {
 template <class C>
 struct Fp8State {
   f32x16 o[C::DT];
-  f32x16 lt;         // row sums of the quantised P (each register holds the lane's row sum)
+  f32x4 lt;          // row sums of the quantised P: lane n < 16 holds query n's in register 0 and
+                     // query n+16's in register 1 (16x16 layout of the row-sum MFMA)
   i32x8 qf[C::KS];
   u32x4 p0, p1;      // P^T operand: e4m3 probabilities of keys 0..31 and 32..63
   float m, alpha;
@@ -98,12 +109,23 @@ struct Fp8State {
   bool rescale;
 };
 
-// The A operand of the row-sum MFMA: every element e4m3 1.0 (0x38), so
-// lt += ONES P^T adds each query's sum of quantised probabilities to all 32
-// rows of its column.
-__device__ __forceinline__ i32x8 ones_e4m3() {
-  const int w = 0x38383838;
+// The A operand of the row-sum MFMA, lt += SEL P^T with the 16x16x128 e4m3
+// instruction (half the matrix-core time of a 32x32x64 one): each query's sum
+// of the quantised probabilities of the block, accumulated in lane n < 16,
+// register 0 (query n) and register 1 (query n+16).
+__device__ __forceinline__ i32x8 ones_e4m3(int lane) {
+  // A operand of v_mfma_f32_16x16x128_f8f6f4, lane l = row l%16, k = 32(l/16) ..
+  // 32(l/16)+31.  The P^T operand, read as that instruction's B operand, gives
+  // column n the bytes of lanes n, n+16, n+32, n+48: query n's keys 0..31, query
+  // n+16's keys 0..31, query n's keys 32..63, query n+16's keys 32..63.  Row 0
+  // (e4m3 1.0 on k groups 0 and 2) sums query n's, row 1 (groups 1 and 3) query
+  // n+16's; the other rows are zero.
+  const int row = lane & 15, g = lane >> 4;
+  const int w = (row == 0 && (g & 1) == 0) || (row == 1 && (g & 1) == 1) ? 0x38383838 : 0;
   return i32x8{w, w, w, w, w, w, w, w};
+}
+__device__ __forceinline__ f32x4 mfma_rowsum(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 template <class C>
@@ -165,7 +187,11 @@ __device__ __forceinline__ bool softmax_max8(Fp8State<C>& st, const Scores8<C>& 
 // probabilities (the sum the log-sum-exp is defined by).
 template <class C>
 __device__ __forceinline__ float row_sum(const Fp8State<C>& st) {
-  return C::LSE ? sum_halves(st.l32) : st.lt[0];
+  if (C::LSE) return sum_halves(st.l32);
+  const int lane = __lane_id(), src = (lane & 15) << 2;
+  const float r0 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(st.lt[0])));
+  const float r1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(st.lt[1])));
+  return (lane & 16) ? r1 : r0;
 }
 
 // O^T and the row sums *= alpha (rare: only when the running max moved).
@@ -176,7 +202,12 @@ __device__ __forceinline__ void rescale_o8(Fp8State<C>& st) {
     st.o[dt] *= st.alpha;
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (!C::LSE) st.lt *= st.alpha;
+  if (!C::LSE) {
+    // lane n < 16: register 0 is query n's (alpha of this lane), register 1 query n+16's
+    const int src = ((__lane_id() + 16) & 63) << 2;
+    st.lt[0] *= st.alpha;
+    st.lt[1] *= __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(st.alpha)));
+  }
   st.alpha = 1.0f;
   st.rescale = false;
 }
@@ -258,6 +289,54 @@ __device__ __forceinline__ uint32_t pack4(f32x4 p) {
   return pk;
 }
 
+// Without the log-sum-exp output the probabilities are not exponentiated: an
+// e4m3 number is 2^(E - 7) (1 + M/8) with code 8E + M, so for y = x + SHIFT
+// = e + f (e integer, f in [0, 1)) the code round(8 (y + 7)) encodes 2^e (1 + f)
+// -- 2^y interpolated linearly between powers of two (within +6.2 % of it), on
+// e4m3's three-bit mantissa grid (within half a step, 6.25 %).  One FMA gives
+// 8 (y + 7) = s (8c) + 8 (SHIFT + 7 - m) and one conversion rounds it to the
+// nearest integer byte (v_cvt_pk_u8_f32: round to nearest even, clamped to
+// [0, 255]).  The row sums that normalise O are those of the same codes' values
+// (row-sum MFMA), and the constant 2^SHIFT cancels in O / l.  x <= TAU = 4 keeps
+// every code <= 126; x < -10.75 gives subnormal codes and x below about -11.7
+// code 0: weights under 2^-10.75 of the row's largest key (which has x >= 0).
+// code4 computes the four codes as fp32 (pinned), pack_codes4 packs the bytes.
+template <class C>
+__device__ __forceinline__ f32x4 code4(const Scores8<C>& sc, int nt, int q, float c8, float bias) {
+  float t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t[i] = __builtin_fmaf(sc.s[nt][4 * q + i], c8, bias);
+    pin(t[i]);
+  }
+  return f32x4{t[0], t[1], t[2], t[3]};
+}
+__device__ __forceinline__ uint32_t pack_codes4(f32x4 t) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(t[0], 0, 0u);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(t[1], 1, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(t[2], 2, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(t[3], 3, w);
+  pin(w);
+  return w;
+}
+// The instantiation's form of the probabilities: exp4/pack4 with the
+// log-sum-exp (factors (a, b) = (c, -m)), code4/pack_codes4 without it
+// ((a, b) = (8c, 8(-m) + CODE_BIAS)).
+template <class C>
+__device__ __forceinline__ float prob_a(float c) { return C::LSE ? c : 8.0f * c; }
+template <class C>
+__device__ __forceinline__ float prob_b(float neg_m) { return C::LSE ? neg_m : 8.0f * neg_m + C::CODE_BIAS; }
+template <class C>
+__device__ __forceinline__ f32x4 prob4(const Scores8<C>& sc, int nt, int q, float a, float b,
+                                       float& lsum) {
+  if (C::LSE) return exp4<C>(sc, nt, q, a, b, lsum);
+  return code4<C>(sc, nt, q, a, b);
+}
+template <class C>
+__device__ __forceinline__ uint32_t packp4(f32x4 p) {
+  return C::LSE ? pack4(p) : pack_codes4(p);
+}
+
 // Probabilities of all 32 keys of tile nt (prologue and tail, not pipelined).
 template <class C>
 __device__ __forceinline__ void exp_tile8(Fp8State<C>& st, const Scores8<C>& sc, int nt, float c,
@@ -266,7 +345,8 @@ __device__ __forceinline__ void exp_tile8(Fp8State<C>& st, const Scores8<C>& sc,
   float lsum = st.l32;
   uint32_t w[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) w[q] = pack4(exp4<C>(sc, nt, q, c, neg_m, lsum));
+  for (int q = 0; q < 4; ++q)
+    w[q] = packp4<C>(prob4<C>(sc, nt, q, prob_a<C>(c), prob_b<C>(neg_m), lsum));
   st.l32 = lsum;
   out = u32x4{w[0], w[1], w[2], w[3]};
 }
@@ -288,6 +368,7 @@ __device__ __forceinline__ void step_a8(Scores8<C>& nxt, const Scores8<C>& cur, 
     return __builtin_bit_cast(i32x8, (u32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}));
   };
   const float neg_m = -st.m;
+  const float pa = prob_a<C>(c), pb = prob_b<C>(neg_m);
   float lsum = st.l32;
   uint32_t w[4];
   f32x4 pe[4];
@@ -301,15 +382,15 @@ __device__ __forceinline__ void step_a8(Scores8<C>& nxt, const Scores8<C>& cur, 
     nxt.s[nt] = mfma_fp8(kf[f % R], st.qf[t], t == 0 ? f32x16{} : nxt.s[nt]);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      if (f > 0 && q * NF / 4 == f - 1) w[q] = pack4(pe[q]);
+      if (f > 0 && q * NF / 4 == f - 1) w[q] = packp4<C>(pe[q]);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      if (q * NF / 4 == f) pe[q] = exp4<C>(cur, 1, q, c, neg_m, lsum);
+      if (q * NF / 4 == f) pe[q] = prob4<C>(cur, 1, q, pa, pb, lsum);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    if (q * NF / 4 == NF - 1) w[q] = pack4(pe[q]);
+    if (q * NF / 4 == NF - 1) w[q] = packp4<C>(pe[q]);
   st.l32 = lsum;
   st.p1 = u32x4{w[0], w[1], w[2], w[3]};
   keep(st.p1);
@@ -354,7 +435,7 @@ __device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
         i32x8, (u32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]}));
   };
   float mx = nxt.s[0][0];
-  float neg_m = 0.0f, lsum = 0.0f;
+  float neg_m = 0.0f, lsum = 0.0f, pa = 0.0f, pb = 0.0f;
   uint32_t w[4];
   f32x4 pe[4];
   i32x8 vf[R];
@@ -364,7 +445,7 @@ __device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
   for (int f = 0; f < NF; ++f) {
     if (f + LEAD < NF) vf[(f + LEAD) % R] = vread(f + LEAD);
     st.o[f] = mfma_fp8(vf[f % R], pf, st.o[f]);
-    if (!C::LSE && f == NF - 1) st.lt = mfma_fp8(ones, pf, st.lt);
+    if (!C::LSE && f == NF - 1) st.lt = mfma_rowsum(ones, pf, st.lt);
     if (f < HALF) {
       // Without the log-sum-exp: the next block's row max and the lazy move of
       // the running max.  With it, the max is not taken here: the fp32 row sums
@@ -391,22 +472,24 @@ __device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
           }
         }
         neg_m = -st.m;
+        pa = prob_a<C>(c);
+        pb = prob_b<C>(neg_m);
         lsum = st.l32;
         if (C::LSE) st.lb = st.l32;
       }
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (f > HALF && q * HALF / 4 == f - 1 - HALF) w[q] = pack4(pe[q]);
+        if (f > HALF && q * HALF / 4 == f - 1 - HALF) w[q] = packp4<C>(pe[q]);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (q * HALF / 4 == f - HALF) pe[q] = exp4<C>(nxt, 0, q, c, neg_m, lsum);
+        if (q * HALF / 4 == f - HALF) pe[q] = prob4<C>(nxt, 0, q, pa, pb, lsum);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    if (q * HALF / 4 == NF - 1 - HALF) w[q] = pack4(pe[q]);
+    if (q * HALF / 4 == NF - 1 - HALF) w[q] = packp4<C>(pe[q]);
   st.l32 = lsum;
   st.p0 = u32x4{w[0], w[1], w[2], w[3]};
   keep(st.p0);
@@ -433,7 +516,7 @@ __device__ __forceinline__ void pv_only8(Fp8State<C>& st, const uint8_t XS_LDS* 
     st.o[dt] = mfma_fp8(vf, pf, st.o[dt]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (!C::LSE) st.lt = mfma_fp8(ones, pf, st.lt);
+  if (!C::LSE) st.lt = mfma_rowsum(ones, pf, st.lt);
 }
 
 // Takes the next piece of the walk and issues its first loads: K of blocks jb,
@@ -509,7 +592,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
   const LdsOffs8<C> off = lds_offsets8<C>(lane);
   // the row-sum MFMA's constant operand, held in registers for the whole kernel
   // (opaque, so the compiler does not rebuild it before every use)
-  i32x8 ones = ones_e4m3();
+  i32x8 ones = ones_e4m3(lane);
   asm volatile("" : "+v"(ones));
 
   const Sched sch{a.units, a.groups, a.npair, a.dp};
@@ -527,7 +610,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
     const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
 
     st.m = -INFINITY;
-    st.lt = f32x16{};
+    st.lt = f32x4{};
     st.l32 = 0.0f;
     st.alpha = 1.0f;
     st.rescale = false;

@@ -65,6 +65,44 @@ def f64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
+# Per-element rounding bounds of the fp8 path, from its two encodings of P.
+#  * With the log-sum-exp output, P is 2^(s c - m) rounded to e4m3 (unit roundoff
+#    u = 2^-4 for normal values, absolute 2^-10 below 2^-6) and O is normalised by
+#    the fp32 sum of the unrounded values: |O' - O| <= u / (1 - u) (sum_j w_j |v_j|
+#    + |O|) + 2^-8 |O| (bf16 output) + 2^-9 max|v| (weights in the subnormal range).
+#  * Without it, P is the e4m3 code round(8 (y + 7)) of y = s c - m + 4.75: the
+#    value 2^e (1 + f) (e + f = y) is 2^y times a factor in [1, 1.0614], and the
+#    rounding of the code moves it by at most half a mantissa step (1/16 of it),
+#    so p'_j = K 2^(y_j) g_j with g_j in [a, b] = [15/16, 1.0614 * 17/16], and O is
+#    normalised by the sum of the same p'_j: O' - O = sum_j w_j (g_j - g) v_j / g
+#    with g = sum_j w_j g_j in [a, b], so |O' - O| <= (b - a)/a sum_j w_j |v_j|.
+#    Keys more than 10.75 octaves below the row's largest score are subnormal or
+#    zero codes: their error is at most twice their share, 2 sum_(small j) w_j |v_j|.
+#    Plus 2^-8 |O| for the bf16 output.
+CODE_SPREAD = (1.0614 * 17 / 16 - 15 / 16) / (15 / 16)
+
+
+def fp8_bounds(inp, P, scale):
+    """(bound with the log-sum-exp output, bound without it), both [P][B][T][H][D]."""
+    dq, dk, dv = inp["descales"]
+    qf = inp["q"].to(torch.float64) * dq
+    kf = inp["k"].to(torch.float64) * dk
+    vabs = inp["v"].to(torch.float64).abs() * dv
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, scale, inp["descales"])
+    ref_abs = oracle.attention_packed(qf, kf, vabs, P, scale)  # sum_j w_j |v_j|
+    # keys below 2^-10.75 of the row's largest weight (softmax weights in fp64)
+    s = torch.matmul(qf.permute(0, 2, 1, 3), kf.permute(0, 2, 3, 1).contiguous()) * scale
+    w = torch.exp(s - s.amax(-1, keepdim=True))  # [B][H][S][S]
+    small = (w < 2.0 ** -10.75).to(torch.float64)
+    sub = torch.matmul(w * small, vabs.permute(0, 2, 1, 3).contiguous()) / w.sum(-1, keepdim=True)
+    sub = oracle.pack(sub.permute(0, 2, 1, 3).numpy(), P)
+    u = 2.0 ** -4
+    with_lse = u / (1 - u) * (ref_abs + np.abs(ref)) + 2.0 ** -8 * np.abs(ref) \
+        + 2.0 ** -9 * float(vabs.max())
+    without = CODE_SPREAD * ref_abs + 2.0 ** -8 * np.abs(ref) + 2.0 * sub
+    return with_lse, without
+
+
 # ------------------------------------------------------------------ small shapes, every element
 SMALL = [
     # (B, S, H, D, P)
@@ -362,13 +400,7 @@ def test_running_max_moves_every_block(gpu, dtype, B, S, H, D, P):
     ref, ref_l = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, scale, inp["descales"],
                                          with_lse=True)
     if dtype == "fp8":
-        dq, dk, dv = inp["descales"]
-        vabs = inp["v"].to(torch.float64).abs() * dv
-        qf, kf = inp["q"].to(torch.float64) * dq, inp["k"].to(torch.float64) * dk
-        ref_abs = oracle.attention_packed(qf, kf, vabs, P, scale)
-        u = 2.0 ** -4
-        bound = u / (1 - u) * (ref_abs + np.abs(ref)) + 2.0 ** -8 * np.abs(ref) \
-            + 2.0 ** -9 * float(vabs.max())
+        bound_l, bound = fp8_bounds(inp, P, scale)
         q, k, v = to_gpu(inp, gpu)
         out = xs.fwd_fp8(q, k, v, inp["descales"], P, scale)
         out_l, lse = xs.fwd_fp8(q, k, v, inp["descales"], P, scale, lse=True)
@@ -376,13 +408,14 @@ def test_running_max_moves_every_block(gpu, dtype, B, S, H, D, P):
         ref_abs = oracle.attention_packed(inp["q"], inp["k"], inp["v"].abs(), P, scale)
         u = 2.0 ** -8
         bound = u * np.abs(ref) + u * (1 + u) * ref_abs + 1e-5
+        bound_l = bound
         q, k, v = to_gpu(inp, gpu)
         out = xs.fwd(q, k, v, P, scale)
         out_l, lse = xs.fwd(q, k, v, P, scale, lse=True)
     torch.cuda.synchronize()
-    for name, o in (("O", out), ("O with lse", out_l)):
+    for name, o, bd in (("O", out, bound), ("O with lse", out_l, bound_l)):
         got = f64(o)
-        worst = float((np.abs(got - ref) / bound).max())
+        worst = float((np.abs(got - ref) / bd).max())
         print(f"  {name}: worst error / bound = {worst:.3f}", flush=True)
         assert worst <= 1.0 and np.isfinite(got).all(), name
     d = np.abs(f64(lse) - ref_l)
@@ -462,30 +495,24 @@ def test_fp8_negative_scale(gpu):
 
 def test_fp8_peaked_softmax_within_rounding_bound(gpu):
     # At scale 0.25, D=64 a few keys dominate each row and the e4m3 rounding of P
-    # (unit roundoff u = 2^-4 for normal values, absolute 2^-10 below 2^-6) no
-    # longer averages out.  O is normalised by the sum of the same quantised
-    # probabilities, p^_j = p_j (1 + d_j): O' - O = (sum_j w_j d_j v_j - d O) /
-    # (1 + d) with d = sum_j w_j d_j, so per element |O' - O| <= u / (1 - u)
-    # (sum_j w_ij |v_j| + |O_i|); plus 2^-8 |O_i| for the bf16 output and
-    # 2^-9 max|v| for weights in the subnormal range.  The relative-L2 gate of
-    # the fp8 workloads still applies.
+    # no longer averages out: each output is held to the rounding bound of its
+    # encoding of P (fp8_bounds), with and without the log-sum-exp output.  The
+    # relative-L2 gate of the fp8 workloads still applies.
     w = workloads.custom(2, 333, 2, 64, 3, dtype="fp8", index=4200)
     inp = workloads.make_inputs(w)
     ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], 3, 0.25, inp["descales"])
-    vabs = inp["v"].to(torch.float64).abs().to(torch.float64)
-    # sum_j w_ij |v_j| from the oracle on |V| (same weights, dequantised |v|)
-    dq, dk, dv = inp["descales"]
-    qf = inp["q"].to(torch.float64) * dq
-    kf = inp["k"].to(torch.float64) * dk
-    ref_abs = oracle.attention_packed(qf, kf, vabs * dv, 3, 0.25)
-    got = f64(run(inp, 3, gpu, scale=0.25))
-    vmax = float(vabs.max()) * dv
-    u = 2.0 ** -4
-    bound = u / (1 - u) * (ref_abs + np.abs(ref)) + 2.0 ** -8 * np.abs(ref) + 2.0 ** -9 * vmax
-    worst = float((np.abs(got - ref) / bound).max())
-    print(f"  fp8 scale=0.25 worst error / bound = {worst:.3f}", flush=True)
-    assert worst <= 1.0
-    assert gate(got, ref, "fp8")[1] <= TOL["fp8"][1]
+    bound_l, bound = fp8_bounds(inp, 3, 0.25)
+    q, k, v = to_gpu(inp, gpu)
+    _say("fp8 peaked softmax, scale 0.25")
+    out = xs.fwd_fp8(q, k, v, inp["descales"], 3, 0.25)
+    out_l, _ = xs.fwd_fp8(q, k, v, inp["descales"], 3, 0.25, lse=True)
+    torch.cuda.synchronize()
+    for name, o, bd in (("O", out, bound), ("O with lse", out_l, bound_l)):
+        got = f64(o)
+        worst = float((np.abs(got - ref) / bd).max())
+        print(f"  fp8 scale=0.25 {name}: worst error / bound = {worst:.3f}", flush=True)
+        assert worst <= 1.0, name
+        assert gate(got, ref, "fp8")[1] <= TOL["fp8"][1], name
 
 
 def test_fp8_constant_v_gives_constant_output(gpu):
@@ -668,13 +695,8 @@ def test_fp8_running_max_moves_mid_block_with_lse(gpu, lo, hi):
     ref, ref_l = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, scale, inp["descales"],
                                          with_lse=True)
     dq, dk, dv = inp["descales"]
-    vabs = inp["v"].to(torch.float64).abs() * dv
     qf, kf = inp["q"].to(torch.float64) * dq, inp["k"].to(torch.float64) * dk
-    ref_abs = oracle.attention_packed(qf, kf, vabs, P, scale)
-    # rounding bound of the e4m3 probabilities (as in the rising-scores test)
-    u = 2.0 ** -4
-    bound = u / (1 - u) * (ref_abs + np.abs(ref)) + 2.0 ** -8 * np.abs(ref) \
-        + 2.0 ** -9 * float(vabs.max())
+    bound_l, bound = fp8_bounds(inp, P, scale)  # rounding bounds of the two encodings of P
     # log-sum-exp bar: 5e-3 plus the e4m3 matrix core's score accumulation
     sabs = torch.einsum("bqhd,bkhd->bhqk", qf.abs(), kf.abs()).amax(-1).numpy() * scale
     bar = 5e-3 + 2.0 ** -11 * sabs
@@ -683,9 +705,9 @@ def test_fp8_running_max_moves_mid_block_with_lse(gpu, lo, hi):
         out, lse = xs.fwd_fp8(q, k, v, inp["descales"], P, scale, lse=True, workspace=ws)
         plain = xs.fwd_fp8(q, k, v, inp["descales"], P, scale, workspace=ws)
         torch.cuda.synchronize()
-        for name, o in (("O with lse", out), ("O", plain)):
+        for name, o, bd in (("O with lse", out, bound_l), ("O", plain, bound)):
             got = f64(o)
-            worst = float((np.abs(got - ref) / bound).max())
+            worst = float((np.abs(got - ref) / bd).max())
             print(f"  workspace={ws} {name}: worst error / bound = {worst:.3f}", flush=True)
             assert np.isfinite(got).all() and worst <= 1.0, name
         d = np.abs(f64(lse) - ref_l)
