@@ -56,6 +56,46 @@ extern "C" {
 int xs_burst_gap(void *dst, size_t dst_bytes, int producers, size_t bytes, int nburst,
                  long long gap_cycles, unsigned long long *times, void *stream);
 
+/* The same measurement with the store pattern of the attention epilogue, whose
+ * bursts are output tiles: a producer is a workgroup of 512 threads (8 waves)
+ * owning one tile of 256 rows of row_bytes bytes each, row_pitch bytes apart (the
+ * rows of one head in the destination-ordered buffer are H_local*D*2 bytes
+ * apart).  Wave w writes rows 32w .. 32w+31 with row_bytes/16 store instructions
+ * of 8 bytes per lane: in instruction c, lane l writes bytes 16c + 8(l/32) .. +7
+ * of row 32w + l%32 -- 16 bytes into each of 32 rows per instruction, the order
+ * in which the attention kernels store a finished tile.  The bytes lane l writes
+ * are the uint32 words {producer, burst}.  A burst of producer p in ring region
+ * r = b % ring covers [(r*producers + p)*256*row_pitch, +256*row_pitch) of dst,
+ * ring = min(nburst, floor(dst_bytes / (producers*256*row_pitch))); bytes
+ * between rows are not touched.
+ *   producers   1 .. 4096;  nburst 1 .. 4096
+ *   row_bytes   16 .. 4096, a multiple of 16 (a tile's row: D * 2 bytes)
+ *   row_pitch   row_bytes .. 2^20, a multiple of 16
+ *   gap_cycles  as for xs_burst_gap
+ *   coupled     0: the recorded time of a burst is its issue time (first store to
+ *               issue of the last, no wait); nonzero: each wave waits for its
+ *               stores to complete (s_waitcnt vmcnt(0)) before its gap, and the
+ *               recorded time runs to that completion -- what a wave pays when it
+ *               next waits on its vector-memory counter, as the attention kernels
+ *               do before the next tile's first barrier (the wait for that tile's
+ *               K/V loads also covers the stores issued before it).
+ *   gap_src     NULL: the gap is gap_cycles of computation-free spinning.
+ *               Otherwise the gap is what a tile's key loop does to memory: each
+ *               wave issues gap_loads loads of 1 KiB (16 bytes per lane) from
+ *               gap_src, fresh addresses every burst (offsets wrap at
+ *               gap_src_bytes, a power of two >= 4096), and waits for them;
+ *               gap_loads 1 .. 65536, gap_src 16-byte aligned device memory.
+ *   times       device memory, 8-byte aligned, producers*8*(2*nburst+3) uint64:
+ *               for producer p and wave w the record at (p*8 + w)*(2*nburst+3)
+ *               holds each burst's time (issue, or completion when coupled),
+ *               then each gap's length, then the drain of the last burst, the
+ *               shader clocks of the whole run and its 100 MHz ticks.
+ * Returns 0 or an XS_BG_ERR_* code (validated before any HIP call). */
+int xs_burst_gap_tiles(void *dst, size_t dst_bytes, int producers, int row_bytes, int row_pitch,
+                       int nburst, long long gap_cycles, int coupled, const void *gap_src,
+                       size_t gap_src_bytes, int gap_loads, unsigned long long *times,
+                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,6 +58,9 @@ def lib() -> ctypes.CDLL:
         L.xs_attn_version.restype = ci
         L.xs_burst_gap.argtypes = [vp, sz, ci, sz, ci, ctypes.c_longlong, vp, vp]
         L.xs_burst_gap.restype = ci
+        L.xs_burst_gap_tiles.argtypes = [vp, sz, ci, ci, ci, ci, ctypes.c_longlong, ci, vp, sz, ci,
+                                         vp, vp]
+        L.xs_burst_gap_tiles.restype = ci
         L.xs_clock_stamp.argtypes = [vp, ctypes.POINTER(ci), vp]
         L.xs_clock_stamp.restype = ci
         _lib = L

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_function():
                           "xs_attn_fwd_ex", "xs_attn_fwd_fp8_ex", "xs_attn_workspace_size",
                           "xs_attn_split_count", "xs_attn_strerror", "xs_attn_version",
                           "xs_attn_fwd_noalloc", "xs_attn_schedule", "xs_burst_gap",
-                          "xs_clock_stamp"}
+                          "xs_burst_gap_tiles", "xs_clock_stamp"}
     L = _lib.lib()
     for n in names:
         assert getattr(L, n) is not None
@@ -233,6 +233,26 @@ def test_burst_gap_validates_before_any_launch():
         assert L.xs_burst_gap(D, 1 << 20, producers, nbytes, nburst, gap, T, None) == -2
     assert L.xs_burst_gap(D + 8, 1 << 20, 4, 4096, 2, 0, T, None) == -4
     assert L.xs_burst_gap(D, 1 << 20, 4, 4096, 2, 0, T + 4, None) == -4
+
+
+def test_burst_gap_tiles_validates_before_any_launch():
+    L = _lib.lib()
+    D, T = 0x60000000, 0x70000000
+    f = L.xs_burst_gap_tiles
+    assert f(0, 1 << 24, 4, 256, 1280, 2, 0, 0, None, 0, 0, T, None) == -1
+    assert f(D, 1 << 24, 4, 256, 1280, 2, 0, 0, None, 0, 0, 0, None) == -1
+    for producers, row_bytes, pitch, nburst, gap in (
+            (0, 256, 1280, 2, 0), (4097, 256, 1280, 2, 0), (4, 8, 1280, 2, 0),
+            (4, 250, 1280, 2, 0), (4, 8192, 8192, 2, 0), (4, 256, 128, 2, 0),
+            (4, 256, 1288, 2, 0), (4, 256, 1280, 0, 0), (4, 256, 1280, 2, -1),
+            (4, 256, 1280, 4096, 1 << 32), (64, 256, 1280, 2, 0)):   # last: dst too small
+        assert f(D, 1 << 24, producers, row_bytes, pitch, nburst, gap, 0, None, 0, 0, T, None) == -2
+    assert f(D + 8, 1 << 24, 4, 256, 1280, 2, 0, 0, None, 0, 0, T, None) == -4
+    assert f(D, 1 << 24, 4, 256, 1280, 2, 0, 0, None, 0, 0, T + 4, None) == -4
+    S = 0x50000000
+    for src_bytes, loads in ((1 << 20, 0), (1 << 20, 65537), (3000, 4), ((1 << 20) + 16, 4)):
+        assert f(D, 1 << 24, 4, 256, 1280, 2, 0, 0, S, src_bytes, loads, T, None) == -2
+    assert f(D, 1 << 24, 4, 256, 1280, 2, 0, 0, S + 8, 1 << 20, 4, T, None) == -4
 
 
 def test_noalloc_entry_validates_before_any_hip_call():

@@ -84,3 +84,34 @@ def test_timings_behave_like_issue_times(gpu):
     assert small.t_steady < idle.t_steady
     # the recorded gap is what was asked for (to the clock-rate estimate)
     assert idle.G == pytest.approx(4e-3 * 2.1e9 / idle.clock_hz, rel=1e-9)
+
+
+@pytest.mark.parametrize("producers,row_bytes,pitch,nburst,ring,coupled", [
+    (3, 256, 1280, 2, 1, 0), (5, 128, 384, 5, 2, 1), (2, 256, 256, 3, 3, 0), (4, 256, 768, 3, 2, 1)])
+def test_tile_pattern_writes_the_documented_rows(gpu, producers, row_bytes, pitch, nburst, ring,
+                                                 coupled):
+    # every row of every tile gets {producer, burst} in each 8-byte word of its
+    # row_bytes; the bytes between rows keep their fill
+    _say(f"burst-gap tiles P={producers} row={row_bytes} pitch={pitch} bursts={nburst} ring={ring}")
+    region = 256 * pitch
+    used = ring * producers * region
+    dst = torch.full((used + 4096,), 0xAB, dtype=torch.uint8, device=gpu)
+    times = torch.zeros(producers * 8 * (2 * nburst + 3), dtype=torch.int64, device=gpu)
+    src = torch.ones(1 << 16, dtype=torch.int32, device=gpu) if coupled else None  # 256 KiB
+    rc = lib().xs_burst_gap_tiles(dst.data_ptr(), used + region - 1, producers, row_bytes, pitch,
+                                  nburst, 1000, coupled, src.data_ptr() if coupled else None,
+                                  src.numel() * 4 if coupled else 0, 8, times.data_ptr(),
+                                  torch.cuda.current_stream(gpu).cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy()
+    assert np.all(got[used:] == 0xAB)
+    body = got[:used].reshape(ring, producers, 256, pitch)
+    words = body[..., :row_bytes].copy().view(np.uint32).reshape(ring, producers, 256, row_bytes // 8, 2)
+    for r in range(ring):
+        last = r + ring * ((nburst - 1 - r) // ring)
+        assert np.all(words[r, :, :, :, 0] == np.arange(producers, dtype=np.uint32)[:, None, None])
+        assert np.all(words[r, :, :, :, 1] == last)
+    assert np.all(body[..., row_bytes:] == 0xAB)
+    t = times.cpu().numpy().reshape(producers, 8, 2 * nburst + 3)
+    assert np.all(t[:, :, :2 * nburst] > 0) and np.all(t[:, :, 2 * nburst + 2] > 0)

@@ -63,3 +63,29 @@ def test_fit_needs_backpressure_free_runs():
     ts = V / 50e9
     with pytest.raises(ValueError):
         bg.fit(K, V, G, ts, ts)
+
+
+def test_completion_coupled_prediction_sums_every_round():
+    # T_c(V) = a + V / R for each round's burst of min(tiles, CUs) tiles
+    pc = bg.Coupled(a=2e-6, R=100e9, runs=[])
+    tile = 65536
+    # 640 tiles on 256 CUs: rounds of 256, 256 and 128 tiles
+    want = 3 * 2e-6 + (256 + 256 + 128) * tile / 100e9
+    assert abs(bg.predict_attention_coupled(pc, 640, 256, tile) - want) < 1e-12
+    # fewer tiles than CUs: one round
+    assert abs(bg.predict_attention_coupled(pc, 54, 256, tile) - (2e-6 + 54 * tile / 100e9)) < 1e-12
+
+
+def test_end_drain_prediction_by_hand():
+    end = bg.Linear(a=5e-6, R=50e9)
+    stretch = bg.Linear(a=0.0, R=600e9)
+    tile = 65536
+    # 640 tiles on 256 CUs: two full rounds stretch the loads after them, the
+    # last (128 tiles) drains at the end
+    want = 2 * (256 * tile / 600e9) + 5e-6 + 128 * tile / 50e9
+    assert bg.predict_attention_end(end, stretch, 640, 256, tile) == pytest.approx(want, rel=1e-12)
+    assert bg.predict_attention_end(end, stretch, 54, 256, tile) == pytest.approx(5e-6 + 54 * tile / 50e9)
+    f = bg.fit_linear([1e6, 2e6, 4e6], [5e-6 + 1e6 / 50e9, 5e-6 + 2e6 / 50e9, 5e-6 + 4e6 / 50e9])
+    assert f.a == pytest.approx(5e-6, rel=1e-6) and f.R == pytest.approx(50e9, rel=1e-6)
+    g = bg.fit_linear([1e6, 2e6], [1e6 / 600e9, 2e6 / 600e9], through_origin=True)
+    assert g.a == 0.0 and g.R == pytest.approx(600e9, rel=1e-9)
