@@ -54,6 +54,9 @@ def parse():
                     help="write a 512 MiB buffer before every timed call (evicts L2 and MALL) and "
                          "report the per-call event times instead of the back-to-back step time")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    ap.add_argument("--no-north-star", action="store_true",
+                    help="skip the extra timing of xs_attn_fwd / xs_attn_fwd_fp8 without workspace "
+                         "(for profiling runs whose dispatches should be the timed calls only)")
     ap.add_argument("--burst-gap", action="store_true",
                     help="characterise the Burst-Gap model with the microbenchmark (fine-grained "
                          "host memory as the remote link) and check it on the attention epilogue")
@@ -432,7 +435,7 @@ def main():
             raise RuntimeError(xs.xs_attn_strerror(rc))
 
     north_star = None
-    if args.in_layout == "bshd" and not args.cold:
+    if args.in_layout == "bshd" and not args.cold and not args.no_north_star:
         for _ in range(min(args.warmup, 3)):
             step_ns()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
