@@ -8,8 +8,7 @@ import re
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libxs_attn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "xs_attn.h")
-HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_PKG), "include", "xs_burst_gap.h"),
-                os.path.join(os.path.dirname(_PKG), "include", "xs_probe.h")]
+HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_PKG), "include", "xs_burst_gap.h")]
 
 _lib = None
 
@@ -61,8 +60,6 @@ def lib() -> ctypes.CDLL:
         L.xs_burst_gap_tiles.argtypes = [vp, sz, ci, ci, ci, ci, ctypes.c_longlong, ci, vp, sz, ci,
                                          vp, vp]
         L.xs_burst_gap_tiles.restype = ci
-        L.xs_clock_stamp.argtypes = [vp, ctypes.POINTER(ci), vp]
-        L.xs_clock_stamp.restype = ci
         _lib = L
     return _lib
 

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_function():
                           "xs_attn_fwd_ex", "xs_attn_fwd_fp8_ex", "xs_attn_workspace_size",
                           "xs_attn_split_count", "xs_attn_strerror", "xs_attn_version",
                           "xs_attn_fwd_noalloc", "xs_attn_schedule", "xs_burst_gap",
-                          "xs_burst_gap_tiles", "xs_clock_stamp"}
+                          "xs_burst_gap_tiles"}
     L = _lib.lib()
     for n in names:
         assert getattr(L, n) is not None
@@ -283,9 +283,3 @@ def test_schedule_query_is_consistent_with_split_count():
         assert s["groups"] >= 1 and s["whole_rounds"] >= 0
     with pytest.raises(xs.XsAttnError):
         xs.xs_attn_schedule(1, 64, 1, 96)
-
-
-def test_clock_stamp_validates_before_launch():
-    L = _lib.lib()
-    assert L.xs_clock_stamp(None, None, None) == -1
-    assert L.xs_clock_stamp(0x10000004, None, None) == -4
