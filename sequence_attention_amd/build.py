@@ -90,7 +90,8 @@ def resource_usage() -> str:
     demangle = subprocess.run(["c++filt"], input="\n".join(r["kernel"] for r in rows),
                               capture_output=True, text=True).stdout.splitlines()
     cols = [("VGPRs", "VGPRs"), ("AGPRs", "AGPRs"), ("TotalSGPRs", "SGPRs"),
-            ("VGPRs Spill", "VGPR spills"), ("ScratchSize", "scratch B/lane"),
+            ("VGPRs Spill", "VGPR spills"), ("SGPRs Spill", "SGPR spills"),
+            ("ScratchSize", "scratch B/lane"),
             ("LDS Size", "LDS B/block"), ("Occupancy", "waves/SIMD")]
     out = ["| kernel | " + " | ".join(c[1] for c in cols) + " |",
            "|---|" + "---|" * len(cols)]
