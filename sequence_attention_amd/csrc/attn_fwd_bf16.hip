@@ -29,16 +29,19 @@
 //    so the matrix core and the vector ALU work on different blocks at once;
 //    each pair's conversion runs one micro-step after its exponentials.
 //  * Online softmax in base 2: p = 2^(s*c - m), c = scale*log2(e) folded into
-//    one FMA per score.  The running max m is taken exactly for a piece's
-//    first and last blocks only; the other blocks' probabilities are computed
-//    with the current m and checked: when a lane's sum of a block's new p
-//    exceeds 2^TAU (as any single p above 2^TAU makes it), the block's exact
-//    max is taken, m moves if that max exceeds it by more than TAU (log2
-//    units), O is rescaled (a rare wave-uniform branch) and the block's p are
-//    recomputed.  So p <= 2^TAU always holds where p is used, as with a
-//    per-block max, without the max's vector work.  The row sum adds the
-//    fp32 p before their rounding to bf16 (plain adds: the vector ALU is the
-//    scarce unit here).
+//    one FMA per score.  First pass over a piece: m is the exact max of the
+//    piece's first block and stays there -- no checks, no rescale in the key
+//    loop; later probabilities may exceed 1, which floating point carries
+//    without loss.  If afterwards any lane's part of a row sum is above 2^40
+//    (or not finite), the workgroup runs the piece again with the lazy
+//    rescale: the running max is taken exactly for the piece's first and last
+//    blocks only; the other blocks' probabilities are computed with the
+//    current m and checked: when a lane's sum of a block's new p exceeds
+//    2^TAU (as any single p above 2^TAU makes it), the block's exact max is
+//    taken, m moves if that max exceeds it by more than TAU (log2 units), O is
+//    rescaled (a rare wave-uniform branch) and the block's p are recomputed.
+//    The row sum adds the fp32 p before their rounding to bf16 (plain adds:
+//    the vector ALU is the scarce unit here).
 //  * Epilogue: O/l rounded to bf16 and stored per query row at its
 //    destination-slice offset (p = s / T, s' = s - p*T).  Tile shapes and the
 //    reduction order never depend on P; only the store address does.
@@ -344,7 +347,7 @@ struct PairOrder {
 
 // Step 1: S^T of the next block from K stage KST || the first NE1 probability
 // pairs of the current block.  Each K fragment feeds the QT query sub-tiles.
-template <class C, int KST>
+template <class C, int KST, bool CHECK>
 __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16State<C>& st,
                                       const uint8_t XS_LDS* lds, const LdsOffs<C>& off, float c) {
   using PO = PairOrder<C>;
@@ -379,7 +382,7 @@ __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16
       if (f > 0 && k * NF / NE == f - 1) {
         const int qt = PO::qt(k), idx = PO::idx(k);
         st.pb[qt][idx / 4][idx % 4] = pack_sum(pe[k], lsum[qt]);
-        if (PO::last_of_first_half(k)) st.lh[qt] = lsum[qt];
+        if (CHECK && PO::last_of_first_half(k)) st.lh[qt] = lsum[qt];
       }
 #pragma unroll
     for (int k = 0; k < NE; ++k)
@@ -391,7 +394,7 @@ __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16
     if (k * NF / NE == NF - 1) {
       const int qt = PO::qt(k), idx = PO::idx(k);
       st.pb[qt][idx / 4][idx % 4] = pack_sum(pe[k], lsum[qt]);
-      if (PO::last_of_first_half(k)) st.lh[qt] = lsum[qt];
+      if (CHECK && PO::last_of_first_half(k)) st.lh[qt] = lsum[qt];
     }
   // Overflow check of the pairs just computed (the running max was not taken
   // for this block): a lane whose new probabilities sum to more than 2^TAU may
@@ -400,8 +403,8 @@ __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16
   // pending for step 2 and these pairs are recomputed with the new max.
   bool over = false;
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) over |= !(lsum[qt] - st.l[qt] <= C::PMAX);
-  if (__builtin_amdgcn_ballot_w64(over)) {
+  for (int qt = 0; qt < QT; ++qt) over |= CHECK && !(lsum[qt] - st.l[qt] <= C::PMAX);
+  if (CHECK && __builtin_amdgcn_ballot_w64(over)) {
     if (softmax_max<C>(st, cur, c)) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) lsum[qt] = st.l[qt];
@@ -425,7 +428,7 @@ __device__ __forceinline__ void step1(Scores<C>& nxt, const Scores<C>& cur, Bf16
 // Step 2: O^T = alpha O^T + V^T P^T from V stage VST; under the first half
 // (the first half of the block's keys) the remaining probability pairs, then
 // their overflow check before the second half uses them.
-template <class C, int VST>
+template <class C, int VST, bool CHECK>
 __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& cur,
                                       const uint8_t XS_LDS* lds, const LdsOffs<C>& off, float c) {
   using PO = PairOrder<C>;
@@ -435,7 +438,7 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& cur,
   constexpr int LEAD = XS_LEAD < NF ? XS_LEAD : NF;
   constexpr int R = LEAD + 1;
   constexpr int NE = PO::NP - PO::NE1;     // pairs left for this step
-  if (st.rescale) rescale_o<C>(st);
+  if (CHECK && st.rescale) rescale_o<C>(st);
   const uint8_t XS_LDS* vb = lds + VST * C::TILE;  // off.v holds the V region's base
   auto vaddr = [&](int f) { return vb + off.v[f % DT] + (f / DT) * 16 * ROWB; };
   float neg_m[QT], lsum[QT];
@@ -465,7 +468,7 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& cur,
         const int qt = PO::qt(PO::NE1 + k), idx = PO::idx(PO::NE1 + k);
         st.pb[qt][idx / 4][idx % 4] = pack_sum(pe[k], lsum[qt]);
       }
-    if (f == HALF) {
+    if (CHECK && f == HALF) {
       // Overflow check of this step's pairs, as in step 1.  The first half of
       // the block is already weighted into O: if the running max moves, O and
       // the sum through that half are rescaled now and the second half's pairs
@@ -510,14 +513,14 @@ __device__ __forceinline__ void step2(Bf16State<C>& st, const Scores<C>& cur,
 // O^T = alpha O^T + V^T P^T of the last block of a piece from the V stage at
 // byte offset stage_off (no next block to overlap with: its probabilities are
 // complete).
-template <class C>
+template <class C, bool CHECK>
 __device__ __forceinline__ void pv_only(Bf16State<C>& st, const uint8_t XS_LDS* lds,
                                         const LdsOffs<C>& off, uint32_t stage_off) {
   constexpr int QT = C::QT, DT = C::DT, ROWB = C::ROWB;
   constexpr int NF = 2 * C::NT * DT;
   constexpr int LEAD = XS_LEAD < NF ? XS_LEAD : NF;
   constexpr int R = LEAD + 1;
-  if (st.rescale) rescale_o<C>(st);
+  if (CHECK && st.rescale) rescale_o<C>(st);
   const uint8_t XS_LDS* vb = lds + stage_off;
   auto vaddr = [&](int f) { return vb + off.v[f % DT] + (f / DT) * 16 * ROWB; };
   u32x2 vlo[R], vhi[R];
@@ -539,15 +542,14 @@ __device__ __forceinline__ void pv_only(Bf16State<C>& st, const uint8_t XS_LDS* 
   }
 }
 
-// Takes the next piece of the walk and issues its first loads: K of blocks jb,
-// jb+1, jb+2 and V of blocks jb, jb+1 into ring stages 0, 1, 2 (stage of block
-// i = (i - jb) % 4).
+// Issues a piece's first loads: K of blocks jb, jb+1, jb+2 and V of blocks jb,
+// jb+1 into ring stages 0, 1, 2 (stage of block i = (i - jb) % 4).  The piece
+// is taken by value: its chunk cursors only move forward, and a pass over the
+// piece starts from the caller's unmoved copy.
 template <class C>
-__device__ __forceinline__ PieceAddr begin_piece(ShareWalk& walk, const Sched& sch, const AttnArgs& a,
-                                                 int nblk, uint32_t row_stride, uint8_t XS_LDS* lds,
-                                                 const uint32_t (&koff)[C::LPW],
-                                                 const uint32_t (&voff)[C::LPW], int wave, int& slot) {
-  PieceAddr pa = next_piece<C::BM, C::ROWB, C::BN>(walk, sch, a, nblk, row_stride, slot);
+__device__ __forceinline__ void piece_loads(PieceAddr pa, const AttnArgs& a, uint32_t row_stride,
+                                            uint8_t XS_LDS* lds, const uint32_t (&koff)[C::LPW],
+                                            const uint32_t (&voff)[C::LPW], int wave) {
   const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
   const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
   uint8_t XS_LDS* const vlds = lds + C::STAGES * C::TILE;
@@ -562,6 +564,16 @@ __device__ __forceinline__ PieceAddr begin_piece(ShareWalk& walk, const Sched& s
   if (pa.jb + 2 < pa.je)
     load_tile<C>(kbase, row_stride, (pa.jb + 2) * C::BN, pa.kcur.at(pa.jb + 2), a.S,
                  lds + 2 * C::TILE, koff, wave);
+}
+
+// Takes the next piece of the walk and issues its first loads.
+template <class C>
+__device__ __forceinline__ PieceAddr begin_piece(ShareWalk& walk, const Sched& sch, const AttnArgs& a,
+                                                 int nblk, uint32_t row_stride, uint8_t XS_LDS* lds,
+                                                 const uint32_t (&koff)[C::LPW],
+                                                 const uint32_t (&voff)[C::LPW], int wave, int& slot) {
+  PieceAddr pa = next_piece<C::BM, C::ROWB, C::BN>(walk, sch, a, nblk, row_stride, slot);
+  piece_loads<C>(pa, a, row_stride, lds, koff, voff, wave);
   return pa;
 }
 
@@ -582,6 +594,140 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[C::QT][C::KS], const AttnArgs
   }
 }
 
+// The fast pass's results are usable while every lane's part of every row sum is
+// at most 2^40 (false for inf and NaN as well): then no probability exceeded 2^40,
+// and O holds at most 2^40 times the largest |v|, far inside the fp32 range.
+template <class C>
+__device__ __forceinline__ bool sums_ok(const Bf16State<C>& st) {
+  bool ok = true;
+#pragma unroll
+  for (int qt = 0; qt < C::QT; ++qt) ok = ok && st.l[qt] <= 0x1p40f;
+  return ok;
+}
+
+// One pass over a piece's key blocks jb .. je-1, its first loads already issued.
+// CHECK = false (the fast pass): the running max is the piece's first block's
+// exact max and stays there, with no overflow checks; the probabilities of later
+// blocks may exceed 1 by any factor, which floating point carries without loss
+// until the sums leave the range that sums_ok() accepts.  CHECK = true: the lazy
+// rescale with the per-block overflow checks above.
+template <class C, bool CHECK>
+__device__ __forceinline__ void key_pass(Bf16State<C>& st, const AttnArgs& a, PieceAddr pa,
+                                         uint32_t row_stride, uint8_t XS_LDS* lds, const LdsOffs<C>& off,
+                                         const uint32_t (&koff)[C::LPW], const uint32_t (&voff)[C::LPW],
+                                         int wave, int lane, int nfull, float c) {
+  constexpr int QT = C::QT, DT = C::DT, BN = C::BN;
+  const int S = a.S;
+  const int jb = pa.jb, je = pa.je;
+  const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
+  const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
+  auto kbuf = [&](int s) { return lds + s * C::TILE; };
+  auto vbuf = [&](int s) { return lds + (C::STAGES + s) * C::TILE; };
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    st.m[qt] = -INFINITY;
+    st.l[qt] = 0.0f;
+    st.alpha[qt] = 1.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.o[qt][dt] = f32x16{};
+  }
+  st.rescale = false;
+
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // prologue: score block jb and take its max
+  Scores<C> sa, sb;
+  qk_block<C>(sa, st, kbuf(0), lane);
+  if (jb >= nfull) mask_tail<C>(sa, jb * BN, S, lane);
+  softmax_max<C>(st, sa, c);
+  if (!CHECK) {
+    // O is still zero: no rescale pending; later blocks use this max as is
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) st.alpha[qt] = 1.0f;
+    st.rescale = false;
+  }
+
+  // K/V blocks stream through a four-stage LDS ring (block i in stage
+  // (i - jb) % 4) with one barrier per two blocks: at the barrier before
+  // blocks i, i+1 (i - jb even) the loads of K_{i+1}, K_{i+2}, V_i, V_{i+1}
+  // (issued at the previous barrier) are complete and every wave is done
+  // with blocks i-2, i-1, so K_{i+3}, K_{i+4}, V_{i+2}, V_{i+3} go into the
+  // stages those blocks used.  Entering a step for block i: its scores are in
+  // one buffer with their max taken.  Four blocks per trip keep the stages
+  // and score buffers static.
+  auto ld_k = [&](int i, int stage) {
+    load_tile<C>(kbase, row_stride, i * BN, pa.kcur.at(i), S, kbuf(stage), koff, wave);
+  };
+  auto ld_v = [&](int i, int stage) {
+    load_tile<C>(vbase, row_stride, i * BN, pa.vcur.at(i), S, vbuf(stage), voff, wave);
+  };
+  int j = jb;
+  for (; j + 4 < je; j += 4) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    ld_k(j + 3, 3);
+    ld_k(j + 4, 0);
+    ld_v(j + 2, 2);
+    ld_v(j + 3, 3);
+    step1<C, 1, CHECK>(sb, sa, st, lds, off, c);  // block j
+    if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
+    step2<C, 0, CHECK>(st, sa, lds, off, c);
+    step1<C, 2, CHECK>(sa, sb, st, lds, off, c);  // block j+1
+    if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
+    step2<C, 1, CHECK>(st, sb, lds, off, c);
+
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (j + 5 < je) ld_k(j + 5, 1);
+    if (j + 6 < je) ld_k(j + 6, 2);
+    ld_v(j + 4, 0);
+    if (j + 5 < je) ld_v(j + 5, 1);
+    step1<C, 3, CHECK>(sb, sa, st, lds, off, c);  // block j+2
+    if (j + 3 >= nfull) mask_tail<C>(sb, (j + 3) * BN, S, lane);
+    step2<C, 2, CHECK>(st, sa, lds, off, c);
+    step1<C, 0, CHECK>(sa, sb, st, lds, off, c);  // block j+3
+    if (j + 4 >= nfull) mask_tail<C>(sa, (j + 4) * BN, S, lane);
+    step2<C, 3, CHECK>(st, sb, lds, off, c);
+  }
+  // the last one to four blocks j .. je-1 (stages 0..3, scores of block j in sa)
+  {
+    const int r = je - j;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (r > 3) ld_k(j + 3, 3);
+    if (r > 2) ld_v(j + 2, 2);
+    if (r > 3) ld_v(j + 3, 3);
+    if (r > 1) {
+      step1<C, 1, CHECK>(sb, sa, st, lds, off, c);  // block j
+      if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
+      step2<C, 0, CHECK>(st, sa, lds, off, c);
+    }
+    if (r > 2) {
+      step1<C, 2, CHECK>(sa, sb, st, lds, off, c);  // block j+1
+      if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
+      step2<C, 1, CHECK>(st, sb, lds, off, c);
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    if (r > 3) {
+      step1<C, 3, CHECK>(sb, sa, st, lds, off, c);  // block j+2
+      if (j + 3 >= nfull) mask_tail<C>(sb, (j + 3) * BN, S, lane);
+      step2<C, 2, CHECK>(st, sa, lds, off, c);
+    }
+    // the last block, j + r - 1: scores in sa when r is odd (its max not yet
+    // taken)
+    if (r & 1) {
+      if (CHECK) softmax_max<C>(st, sa, c);
+      softmax_exp<C>(st, sa, c);
+    } else {
+      if (CHECK) softmax_max<C>(st, sb, c);
+      softmax_exp<C>(st, sb, c);
+    }
+    pv_only<C, CHECK>(st, lds, off, (uint32_t)(r - 1) * C::TILE);
+  }
+}
+
 // Persistent workgroups: each walks its share of the schedule (attn_launch.h,
 // Sched) piece by piece: whole tiles in rounds, then an equal run of the
 // remaining tiles' (tile, key-block pair) units, so no workgroup idles at the
@@ -593,9 +739,8 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
   constexpr int QT = C::QT, DT = C::DT, BN = C::BN;
   // K stages 0..3 | V stages 0..3
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGES * C::TILE];
+  __shared__ int vote[C::NW];  // per wave: the fast pass must be redone
   uint8_t XS_LDS* const lds = (uint8_t XS_LDS*)smem;
-  auto kbuf = [&](int s) { return lds + s * C::TILE; };
-  auto vbuf = [&](int s) { return lds + (C::STAGES + s) * C::TILE; };
 
   const int S = a.S, H = a.H, T = a.T, B = a.B;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -621,106 +766,18 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
   load_q<C>(st.qf, a, pa, row_stride, qflip, wave, lane);
 
   for (;;) {
-    const int jb = pa.jb, je = pa.je, m0 = pa.m0;
-    const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
-    const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
-
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      st.m[qt] = -INFINITY;
-      st.l[qt] = 0.0f;
-      st.alpha[qt] = 1.0f;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) st.o[qt][dt] = f32x16{};
-    }
-    st.rescale = false;
-
-    wait_vmcnt<0>();
+    const int m0 = pa.m0;
+    // fast pass; if any wave's row sums left the accepted range, the whole
+    // workgroup runs the piece again with the checked lazy rescale
+    key_pass<C, false>(st, a, pa, row_stride, lds, off, koff, voff, wave, lane, nfull, c);
+    if (lane == 0) vote[wave] = __builtin_amdgcn_ballot_w64(!sums_ok<C>(st)) != 0;
     __syncthreads();
-
-    // prologue: score block jb and take its max
-    Scores<C> sa, sb;
-    qk_block<C>(sa, st, kbuf(0), lane);
-    if (jb >= nfull) mask_tail<C>(sa, jb * BN, S, lane);
-    softmax_max<C>(st, sa, c);
-
-    // K/V blocks stream through a four-stage LDS ring (block i in stage
-    // (i - jb) % 4) with one barrier per two blocks: at the barrier before
-    // blocks i, i+1 (i - jb even) the loads of K_{i+1}, K_{i+2}, V_i, V_{i+1}
-    // (issued at the previous barrier) are complete and every wave is done
-    // with blocks i-2, i-1, so K_{i+3}, K_{i+4}, V_{i+2}, V_{i+3} go into the
-    // stages those blocks used.  Entering a step for block i: its scores are in
-    // one buffer with their max taken.  Four blocks per trip keep the stages
-    // and score buffers static.
-    auto ld_k = [&](int i, int stage) {
-      load_tile<C>(kbase, row_stride, i * BN, pa.kcur.at(i), S, kbuf(stage), koff, wave);
-    };
-    auto ld_v = [&](int i, int stage) {
-      load_tile<C>(vbase, row_stride, i * BN, pa.vcur.at(i), S, vbuf(stage), voff, wave);
-    };
-    int j = jb;
-    for (; j + 4 < je; j += 4) {
-      wait_vmcnt<0>();
-      __syncthreads();
-      ld_k(j + 3, 3);
-      ld_k(j + 4, 0);
-      ld_v(j + 2, 2);
-      ld_v(j + 3, 3);
-      step1<C, 1>(sb, sa, st, lds, off, c);  // block j
-      if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
-      step2<C, 0>(st, sa, lds, off, c);
-      step1<C, 2>(sa, sb, st, lds, off, c);  // block j+1
-      if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
-      step2<C, 1>(st, sb, lds, off, c);
-
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (j + 5 < je) ld_k(j + 5, 1);
-      if (j + 6 < je) ld_k(j + 6, 2);
-      ld_v(j + 4, 0);
-      if (j + 5 < je) ld_v(j + 5, 1);
-      step1<C, 3>(sb, sa, st, lds, off, c);  // block j+2
-      if (j + 3 >= nfull) mask_tail<C>(sb, (j + 3) * BN, S, lane);
-      step2<C, 2>(st, sa, lds, off, c);
-      step1<C, 0>(sa, sb, st, lds, off, c);  // block j+3
-      if (j + 4 >= nfull) mask_tail<C>(sa, (j + 4) * BN, S, lane);
-      step2<C, 3>(st, sb, lds, off, c);
-    }
-    // the last one to four blocks j .. je-1 (stages 0..3, scores of block j in sa)
-    {
-      const int r = je - j;
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (r > 3) ld_k(j + 3, 3);
-      if (r > 2) ld_v(j + 2, 2);
-      if (r > 3) ld_v(j + 3, 3);
-      if (r > 1) {
-        step1<C, 1>(sb, sa, st, lds, off, c);  // block j
-        if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
-        step2<C, 0>(st, sa, lds, off, c);
-      }
-      if (r > 2) {
-        step1<C, 2>(sa, sb, st, lds, off, c);  // block j+1
-        if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
-        step2<C, 1>(st, sb, lds, off, c);
-        wait_vmcnt<0>();
-        __syncthreads();
-      }
-      if (r > 3) {
-        step1<C, 3>(sb, sa, st, lds, off, c);  // block j+2
-        if (j + 3 >= nfull) mask_tail<C>(sb, (j + 3) * BN, S, lane);
-        step2<C, 2>(st, sa, lds, off, c);
-      }
-      // the last block, j + r - 1: scores in sa when r is odd (its max not yet
-      // taken)
-      if (r & 1) {
-        softmax_max<C>(st, sa, c);
-        softmax_exp<C>(st, sa, c);
-      } else {
-        softmax_max<C>(st, sb, c);
-        softmax_exp<C>(st, sb, c);
-      }
-      pv_only<C>(st, lds, off, (uint32_t)(r - 1) * C::TILE);
+    bool redo = false;
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) redo |= vote[w] != 0;
+    if (redo) {
+      piece_loads<C>(pa, a, row_stride, lds, koff, voff, wave);
+      key_pass<C, true>(st, a, pa, row_stride, lds, off, koff, voff, wave, lane, nfull, c);
     }
 
     // ---- next piece: request its first K/V blocks and its queries before

@@ -10,6 +10,8 @@ and by properties that hold at any size; tests/test_parity_full_gpu.py checks
 the video and fp8 shares on every element and the long share on three rows of
 every query tile.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -346,6 +348,46 @@ def _rising_scores(B, S, H, D, dtype, index):
         inp["q"][..., 0] = 1.0
         inp["k"][..., 0] = torch.arange(S, dtype=torch.float32).view(1, S, 1).to(torch.bfloat16)
     return w, inp
+
+
+def _sloped_scores(B, S, H, D, rise, index):
+    """bf16 inputs whose scores rise linearly along the keys by `rise` log2 units
+    over the whole sequence (q[..., 0] = 1, k[:, j, :, 0] = j * slope): the kernel's
+    first pass keeps the first block's max, so its probabilities grow to about
+    2^rise; below 2^40 that pass's result stands, above it the piece is computed
+    again with the lazy rescale."""
+    w = workloads.custom(B, S, H, D, 1, index=index)
+    inp = workloads.make_inputs(w)
+    slope = rise / ((S - 1) * inp["scale"] * math.log2(math.e))
+    inp["q"][..., 0] = 1.0
+    inp["k"][..., 0] = (torch.arange(S, dtype=torch.float32) * slope).view(1, S, 1).to(torch.bfloat16)
+    return w, inp
+
+
+@pytest.mark.parametrize("rise", [12.0, 30.0, 38.0, 44.0, 90.0, 200.0])
+@pytest.mark.parametrize("B,S,H,D,P", [(1, 1000, 2, 64, 4), (1, 2056, 2, 128, 8)])
+def test_scores_rising_across_the_fast_pass_limit(gpu, rise, B, S, H, D, P):
+    # Rows whose running max rises by `rise` log2 units: below 2^40 the first
+    # pass's probabilities (up to 2^rise) are used as they are, above it the
+    # piece is redone with the lazy rescale; both must match the oracle, with and
+    # without the split-key workspace (cut pieces see a smaller rise each).
+    w, inp = _sloped_scores(B, S, H, D, rise, 4700 + S + D + int(rise))
+    scale = inp["scale"]
+    _say(f"sloped scores rise={rise} B={B} S={S} H={H} D={D} P={P}")
+    ref, ref_l = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, scale, with_lse=True)
+    ref_abs = oracle.attention_packed(inp["q"], inp["k"], inp["v"].abs(), P, scale)
+    u = 2.0 ** -8
+    bound = u * np.abs(ref) + u * (1 + u) * ref_abs + 1e-5
+    q, k, v = to_gpu(inp, gpu)
+    for ws in (None, "auto"):
+        out_l, lse = xs.fwd(q, k, v, P, scale, lse=True, workspace=ws)
+        torch.cuda.synchronize()
+        got = f64(out_l)
+        worst = float((np.abs(got - ref) / bound).max())
+        d = np.abs(f64(lse) - ref_l)
+        print(f"  workspace={ws}: worst error / bound = {worst:.3f}, lse max_abs={d.max():.3e}", flush=True)
+        assert worst <= 1.0 and np.isfinite(got).all()
+        assert d.max() <= 5e-3
 
 
 def _mid_block_spikes(B, S, H, D, index):
