@@ -15,6 +15,7 @@ of the same workload on this host's cores.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -66,6 +67,10 @@ def parse():
     ap.add_argument("--torch-sdpa", action="store_true",
                     help="context: time torch's own fused attention (scaled_dot_product_attention, "
                          "flash backend only) on the same inputs next to this library's call")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of the benchmark, run the matrix-core ceiling probes "
+                         "(xs_mfma_ceiling: MFMA rate next to LDS operand reads and softmax "
+                         "vector work, one and two waves per SIMD)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -82,6 +87,50 @@ def copy_calibration(mib, steps):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read": n * 4, "bytes_written": n * 4,
                                            "launches": steps}}), flush=True)
+
+
+CEILING_MODES = ["mfma only", "1 KiB ds_read_b128 per MFMA", "0.5 KiB ds_read_b128 per MFMA",
+                 "1 KiB ds_read_b64_tr_b16 per MFMA",
+                 "softmax work per MFMA (fma, exp, add, half a bf16 pack)",
+                 "softmax work + 1 KiB ds_read_b128 per MFMA (32 query rows per wave)",
+                 "softmax work + 0.5 KiB ds_read_b128 per MFMA (64 query rows per wave)"]
+
+
+def ceilings(iters, reps=5):
+    """MFMA issue rate of each xs_mfma_ceiling mode against MFMA-only issue with the same
+    number of waves per SIMD (minimum time over `reps` launches after one warm-up)."""
+    from sequence_attention_amd import _lib
+
+    L = _lib.lib()
+    stream = torch.cuda.current_stream()
+    sink = torch.empty(1024 * 512, dtype=torch.float32, device="cuda:0")
+
+    def run(mode, waves):
+        best = None
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            _lib.check(L.xs_mfma_ceiling(mode, waves, iters, ctypes.c_void_p(sink.data_ptr()),
+                                          sink.numel() * 4, ctypes.c_void_p(stream.cuda_stream)))
+            e1.record(stream)
+            e1.synchronize()
+            t = e0.elapsed_time(e1)
+            if r and (best is None or t < best):
+                best = t
+        return best
+
+    res = {}
+    for waves in (2, 1):
+        base = run(0, waves)
+        mfma_per_simd = 1024 / 256 * waves * 16 * iters
+        rows = []
+        for mode, name in enumerate(CEILING_MODES):
+            t = base if mode == 0 else run(mode, waves)
+            rows.append({"mode": mode, "stream": name, "ms": round(t, 4),
+                         "mfma_rate_vs_mfma_only": round(base / t, 4)})
+        res[f"{waves}_waves_per_simd"] = {
+            "mfma_only_clock_ghz": round(mfma_per_simd * 32 / (base * 1e-3) / 1e9, 3), "modes": rows}
+    return res
 
 
 def recorded_traffic(kernel_tag, workload):
@@ -311,6 +360,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.ceilings:
+        print(json.dumps({"metric": "mfma_ceilings", "n_gpus": 1, "iters": 2048,
+                          **ceilings(2048)}), flush=True)
         return
     if args.epilogue_overhead:
         epilogue_overhead(args)

@@ -1,0 +1,65 @@
+/*
+ * xs_ceiling.h -- C ABI of the matrix-core ceiling probes of the same library
+ * (libxs_attn.so): how fast one gfx950 SIMD issues v_mfma_f32_32x32x16_bf16
+ * while it also streams the LDS operand reads and the vector work that the
+ * attention kernels put next to each MFMA.
+ *
+ * The attention forward (FlashAttention over the full sequence of this GPU's
+ * Ulysses share: X-Stage paper, gist.science explainer, "Zentrale Beitraege",
+ * "FlashAttention-A2A (Piggybacking)") is bound by the matrix cores, but each
+ * MFMA of the bf16 kernel needs 1 KiB of operand data from LDS (32 query rows
+ * per wave) and about three vector instructions and one exponential of
+ * softmax work.  These probes measure the MFMA rate the chip sustains under
+ * each stream alone and under both, so the kernel's own MFMA-busy fraction
+ * can be read against them.
+ */
+#ifndef XS_CEILING_H
+#define XS_CEILING_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define XS_CEIL_MFMA 0      /* MFMAs only, four independent accumulators per wave */
+#define XS_CEIL_LDS_1K 1    /* + one 1 KiB ds_read_b128 per MFMA, read three MFMAs ahead */
+#define XS_CEIL_LDS_HALF 2  /* + one 1 KiB ds_read_b128 per two MFMAs (0.5 KiB per MFMA) */
+#define XS_CEIL_TR16_1K 3   /* + two 512-byte ds_read_b64_tr_b16 per MFMA, three MFMAs ahead */
+#define XS_CEIL_SOFTMAX 4   /* + the bf16 kernel's softmax work per MFMA: one v_fma_f32, one
+                               v_exp_f32, one v_add_f32 and half a v_cvt_pk_bf16_f32, no LDS */
+#define XS_CEIL_MIX 5       /* XS_CEIL_SOFTMAX + XS_CEIL_LDS_1K: the mix of 32 query rows per wave */
+#define XS_CEIL_MIX_HALF 6  /* XS_CEIL_SOFTMAX + XS_CEIL_LDS_HALF: the mix of 64 query rows per wave */
+#define XS_CEIL_MODES 7
+
+#define XS_CEIL_SINK_BYTES (1024u * 512u * 4u) /* smallest sink accepted */
+
+#define XS_CEIL_ERR_NULL (-1)   /* sink is NULL */
+#define XS_CEIL_ERR_ARG (-2)    /* mode, waves_per_simd or iters out of range */
+#define XS_CEIL_ERR_SIZE (-3)   /* sink_bytes below XS_CEIL_SINK_BYTES */
+#define XS_CEIL_ERR_ALIGN (-4)  /* sink not 4-byte aligned */
+#define XS_CEIL_ERR_LAUNCH (-5) /* the HIP launch reported an error */
+
+/* Launches one probe kernel: 1024 workgroups of 256*waves_per_simd threads (one
+ * workgroup per compute unit at a time, so each SIMD runs waves_per_simd waves),
+ * every wave issuing 16*iters MFMAs together with the mode's stream.  LDS
+ * addresses stay inside a 64 KiB array that each workgroup fills first; every
+ * other operand lives in registers.  Each thread stores one float into sink
+ * (thread t of workgroup g at index g*512 + t) so that none of the work is dead;
+ * the values carry no meaning.
+ *   mode            XS_CEIL_* (0 .. XS_CEIL_MODES-1)
+ *   waves_per_simd  1 or 2
+ *   iters           1 .. 2^20
+ *   sink            device memory, at least XS_CEIL_SINK_BYTES bytes, 4-byte aligned
+ *   stream          hipStream_t as void*, NULL = default stream; asynchronous:
+ *                   time it with events on the same stream.
+ * A run issues 1024/256 * waves_per_simd * 16 * iters MFMAs per SIMD (256
+ * compute units, 4 SIMDs each), 32 shader clocks each at full rate.
+ * Returns 0 or an XS_CEIL_ERR_* code (validated before any HIP call). */
+int xs_mfma_ceiling(int mode, int waves_per_simd, int iters, float *sink, size_t sink_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XS_CEILING_H */

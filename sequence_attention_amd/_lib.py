@@ -8,7 +8,8 @@ import re
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libxs_attn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "xs_attn.h")
-HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_PKG), "include", "xs_burst_gap.h")]
+HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_PKG), "include", "xs_burst_gap.h"),
+                os.path.join(os.path.dirname(_PKG), "include", "xs_ceiling.h")]
 
 _lib = None
 
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.xs_burst_gap_tiles.argtypes = [vp, sz, ci, ci, ci, ci, ctypes.c_longlong, ci, vp, sz, ci,
                                          vp, vp]
         L.xs_burst_gap_tiles.restype = ci
+        L.xs_mfma_ceiling.argtypes = [ci, ci, ci, vp, sz, vp]
+        L.xs_mfma_ceiling.restype = ci
         _lib = L
     return _lib
 

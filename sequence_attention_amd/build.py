@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libxs_attn.so")
 DEMO = os.path.join(PKG, "c_api_demo")  # host program using the C ABI alone
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["xs_attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "attn_combine.hip",
-           "burst_gap.hip"]
+           "burst_gap.hip", "ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

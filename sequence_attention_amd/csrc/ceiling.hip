@@ -1,0 +1,124 @@
+// ceiling.hip -- matrix-core ceiling probes: v_mfma_f32_32x32x16_bf16 issued
+// back to back next to the LDS operand reads and the softmax vector work of
+// the attention kernels (declared in xs_ceiling.h).
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "xs_ceiling.h"
+
+namespace xs {
+namespace {
+
+constexpr int kInner = 16;                    // MFMAs per loop trip
+constexpr int kLead = 3;                      // LDS reads issued this many MFMAs ahead
+constexpr int kGroups = 1024;
+
+// One trip's worth of a mode's extra stream is written out per MFMA; the
+// scheduling barrier after each MFMA and its slice keeps the interleave.
+template <int MODE, int THREADS>
+__global__ __launch_bounds__(THREADS, 1) void ceiling_kernel(float* sink, int iters) {
+  // 96 KiB: one workgroup per compute unit; reads stay below 68 KiB of it
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[96 * 1024];
+  uint8_t XS_LDS* lds = (uint8_t XS_LDS*)smem;
+  const int lane = threadIdx.x & 63;
+  for (uint32_t i = threadIdx.x * 4; i < sizeof(smem); i += THREADS * 4)
+    *(uint32_t XS_LDS*)(lds + i) = i * 2654435761u;
+  __syncthreads();
+
+  constexpr bool kPerMfma = MODE == XS_CEIL_LDS_1K || MODE == XS_CEIL_TR16_1K || MODE == XS_CEIL_MIX;
+  constexpr bool kHalf = MODE == XS_CEIL_LDS_HALF || MODE == XS_CEIL_MIX_HALF;
+  constexpr bool kSoftmax = MODE == XS_CEIL_SOFTMAX || MODE == XS_CEIL_MIX || MODE == XS_CEIL_MIX_HALF;
+  f32x16 acc[4] = {};
+  const u32x4 a = {lane * 3u, lane * 5u, 7u, 9u};
+  // softmax stand-in, as in the bf16 kernel: p = 2^(x c - m) of eight independent
+  // chains, their row sum, and the pairs rounded to bf16 as the next MFMAs' B operand
+  float z[8], lsum = 0.0f;
+  uint32_t pk[4] = {lane * 11u, 13u, 17u, 19u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = 0.5f + lane * 0.001f + 0.01f * i;
+  // one fragment per 1 KiB of a 16 KiB window per loop trip, the window moving by
+  // 16 KiB per trip over four positions: offsets are immediates within a trip
+  u32x4 frag[kLead + 1];
+  auto read = [&](const uint8_t XS_LDS* tb, int f) -> u32x4 {
+    if (MODE == XS_CEIL_TR16_1K) {
+      const u32x2 lo = lds_read_tr16(tb + f * 1024);
+      const u32x2 hi = lds_read_tr16(tb + f * 1024 + 512);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+    return lds_read_b128(tb + f * 1024);
+  };
+  const uint8_t XS_LDS* const lane_base = lds + (MODE == XS_CEIL_TR16_1K ? lane * 8 : lane * 16);
+  if (kPerMfma || kHalf)
+#pragma unroll
+    for (int k = 0; k < kLead; ++k) frag[k] = read(lane_base, k);
+
+  for (int it = 0; it < iters; ++it) {
+    const uint8_t XS_LDS* tb = lane_base + (it & 3) * 16384;
+#pragma unroll
+    for (int k = 0; k < kInner; ++k) {
+      u32x4 op = a;
+      if (kPerMfma) {
+        frag[(k + kLead) % (kLead + 1)] = read(tb, k + kLead);
+        op = frag[k % (kLead + 1)];
+      } else if (kHalf) {
+        if ((k & 1) == 0) frag[((k >> 1) + kLead) % (kLead + 1)] = read(tb, (k >> 1) + kLead);
+        op = frag[(k >> 1) % (kLead + 1)];
+      }
+      acc[k & 3] = mfma_bf16(op, u32x4{pk[0], pk[1], pk[2], pk[3]}, acc[k & 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kSoftmax) {
+        z[k & 7] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[k & 7], 0.5f, -0.4f));
+        lsum += z[k & 7];
+        if (k & 1) pk[(k >> 1) & 3] = pack_bf16(z[(k - 1) & 7], z[k & 7]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  float s = lsum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[q][r];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += z[i];
+  if (kPerMfma || kHalf)
+#pragma unroll
+    for (int k = 0; k <= kLead; ++k) s += (float)(frag[k][0] ^ frag[k][3]);
+  sink[blockIdx.x * 512 + threadIdx.x] = s;
+}
+
+template <int MODE>
+hipError_t launch_mode(int waves, float* sink, int iters, hipStream_t stream) {
+  if (waves == 1) {
+    hipLaunchKernelGGL((ceiling_kernel<MODE, 256>), dim3(kGroups), dim3(256), 0, stream, sink, iters);
+  } else {
+    hipLaunchKernelGGL((ceiling_kernel<MODE, 512>), dim3(kGroups), dim3(512), 0, stream, sink, iters);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace xs
+
+extern "C" int xs_mfma_ceiling(int mode, int waves_per_simd, int iters, float* sink, size_t sink_bytes,
+                               void* stream) {
+  using namespace xs;
+  if (!sink) return XS_CEIL_ERR_NULL;
+  if (mode < 0 || mode >= XS_CEIL_MODES || (waves_per_simd != 1 && waves_per_simd != 2) || iters < 1 ||
+      iters > (1 << 20))
+    return XS_CEIL_ERR_ARG;
+  if (sink_bytes < XS_CEIL_SINK_BYTES) return XS_CEIL_ERR_SIZE;
+  if ((uintptr_t)sink % 4) return XS_CEIL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  switch (mode) {
+    case XS_CEIL_MFMA: e = launch_mode<XS_CEIL_MFMA>(waves_per_simd, sink, iters, s); break;
+    case XS_CEIL_LDS_1K: e = launch_mode<XS_CEIL_LDS_1K>(waves_per_simd, sink, iters, s); break;
+    case XS_CEIL_LDS_HALF: e = launch_mode<XS_CEIL_LDS_HALF>(waves_per_simd, sink, iters, s); break;
+    case XS_CEIL_TR16_1K: e = launch_mode<XS_CEIL_TR16_1K>(waves_per_simd, sink, iters, s); break;
+    case XS_CEIL_SOFTMAX: e = launch_mode<XS_CEIL_SOFTMAX>(waves_per_simd, sink, iters, s); break;
+    case XS_CEIL_MIX: e = launch_mode<XS_CEIL_MIX>(waves_per_simd, sink, iters, s); break;
+    default: e = launch_mode<XS_CEIL_MIX_HALF>(waves_per_simd, sink, iters, s); break;
+  }
+  return e == hipSuccess ? 0 : XS_CEIL_ERR_LAUNCH;
+}

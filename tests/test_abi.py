@@ -24,7 +24,7 @@ def test_library_exports_every_declared_function():
                           "xs_attn_fwd_ex", "xs_attn_fwd_fp8_ex", "xs_attn_workspace_size",
                           "xs_attn_split_count", "xs_attn_strerror", "xs_attn_version",
                           "xs_attn_fwd_noalloc", "xs_attn_schedule", "xs_burst_gap",
-                          "xs_burst_gap_tiles"}
+                          "xs_burst_gap_tiles", "xs_mfma_ceiling"}
     L = _lib.lib()
     for n in names:
         assert getattr(L, n) is not None
@@ -253,6 +253,17 @@ def test_burst_gap_tiles_validates_before_any_launch():
     for src_bytes, loads in ((1 << 20, 0), (1 << 20, 65537), (3000, 4), ((1 << 20) + 16, 4)):
         assert f(D, 1 << 24, 4, 256, 1280, 2, 0, 0, S, src_bytes, loads, T, None) == -2
     assert f(D, 1 << 24, 4, 256, 1280, 2, 0, 0, S + 8, 1 << 20, 4, T, None) == -4
+
+
+def test_mfma_ceiling_validates_before_any_launch():
+    L = _lib.lib()
+    S, n = 0x60000000, 1024 * 512 * 4
+    assert L.xs_mfma_ceiling(0, 2, 16, None, n, None) == -1
+    for mode, waves, iters in ((-1, 2, 16), (7, 2, 16), (0, 0, 16), (0, 3, 16), (0, 2, 0),
+                               (0, 2, (1 << 20) + 1)):
+        assert L.xs_mfma_ceiling(mode, waves, iters, S, n, None) == -2
+    assert L.xs_mfma_ceiling(0, 2, 16, S, n - 4, None) == -3
+    assert L.xs_mfma_ceiling(0, 2, 16, S + 2, n, None) == -4
 
 
 def test_noalloc_entry_validates_before_any_hip_call():
