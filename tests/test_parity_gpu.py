@@ -365,7 +365,7 @@ def _sloped_scores(B, S, H, D, rise, index):
 
 
 @pytest.mark.parametrize("rise", [12.0, 30.0, 38.0, 44.0, 90.0, 200.0])
-@pytest.mark.parametrize("B,S,H,D,P", [(1, 1000, 2, 64, 4), (1, 2056, 2, 128, 8)])
+@pytest.mark.parametrize("B,S,H,D,P", [(2, 1024, 2, 64, 4), (2, 2048, 2, 128, 8)])
 def test_scores_rising_across_the_fast_pass_limit(gpu, rise, B, S, H, D, P):
     # Rows whose running max rises by `rise` log2 units: below 2^40 the first
     # pass's probabilities (up to 2^rise) are used as they are, above it the
@@ -379,15 +379,20 @@ def test_scores_rising_across_the_fast_pass_limit(gpu, rise, B, S, H, D, P):
     u = 2.0 ** -8
     bound = u * np.abs(ref) + u * (1 + u) * ref_abs + 1e-5
     q, k, v = to_gpu(inp, gpu)
-    for ws in (None, "auto"):
-        out_l, lse = xs.fwd(q, k, v, P, scale, lse=True, workspace=ws)
-        torch.cuda.synchronize()
-        got = f64(out_l)
-        worst = float((np.abs(got - ref) / bound).max())
-        d = np.abs(f64(lse) - ref_l)
-        print(f"  workspace={ws}: worst error / bound = {worst:.3f}, lse max_abs={d.max():.3e}", flush=True)
-        assert worst <= 1.0 and np.isfinite(got).all()
-        assert d.max() <= 5e-3
+    # the chunk layout too: a piece run a second time restarts the chunk cursors
+    # of its K/V addresses from the piece's first block
+    qc, kc, vc = (xs.chunk(t, P) for t in (q, k, v))
+    for layout, args in (("bshd", (q, k, v)), ("chunked", (qc, kc, vc))):
+        for ws in (None, "auto"):
+            out_l, lse = xs.fwd(*args, P, scale, lse=True, workspace=ws, in_layout=layout)
+            torch.cuda.synchronize()
+            got = f64(out_l)
+            worst = float((np.abs(got - ref) / bound).max())
+            d = np.abs(f64(lse) - ref_l)
+            print(f"  {layout} workspace={ws}: worst error / bound = {worst:.3f}, "
+                  f"lse max_abs={d.max():.3e}", flush=True)
+            assert worst <= 1.0 and np.isfinite(got).all()
+            assert d.max() <= 5e-3
 
 
 def _mid_block_spikes(B, S, H, D, index):
