@@ -6,8 +6,8 @@ They cover what the fixed cases leave to chance: every residue of the key count
 modulo the 64-key block and of the block count modulo the four-stage LDS ring
 (so every tail length of a piece), pieces that start and end anywhere in a
 tile, destination slices that straddle tiles, and B, H, P combinations.  Bars
-as in the parity tests: max-abs 1e-2 / 5e-2 and rel-L2 1e-2 / 8e-2 on O, 5e-3 on
-the log-sum-exp.
+as in the parity tests: max-abs 1e-2 / 5e-2 (fp8: or the per-element bound of its
+encoding of P, where larger) and rel-L2 1e-2 / 8e-2 on O, 5e-3 on the log-sum-exp.
 """
 import os
 
@@ -17,6 +17,7 @@ import torch
 
 import sequence_attention_amd as xs
 import workloads
+from fp8_bounds import fp8_bounds
 from oracle import oracle
 
 pytestmark = pytest.mark.gpu
@@ -68,12 +69,21 @@ def test_sweep(gpu, i, dtype, B, S, H, D, P, split, chunked):
         plain = xs.fwd(q, k, v, P, inp["scale"], workspace=ws, in_layout=layout)
     torch.cuda.synchronize()
     ta, tr = TOL[dtype]
+    # fp8: the flat max-abs bar is stated for the workloads' |O| (outputs averaged
+    # over thousands of keys); a row over a handful of keys is held to the larger
+    # of that bar and the per-element bound derived from P's encoding
+    bars = {"O": ta, "O with lse": ta}
+    if dtype == "fp8":
+        b_lse, b_plain = fp8_bounds(inp, P, inp["scale"])
+        bars = {"O": np.maximum(ta, b_plain), "O with lse": np.maximum(ta, b_lse)}
     for name, o in (("O", plain), ("O with lse", out)):
         got = o.float().cpu().numpy().astype(np.float64)
         err = np.abs(got - ref_o)
         rel = float(np.linalg.norm(got - ref_o) / np.linalg.norm(ref_o))
-        print(f"  {name}: max_abs={err.max():.3e} rel_l2={rel:.3e}", flush=True)
-        assert np.isfinite(got).all() and err.max() <= ta and rel <= tr, name
+        worst = float((err / bars[name]).max())
+        print(f"  {name}: max_abs={err.max():.3e} rel_l2={rel:.3e} worst error / bar={worst:.3f}",
+              flush=True)
+        assert np.isfinite(got).all() and worst <= 1.0 and rel <= tr, name
     if dtype == "bf16":  # the log-sum-exp output does not change O
         assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
     d = float(np.abs(lse.cpu().numpy().astype(np.float64) - ref_l).max())
