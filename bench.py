@@ -67,6 +67,10 @@ def parse():
     ap.add_argument("--torch-sdpa", action="store_true",
                     help="context: time torch's own fused attention (scaled_dot_product_attention, "
                          "flash backend only) on the same inputs next to this library's call")
+    ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
+                    help="instead of the timed steps, run back-to-back steps for SECONDS while "
+                         "sampling the socket power and GFX clocks with amd-smi; report the "
+                         "energy per step")
     ap.add_argument("--ceilings", action="store_true",
                     help="instead of the benchmark, run the matrix-core ceiling probes "
                          "(xs_mfma_ceiling: MFMA rate next to LDS operand reads and softmax "
@@ -131,6 +135,80 @@ def ceilings(iters, reps=5):
         res[f"{waves}_waves_per_simd"] = {
             "mfma_only_clock_ghz": round(mfma_per_simd * 32 / (base * 1e-3) / 1e9, 3), "modes": rows}
     return res
+
+
+def smi_parse(text):
+    """(socket power in W, mean GFX clock in MHz over the XCDs) from the text of
+    `amd-smi metric -p -c`, or None when a field is missing."""
+    import re
+
+    m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text)
+    clocks, in_gfx = [], False
+    for line in text.splitlines():
+        if re.match(r"\s*GFX_\d+:", line):
+            in_gfx = True
+        elif in_gfx and re.match(r"\s*CLK:", line):
+            clocks.append(float(re.findall(r"[0-9.]+", line)[0]))
+            in_gfx = False
+    if not m or not clocks:
+        return None
+    return float(m.group(1)), sum(clocks) / len(clocks)
+
+
+def smi_sample():
+    """One amd-smi sample (see smi_parse), or None when the tool is not there."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
+                             timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return smi_parse(out)
+
+
+def power_run(step, seconds, flops):
+    """Back-to-back steps for `seconds` while a thread samples amd-smi every 0.25 s;
+    samples of the first second (clock ramp) are dropped."""
+    import threading
+
+    idle = smi_sample()
+    samples, stop = [], threading.Event()
+    t0 = time.time()
+
+    def sampler():
+        while not stop.is_set():
+            v = smi_sample()
+            if v is not None:
+                samples.append((time.time() - t0, *v))
+            stop.wait(0.25)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    n = 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    while time.time() - t0 < seconds:
+        for _ in range(20):
+            step()
+        n += 20
+        torch.cuda.current_stream().synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    ms = e0.elapsed_time(e1) / n
+    steady = [s for s in samples if s[0] >= 1.0] or samples
+    if not steady:
+        return {"available": False}
+    watts = sum(s[1] for s in steady) / len(steady)
+    mhz = sum(s[2] for s in steady) / len(steady)
+    return {"available": True, "steps": n, "ms_per_step": round(ms, 4),
+            "value_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "socket_w_mean": round(watts, 1), "gfx_mhz_mean": round(mhz, 1),
+            "samples": len(steady), "idle_socket_w": idle[0] if idle else None,
+            "joules_per_step": round(watts * ms * 1e-3, 4),
+            "tflop_per_joule": round(flops / (watts * ms * 1e-3) / 1e12, 4)}
 
 
 def recorded_traffic(kernel_tag, workload):
@@ -405,6 +483,11 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.power:
+        print(json.dumps({"metric": "power", "n_gpus": 1, "workload": w.name,
+                          "entry": "xs_attn_fwd_ex with a caller workspace",
+                          **power_run(step, args.power, w.flops)}), flush=True)
+        return
     if args.graph:
         # the library launches kernels only (no memset, no allocation), so one call
         # captures as is; every replay re-reads the current contents of q, k, v

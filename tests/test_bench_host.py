@@ -46,3 +46,27 @@ def test_cpu_baseline_record():
     assert cb["value"] > 0 and cb["cores"] >= 1
     n = int(cb["sample"].split(" of ")[0])
     assert 1 <= n <= w.B * w.S * w.H and n % cb["cores"] == 0 or n == w.B * w.S * w.H
+
+
+SMI_TEXT = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1331 W
+        GFX_VOLTAGE: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 1760 MHz
+            MIN_CLK: 500 MHz
+            MAX_CLK: 2400 MHz
+        GFX_1:
+            CLK: 1772 MHz
+            MIN_CLK: 500 MHz
+            MAX_CLK: 2400 MHz
+        MEM_0:
+            CLK: 2000 MHz
+"""
+
+
+def test_amd_smi_text_parsed():
+    # socket power and the mean of the GFX clocks only (not the memory clock, not the limits)
+    assert bench.smi_parse(SMI_TEXT) == (1331.0, 1766.0)
+    assert bench.smi_parse("GPU: 0\n    POWER:\n        SOCKET_POWER: N/A\n") is None
