@@ -55,7 +55,7 @@ def parse():
                     help="write a 512 MiB buffer before every timed call (evicts L2 and MALL) and "
                          "report the per-call event times instead of the back-to-back step time")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
-    ap.add_argument("--no-north-star", action="store_true",
+    ap.add_argument("--no-plain-entry", action="store_true",
                     help="skip the extra timing of xs_attn_fwd / xs_attn_fwd_fp8 without workspace "
                          "(for profiling runs whose dispatches should be the timed calls only)")
     ap.add_argument("--burst-gap", action="store_true",
@@ -544,7 +544,7 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     achieved = flops / (float(launch_ms.mean()) * 1e-3) / 1e12
 
-    # The spec signature itself (xs_attn_fwd / xs_attn_fwd_fp8 by name: no
+    # The plain signature itself (xs_attn_fwd / xs_attn_fwd_fp8 by name: no
     # workspace, so the schedule never cuts a tile), timed the same way after the
     # product path's timed steps, on the same inputs.
     out_ns = torch.empty_like(out)
@@ -561,8 +561,8 @@ def main():
         if rc != 0:
             raise RuntimeError(xs.xs_attn_strerror(rc))
 
-    north_star = None
-    if args.in_layout == "bshd" and not args.cold and not args.no_north_star:
+    plain_entry = None
+    if args.in_layout == "bshd" and not args.cold and not args.no_plain_entry:
         for _ in range(min(args.warmup, 3)):
             step_ns()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -573,7 +573,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ms_ns = e0.elapsed_time(e1) / args.steps
-        north_star = {"entry": "xs_attn_fwd_fp8" if w.dtype == "fp8" else "xs_attn_fwd",
+        plain_entry = {"entry": "xs_attn_fwd_fp8" if w.dtype == "fp8" else "xs_attn_fwd",
                       "workspace_bytes": 0, "schedule": sched_ns, "steps": args.steps,
                       "ms_per_call": round(ms_ns, 4),
                       "value": round(flops / (ms_ns * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
@@ -622,7 +622,7 @@ def main():
                                + (" + attn_combine_kernel" if nsplit > 1 else ""),
                      "flops_per_launch": flops},
         "clock": profile_clock(kernel_tag, w.name, achieved, peak),
-        "north_star_entry": north_star,
+        "plain_entry": plain_entry,
         "check": check,
     }
     if not args.no_cpu_baseline:

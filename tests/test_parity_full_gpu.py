@@ -1,5 +1,5 @@
-"""GPU parity at the full sizes of the workloads, and of the two spec entry
-points called by name, against the fp64 CPU oracle.
+"""GPU parity at the full sizes of the workloads, and of the two plain entry points
+(no workspace argument) called by name, against the fp64 CPU oracle.
 
 * video and fp8 shares: every element of out_packed, both through the product
   path (the split schedule with a caller workspace, what the benchmark times)
@@ -16,7 +16,7 @@ points called by name, against the fp64 CPU oracle.
   share, where the default plan would cut tiles, on every element.
 
 Bar: max-abs 1e-2 (bf16 inputs) / 5e-2 (fp8) and relative L2 1e-2 / 8e-2 on every
-compared element, the benchmark spec's tolerance on the workloads' own inputs.
+compared element, the stated tolerance on the workloads' own inputs.
 """
 import numpy as np
 import pytest
@@ -147,9 +147,9 @@ def test_whole_tile_round_then_cut_remainder_every_element(gpu, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_north_star_entry_points_by_name(gpu, dtype):
+def test_plain_entry_points_by_name(gpu, dtype):
     # The image share: 54 tiles on 256 CUs, where the default (workspace) plan
-    # cuts every tile; the spec signatures take no workspace and run the
+    # cuts every tile; the plain signatures take no workspace and run the
     # uncut schedule.
     w = workloads.WORKLOADS["image"].with_(dtype=dtype, index=8200 + (dtype == "fp8"))
     assert xs.split_count(w.B, w.S, w.H, w.D) > 1
