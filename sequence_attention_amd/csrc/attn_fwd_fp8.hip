@@ -294,13 +294,15 @@ __device__ __forceinline__ uint32_t pack4(f32x4 p) {
 // = e + f (e integer, f in [0, 1)) the code round(8 (y + 7)) encodes 2^e (1 + f)
 // -- 2^y interpolated linearly between powers of two (within +6.2 % of it), on
 // e4m3's three-bit mantissa grid (within half a step, 6.25 %).  One FMA gives
-// 8 (y + 7) = s (8c) + 8 (SHIFT + 7 - m) and one conversion rounds it to the
-// nearest integer byte (v_cvt_pk_u8_f32: round to nearest even, clamped to
-// [0, 255]).  The row sums that normalise O are those of the same codes' values
-// (row-sum MFMA), and the constant 2^SHIFT cancels in O / l.  x <= TAU = 4 keeps
-// every code <= 126; x < -10.75 gives subnormal codes and x below about -11.7
+// z = 8 (y + 7) / 65535 = s (8c / 65535) + 8 (SHIFT + 7 - m) / 65535, and a
+// normalised 16-bit conversion (v_cvt_pknorm_u16_f32: clamp to [0, 1], times
+// 65535, rounded to the nearest integer) turns two such values into two codes at
+// once; one byte permutation packs four.  The row sums that normalise O are those
+// of the same codes' values (row-sum MFMA), and the constant 2^SHIFT cancels in
+// O / l.  x <= TAU = 4 keeps every code <= 126 (so the low byte of each 16-bit
+// result is the code); x < -10.75 gives subnormal codes and x below about -11.7
 // code 0: weights under 2^-10.75 of the row's largest key (which has x >= 0).
-// code4 computes the four codes as fp32 (pinned), pack_codes4 packs the bytes.
+// code4 computes the four values z as fp32 (pinned), pack_codes4 packs the codes.
 template <class C>
 __device__ __forceinline__ f32x4 code4(const Scores8<C>& sc, int nt, int q, float c8, float bias) {
   float t[4];
@@ -312,20 +314,23 @@ __device__ __forceinline__ f32x4 code4(const Scores8<C>& sc, int nt, int q, floa
   return f32x4{t[0], t[1], t[2], t[3]};
 }
 __device__ __forceinline__ uint32_t pack_codes4(f32x4 t) {
-  uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(t[0], 0, 0u);
-  w = __builtin_amdgcn_cvt_pk_u8_f32(t[1], 1, w);
-  w = __builtin_amdgcn_cvt_pk_u8_f32(t[2], 2, w);
-  w = __builtin_amdgcn_cvt_pk_u8_f32(t[3], 3, w);
+  // codes 0 and 1 in the low bytes of lo's halves, codes 2 and 3 in hi's;
+  // selector bytes 0, 2 pick lo's bytes 0, 2 and 4, 6 hi's bytes 0, 2
+  const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_u16(t[0], t[1]));
+  const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_u16(t[2], t[3]));
+  uint32_t w = __builtin_amdgcn_perm(hi, lo, 0x06040200u);
   pin(w);
   return w;
 }
 // The instantiation's form of the probabilities: exp4/pack4 with the
 // log-sum-exp (factors (a, b) = (c, -m)), code4/pack_codes4 without it
-// ((a, b) = (8c, 8(-m) + CODE_BIAS)).
+// ((a, b) = (8c, 8(-m) + CODE_BIAS) / 65535).
 template <class C>
-__device__ __forceinline__ float prob_a(float c) { return C::LSE ? c : 8.0f * c; }
+__device__ __forceinline__ float prob_a(float c) { return C::LSE ? c : 8.0f * c * (1.0f / 65535.0f); }
 template <class C>
-__device__ __forceinline__ float prob_b(float neg_m) { return C::LSE ? neg_m : 8.0f * neg_m + C::CODE_BIAS; }
+__device__ __forceinline__ float prob_b(float neg_m) {
+  return C::LSE ? neg_m : (8.0f * neg_m + C::CODE_BIAS) * (1.0f / 65535.0f);
+}
 template <class C>
 __device__ __forceinline__ f32x4 prob4(const Scores8<C>& sc, int nt, int q, float a, float b,
                                        float& lsum) {
