@@ -43,7 +43,8 @@ def parse():
                     help="target wall time of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--samples", type=int, default=20,
-                    help="timed launches also bracketed by their own events (roofline launch time)")
+                    help="timed launches also bracketed by their own events (roofline launch "
+                         "time): every max(4, K/samples)-th call")
     ap.add_argument("--in-layout", default="bshd", choices=["bshd", "chunked"],
                     help="input layout: [B][S][H][D] or the pre-attention All-to-All chunk layout "
                          "[P][B][S/P][H][D] (converted once, before timing)")
@@ -513,7 +514,8 @@ def main():
     # bracketed by its own pair of events, for the kernel's mean launch duration
     # in the roofline: each event between launches adds queue time of its own, so
     # instrumenting every launch would slow the back-to-back steps being timed.
-    every = 1 if args.cold else max(1, args.steps // args.samples)
+    # at most every fourth call carries events (a short run still gets K/4 samples)
+    every = 1 if args.cold else max(4, args.steps // args.samples)
     ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for i in range(0, args.steps, every)}
     t_start = torch.cuda.Event(enable_timing=True)
