@@ -75,7 +75,8 @@ def parse():
     ap.add_argument("--ceilings", action="store_true",
                     help="instead of the benchmark, run the matrix-core ceiling probes "
                          "(xs_mfma_ceiling: MFMA rate next to LDS operand reads and softmax "
-                         "vector work, one and two waves per SIMD)")
+                         "vector work, one and two waves per SIMD); with --power, the socket "
+                         "power and matrix work per joule of probe modes 0, 5, 7 and 8 instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -98,7 +99,9 @@ CEILING_MODES = ["mfma only", "1 KiB ds_read_b128 per MFMA", "0.5 KiB ds_read_b1
                  "1 KiB ds_read_b64_tr_b16 per MFMA",
                  "softmax work per MFMA (fma, exp, add, half a bf16 pack)",
                  "softmax work + 1 KiB ds_read_b128 per MFMA (32 query rows per wave)",
-                 "softmax work + 0.5 KiB ds_read_b128 per MFMA (64 query rows per wave)"]
+                 "softmax work + 0.5 KiB ds_read_b128 per MFMA (64 query rows per wave)",
+                 "mfma only, random bf16 operands",
+                 "softmax work + 1 KiB ds_read_b128 per MFMA, random bf16 data"]
 
 
 def ceilings(iters, reps=5):
@@ -136,6 +139,27 @@ def ceilings(iters, reps=5):
         res[f"{waves}_waves_per_simd"] = {
             "mfma_only_clock_ghz": round(mfma_per_simd * 32 / (base * 1e-3) / 1e9, 3), "modes": rows}
     return res
+
+
+def ceiling_power(seconds, modes=(0, 5, 7, 8), iters=2048):
+    """Socket power, GFX clock and matrix work per joule of probe modes run back to back
+    (two waves per SIMD) for `seconds` each, sampled as in power_run."""
+    from sequence_attention_amd import _lib
+
+    L = _lib.lib()
+    stream = torch.cuda.current_stream()
+    sink = torch.empty(1024 * 512, dtype=torch.float32, device="cuda:0")
+    flops = 1024 * 8 * 16 * iters * 32 * 32 * 16 * 2.0
+    out = []
+    for mode in modes:
+        def step(mode=mode):
+            _lib.check(L.xs_mfma_ceiling(mode, 2, iters, ctypes.c_void_p(sink.data_ptr()),
+                                          sink.numel() * 4, ctypes.c_void_p(stream.cuda_stream)))
+        step()
+        torch.cuda.synchronize()
+        out.append({"mode": mode, "stream": CEILING_MODES[mode], **power_run(step, seconds, flops)})
+        print(f"ceiling power mode {mode} done", file=sys.stderr, flush=True)
+    return out
 
 
 def smi_parse(text):
@@ -441,8 +465,12 @@ def main():
         copy_calibration(args.copy_calibration, args.steps)
         return
     if args.ceilings:
-        print(json.dumps({"metric": "mfma_ceilings", "n_gpus": 1, "iters": 2048,
-                          **ceilings(2048)}), flush=True)
+        if args.power:
+            print(json.dumps({"metric": "mfma_ceilings_power", "n_gpus": 1, "iters": 2048,
+                              "waves_per_simd": 2, "modes": ceiling_power(args.power)}), flush=True)
+        else:
+            print(json.dumps({"metric": "mfma_ceilings", "n_gpus": 1, "iters": 2048,
+                              **ceilings(2048)}), flush=True)
         return
     if args.epilogue_overhead:
         epilogue_overhead(args)

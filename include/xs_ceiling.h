@@ -11,7 +11,10 @@
  * per wave) and about three vector instructions and one exponential of
  * softmax work.  These probes measure the MFMA rate the chip sustains under
  * each stream alone and under both, so the kernel's own MFMA-busy fraction
- * can be read against them.
+ * can be read against them.  Modes 0-6 multiply fixed or arbitrary bit
+ * patterns (little switching activity, and NaN once an accumulator overflows);
+ * modes 7 and 8 repeat modes 0 and 5 on random finite bf16 data, which draws
+ * the power that real inputs draw.
  */
 #ifndef XS_CEILING_H
 #define XS_CEILING_H
@@ -30,7 +33,14 @@ extern "C" {
                                v_exp_f32, one v_add_f32 and half a v_cvt_pk_bf16_f32, no LDS */
 #define XS_CEIL_MIX 5       /* XS_CEIL_SOFTMAX + XS_CEIL_LDS_1K: the mix of 32 query rows per wave */
 #define XS_CEIL_MIX_HALF 6  /* XS_CEIL_SOFTMAX + XS_CEIL_LDS_HALF: the mix of 64 query rows per wave */
-#define XS_CEIL_MODES 7
+#define XS_CEIL_MFMA_DATA 7  /* XS_CEIL_MFMA with operands of the kind the kernel multiplies: A and B
+                               rotate through eight register-held fragments of random bf16 values
+                               (random sign and mantissa, magnitudes 2^-3 .. 2^4), so every MFMA
+                               switches operand bits as the attention kernel's do */
+#define XS_CEIL_MIX_DATA 8   /* XS_CEIL_MIX on such data: the LDS holds those values, the softmax
+                               stand-in takes a new argument per MFMA (the A operand's first word
+                               read as fp32) and its probabilities, 2^-6 .. 2^2, are the B operand */
+#define XS_CEIL_MODES 9
 
 #define XS_CEIL_SINK_BYTES (1024u * 512u * 4u) /* smallest sink accepted */
 

@@ -13,6 +13,23 @@ constexpr int kInner = 16;                    // MFMAs per loop trip
 constexpr int kLead = 3;                      // LDS reads issued this many MFMAs ahead
 constexpr int kGroups = 1024;
 
+// A bf16 operand value of the kind the attention kernels multiply: random sign,
+// exponent 2^-3 .. 2^3, random mantissa (never zero, subnormal, Inf or NaN).
+__device__ __forceinline__ uint32_t bf16_sample(uint32_t h) {
+  const uint32_t e = 124u + ((h >> 7) & 0xFFu) % 7u;
+  return (h & 0x8000u) | (e << 7) | (h & 0x7Fu);
+}
+
+// LDS word i of the data modes: two such bf16 values; read as an fp32 the word
+// is its upper value with noise in the low mantissa bits.
+__device__ __forceinline__ uint32_t data_word(uint32_t i) {
+  uint32_t h = i * 2654435761u;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  return (bf16_sample(h >> 16) << 16) | bf16_sample(h & 0xFFFFu);
+}
+
 // One trip's worth of a mode's extra stream is written out per MFMA; the
 // scheduling barrier after each MFMA and its slice keeps the interleave.
 template <int MODE, int THREADS>
@@ -21,13 +38,16 @@ __global__ __launch_bounds__(THREADS, 1) void ceiling_kernel(float* sink, int it
   __shared__ __attribute__((aligned(1024))) uint8_t smem[96 * 1024];
   uint8_t XS_LDS* lds = (uint8_t XS_LDS*)smem;
   const int lane = threadIdx.x & 63;
+  constexpr bool kData = MODE == XS_CEIL_MFMA_DATA || MODE == XS_CEIL_MIX_DATA;
   for (uint32_t i = threadIdx.x * 4; i < sizeof(smem); i += THREADS * 4)
-    *(uint32_t XS_LDS*)(lds + i) = i * 2654435761u;
+    *(uint32_t XS_LDS*)(lds + i) = kData ? data_word(i >> 2) : i * 2654435761u;
   __syncthreads();
 
-  constexpr bool kPerMfma = MODE == XS_CEIL_LDS_1K || MODE == XS_CEIL_TR16_1K || MODE == XS_CEIL_MIX;
+  constexpr bool kPerMfma =
+      MODE == XS_CEIL_LDS_1K || MODE == XS_CEIL_TR16_1K || MODE == XS_CEIL_MIX || MODE == XS_CEIL_MIX_DATA;
   constexpr bool kHalf = MODE == XS_CEIL_LDS_HALF || MODE == XS_CEIL_MIX_HALF;
-  constexpr bool kSoftmax = MODE == XS_CEIL_SOFTMAX || MODE == XS_CEIL_MIX || MODE == XS_CEIL_MIX_HALF;
+  constexpr bool kSoftmax =
+      MODE == XS_CEIL_SOFTMAX || MODE == XS_CEIL_MIX || MODE == XS_CEIL_MIX_HALF || MODE == XS_CEIL_MIX_DATA;
   f32x16 acc[4] = {};
   const u32x4 a = {lane * 3u, lane * 5u, 7u, 9u};
   // softmax stand-in, as in the bf16 kernel: p = 2^(x c - m) of eight independent
@@ -48,6 +68,12 @@ __global__ __launch_bounds__(THREADS, 1) void ceiling_kernel(float* sink, int it
     return lds_read_b128(tb + f * 1024);
   };
   const uint8_t XS_LDS* const lane_base = lds + (MODE == XS_CEIL_TR16_1K ? lane * 8 : lane * 16);
+  // MFMAs-only data mode: eight register-held fragments of the LDS data, A and B
+  // rotating through them so that every MFMA sees new operand bits
+  u32x4 regf[8];
+  if (MODE == XS_CEIL_MFMA_DATA)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) regf[i] = lds_read_b128(lane_base + i * 1024);
   if (kPerMfma || kHalf)
 #pragma unroll
     for (int k = 0; k < kLead; ++k) frag[k] = read(lane_base, k);
@@ -57,17 +83,25 @@ __global__ __launch_bounds__(THREADS, 1) void ceiling_kernel(float* sink, int it
 #pragma unroll
     for (int k = 0; k < kInner; ++k) {
       u32x4 op = a;
-      if (kPerMfma) {
+      u32x4 opb = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      if (MODE == XS_CEIL_MFMA_DATA) {
+        op = regf[k & 7];
+        opb = regf[(k + 3) & 7];
+      } else if (kPerMfma) {
         frag[(k + kLead) % (kLead + 1)] = read(tb, k + kLead);
         op = frag[k % (kLead + 1)];
       } else if (kHalf) {
         if ((k & 1) == 0) frag[((k >> 1) + kLead) % (kLead + 1)] = read(tb, (k >> 1) + kLead);
         op = frag[(k >> 1) % (kLead + 1)];
       }
-      acc[k & 3] = mfma_bf16(op, u32x4{pk[0], pk[1], pk[2], pk[3]}, acc[k & 3]);
+      acc[k & 3] = mfma_bf16(op, opb, acc[k & 3]);
       __builtin_amdgcn_sched_barrier(0);
       if (kSoftmax) {
-        z[k & 7] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[k & 7], 0.5f, -0.4f));
+        // data mode: the exponent's argument is a new value each time (this MFMA's
+        // A word read as fp32: |x| in [1/8, 16)), so p spans 2^-6 .. 2^2
+        const float x = kData ? __uint_as_float(op[k & 3]) : z[k & 7];
+        z[k & 7] = kData ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, 0.25f, -2.0f))
+                         : __builtin_amdgcn_exp2f(__builtin_fmaf(x, 0.5f, -0.4f));
         lsum += z[k & 7];
         if (k & 1) pk[(k >> 1) & 3] = pack_bf16(z[(k - 1) & 7], z[k & 7]);
       }
@@ -84,6 +118,9 @@ __global__ __launch_bounds__(THREADS, 1) void ceiling_kernel(float* sink, int it
   if (kPerMfma || kHalf)
 #pragma unroll
     for (int k = 0; k <= kLead; ++k) s += (float)(frag[k][0] ^ frag[k][3]);
+  if (MODE == XS_CEIL_MFMA_DATA)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += (float)(regf[k][1] & 0xFFu);
   sink[blockIdx.x * 512 + threadIdx.x] = s;
 }
 
@@ -118,7 +155,9 @@ extern "C" int xs_mfma_ceiling(int mode, int waves_per_simd, int iters, float* s
     case XS_CEIL_TR16_1K: e = launch_mode<XS_CEIL_TR16_1K>(waves_per_simd, sink, iters, s); break;
     case XS_CEIL_SOFTMAX: e = launch_mode<XS_CEIL_SOFTMAX>(waves_per_simd, sink, iters, s); break;
     case XS_CEIL_MIX: e = launch_mode<XS_CEIL_MIX>(waves_per_simd, sink, iters, s); break;
-    default: e = launch_mode<XS_CEIL_MIX_HALF>(waves_per_simd, sink, iters, s); break;
+    case XS_CEIL_MIX_HALF: e = launch_mode<XS_CEIL_MIX_HALF>(waves_per_simd, sink, iters, s); break;
+    case XS_CEIL_MFMA_DATA: e = launch_mode<XS_CEIL_MFMA_DATA>(waves_per_simd, sink, iters, s); break;
+    default: e = launch_mode<XS_CEIL_MIX_DATA>(waves_per_simd, sink, iters, s); break;
   }
   return e == hipSuccess ? 0 : XS_CEIL_ERR_LAUNCH;
 }
