@@ -15,17 +15,21 @@
 
 namespace xs {
 
-// One workgroup per RPB rows of one query tile.  Tiles held whole by one share
-// of the schedule were stored by the attention kernel: those workgroups exit.
-// For a cut tile the pieces are, in key order, the last piece of the share
-// that owns its first unit (slot 2c+1, or 2c if that share's remainder run
-// starts exactly at the tile) and the first piece of every later share up to
-// the owner of its last unit (slot 2c).
+// The attention kernels store a piece's O in the register order of their
+// 32x32 accumulators: per 32-row group of the tile, D/8 chunks of 64 lanes x
+// 4 floats, lane L holding row L%32 and, in chunk k, the columns
+// 32(k/4) + 8(k%4) + 4(L/32) .. +3 of it.  Each workgroup here reads four chunks of one
+// 32-row group (one per wave, 1 KiB contiguous per piece) and merges them.
+// Tiles held whole by one share of the schedule were stored by the attention
+// kernel: those workgroups exit.  For a cut tile the pieces are, in key order,
+// the last piece of the share that owns its first unit (slot 2c+1, or 2c if
+// that share's remainder run starts exactly at the tile) and the first piece
+// of every later share up to the owner of its last unit (slot 2c).
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  constexpr int LPR = D / 4;             // lanes per row, 4 consecutive d each
-  constexpr int RPB = 256 / LPR;         // rows per workgroup
-  constexpr int GPT = kBlockM / RPB;     // workgroups per tile
+  constexpr int CH = D / 8;                   // chunks per 32-row group
+  constexpr int WPG = CH / 4;                 // workgroups per 32-row group
+  constexpr int GPT = (kBlockM / 32) * WPG;   // workgroups per tile
   const Sched sch{a.units, a.groups, a.npair, a.dp};
   // only the remainder tiles can be cut: the grid covers them alone
   const int rt = blockIdx.x / GPT;  // index among the remainder tiles
@@ -35,10 +39,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   if (c_lo == c_hi) return;
   const int mtiles = (a.S + kBlockM - 1) / kBlockM;
   const int bh = tile / mtiles;
-  const int r = (blockIdx.x % GPT) * RPB + threadIdx.x / LPR;  // row within the tile
+  const int wg = blockIdx.x % GPT;
+  const int g = wg / WPG;                                      // 32-row group
+  const int k = (wg % WPG) * 4 + (int)(threadIdx.x >> 6);      // chunk
+  const int ln = threadIdx.x & 63;
+  const int r = g * 32 + (ln & 31);  // row within the tile
   const int srow = (tile - bh * mtiles) * kBlockM + r;
   if (srow >= a.S) return;
-  const int d0 = (threadIdx.x % LPR) * 4;
+  const int d0 = (k >> 2) * 32 + (k & 3) * 8 + 4 * (ln >> 5);
+  const size_t ooff = ((size_t)(g * CH + k) * 64 + ln) * 4;  // within a slot's O
   // every share holds at least one remainder unit (the plan keeps units >= groups)
   const size_t first = 2 * (size_t)c_lo + (sch.start(c_lo) < u0 ? 1 : 0);
   auto slot_of = [&](int c) { return c == c_lo ? first : 2 * (size_t)c; };
@@ -57,7 +66,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
       const int c = c0 + i <= c_hi ? c0 + i : c_hi;  // clamped: a repeated load, not used
       const size_t sr = slot_of(c) * kBlockM + r;
       ml[i] = *(const f32x2*)(a.ws_ml + 2 * sr);
-      o[i] = *(const f32x4*)(a.ws_o + sr * D + d0);
+      o[i] = *(const f32x4*)(a.ws_o + slot_of(c) * kBlockM * D + ooff);
     }
     float Mg = M;
 #pragma unroll
@@ -87,8 +96,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 template <int D>
 static hipError_t launch_combine_d(const AttnArgs& a, hipStream_t stream) {
-  constexpr int RPB = 256 / (D / 4);
-  const long long blocks = a.units / a.npair * (kBlockM / RPB);
+  constexpr int GPT = (kBlockM / 32) * (D / 32);  // workgroups per tile, as in the kernel
+  const long long blocks = a.units / a.npair * GPT;
   if (blocks < 1 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   AttnArgs args = a;
   void* kargs[] = {&args};

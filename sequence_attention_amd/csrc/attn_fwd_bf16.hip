@@ -820,20 +820,22 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
       }
     } else {
       // a tile cut between shares: unnormalised fp32 partials into this
-      // share's slot, merged by attn_combine
+      // share's slot, merged by attn_combine.  O is stored in register order
+      // (each 32-row group as D/8 chunks of 64 lanes x 16 bytes), so every
+      // store instruction writes 1 KiB contiguously.
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         const float lsum = sum_halves(st.l[qt]);
         const int r = wave * C::QW + qt * 32 + (lane & 31);  // row within the tile
         if (m0 + r < S) {
           const size_t sr = (size_t)cur_slot * C::BM + r;
-          float* orow = a.ws_o + sr * C::D;
+          float* og = a.ws_o + ((size_t)cur_slot * C::BM + wave * C::QW + qt * 32) * C::D;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
               const f32x16& o = st.o[qt][dt];
-              *(f32x4*)(orow + dt * 32 + r4 * 8 + 4 * (lane >> 5)) =
+              *(f32x4*)(og + ((dt * 4 + r4) * 64 + lane) * 4) =
                   f32x4{o[4 * r4 + 0], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]};
             }
           if (lane < 32) *(f32x2*)(a.ws_ml + 2 * sr) = f32x2{st.m[qt], lsum};

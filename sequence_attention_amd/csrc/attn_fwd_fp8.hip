@@ -753,18 +753,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
           }
       }
     } else {
-      // a tile cut between shares: fp32 partials into this share's slot
+      // a tile cut between shares: fp32 partials into this share's slot, O in
+      // register order as in the bf16 kernel (1 KiB per store instruction)
       const float lsum = row_sum(st);
       const int r = srow - m0;
       if (srow < S) {
         const size_t sr = (size_t)cur_slot * C::BM + r;
-        float* orow = a.ws_o + sr * C::D;
+        float* og = a.ws_o + ((size_t)cur_slot * C::BM + wave * C::QW) * C::D;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const f32x16& o = st.o[dt];
-            *(f32x4*)(orow + dt * 32 + r4 * 8 + 4 * (lane >> 5)) =
+            *(f32x4*)(og + ((dt * 4 + r4) * 64 + lane) * 4) =
                 f32x4{o[4 * r4 + 0], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]};
           }
         if (lane < 32) *(f32x2*)(a.ws_ml + 2 * sr) = f32x2{st.m, lsum};

@@ -25,7 +25,7 @@ struct AttnArgs {
   int npair;
   int dp;
   long long units;
-  float* ws_o;    // [2*groups][BM][D] fp32 (NULL when no tile is cut)
+  float* ws_o;    // [2*groups][BM*D] fp32 in register order (NULL when no tile is cut)
   float* ws_ml;   // [2*groups][BM][2] fp32: running max (log2 units), row sum
   // Input layout.  Row s of batch b of an input tensor starts at row index
   //   b*batch_rows + s + (chunk_rows ? s / chunk_rows : 0) * jump_rows
