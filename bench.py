@@ -273,6 +273,52 @@ def profile_clock(kernel_tag, workload, achieved, peak):
             "frac_at_that_clock": round(achieved / (peak * ghz / 2.4), 4)}
 
 
+def clock_sample(L, buf, stream):
+    """Queue one xs_clock_sample on `stream` into the device buffer `buf`; returns the
+    constant counter's rate in kHz."""
+    khz = ctypes.c_int(0)
+    from sequence_attention_amd import _lib
+    _lib.check(L.xs_clock_sample(ctypes.c_void_p(buf.data_ptr()), buf.numel() * 8, ctypes.byref(khz),
+                                 ctypes.c_void_p(stream.cuda_stream)))
+    return khz.value
+
+
+def live_clock(before, after, wall_khz):
+    """Mean shader clock (GHz) of each XCC between two xs_clock_sample records (rows
+    [memtime, realtime, xcc, hw_id]): per compute unit (xcc, hw_id bits 8-15) seen in
+    both, memtime cycles over the constant counter's elapsed time; the median over an
+    XCC's compute units."""
+    def first_by_cu(rec):
+        out = {}
+        for t, r, x, hw in np.asarray(rec, dtype=np.int64).reshape(-1, 4):
+            out.setdefault((int(x), (int(hw) >> 8) & 0xFF), (int(t), int(r)))
+        return out
+    a, b = first_by_cu(before), first_by_cu(after)
+    per = {}
+    for key in set(a) & set(b):
+        dt, dr = b[key][0] - a[key][0], b[key][1] - a[key][1]
+        if dt > 0 and dr > 0 and wall_khz > 0:
+            per.setdefault(key[0], []).append(dt / (dr / (wall_khz * 1e3)) / 1e9)
+    return {x: float(np.median(v)) for x, v in sorted(per.items())}
+
+
+def run_clock(xcc_ghz, value, achieved, peak, profile):
+    """The bench line's clock record: the live per-XCC shader clock of the timed
+    launches, the published peak scaled to its mean, and the profile's figure."""
+    if not xcc_ghz:
+        return {"sclk_ghz": None, "profile": profile}
+    mean = float(np.mean(list(xcc_ghz.values())))
+    at = peak * mean / 2.4
+    return {"sclk_ghz": round(mean, 3),
+            "per_xcc_ghz": {str(k): round(v, 3) for k, v in xcc_ghz.items()},
+            "source": "xs_clock_sample before and after the timed launches on their stream: "
+                      "s_memtime cycles over s_memrealtime time per compute unit, median per XCC",
+            "peak_at_that_clock": round(at, 1),
+            "value_frac_at_that_clock": round(value / at, 4),
+            "frac_at_that_clock": round(achieved / at, 4),
+            "profile": profile}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -585,8 +631,15 @@ def main():
           for i in range(0, args.steps, every)}
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    # the shader clock each XCC held over the timed launches: clock samples queued
+    # right before and right after them on the same stream
+    from sequence_attention_amd import _lib
+    Lc = _lib.lib()
+    clk_a = torch.zeros(1024 * 4, dtype=torch.int64, device=dev)
+    clk_b = torch.zeros_like(clk_a)
     torch.cuda.synchronize()
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+    wall_khz = clock_sample(Lc, clk_a, stream)
     t_start.record(stream)
     for i in range(args.steps):
         if flush is not None:
@@ -598,8 +651,10 @@ def main():
         if pair is not None:
             pair[1].record(stream)
     t_end.record(stream)
+    clock_sample(Lc, clk_b, stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
+    xcc_ghz = live_clock(clk_a.cpu().numpy(), clk_b.cpu().numpy(), wall_khz)
     launch_ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev.values()])
     ms_per_step = total_ms / args.steps
 
@@ -655,7 +710,7 @@ def main():
                      "kernel": ("attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_fp8_kernel")
                                + (" + attn_combine_kernel" if nsplit > 1 else ""),
                      "flops_per_launch": flops},
-        "clock": profile_clock(kernel_tag, w.name, achieved, peak),
+        "clock": run_clock(xcc_ghz, value, achieved, peak, profile_clock(kernel_tag, w.name, achieved, peak)),
         "plain_entry": plain_entry,
         "check": check,
     }

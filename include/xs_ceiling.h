@@ -68,6 +68,27 @@ extern "C" {
  * Returns 0 or an XS_CEIL_ERR_* code (validated before any HIP call). */
 int xs_mfma_ceiling(int mode, int waves_per_simd, int iters, float *sink, size_t sink_bytes, void *stream);
 
+/* Shader clock under a timed run.  The chip sets its clock by the power a kernel
+ * draws, so the clock a run actually held decides how its rate compares with the
+ * published peak (which assumes 2.4 GHz).  Launches one small kernel on `stream`:
+ * XS_CLOCK_GROUPS workgroups of one wave (several per compute unit); wave g
+ * stores, at out[4g .. 4g+3], its s_memtime (shader clock cycles), its
+ * s_memrealtime (a constant-rate counter of *wall_khz kHz), its XCC id (hardware
+ * register XCC_ID) and its HW_ID register (compute unit, shader array and shader
+ * engine in bits 8-15).  The shader-clock counters of different engines are not
+ * synchronised, so a sample taken before and one taken after the timed launches on
+ * the same stream are paired per compute unit (XCC and HW_ID bits 8-15): there
+ * (memtime difference) / (realtime difference) * wall_khz kHz = the mean shader
+ * clock over the interval.
+ *   out       device memory, at least XS_CLOCK_BYTES bytes, 8-byte aligned
+ *   wall_khz  host int: the constant counter's rate (hipDeviceAttributeWallClockRate)
+ *   stream    hipStream_t as void*, NULL = default stream; asynchronous
+ * Returns 0, XS_CEIL_ERR_NULL, XS_CEIL_ERR_SIZE, XS_CEIL_ERR_ALIGN or
+ * XS_CEIL_ERR_LAUNCH (arguments validated before any HIP call). */
+#define XS_CLOCK_GROUPS 1024
+#define XS_CLOCK_BYTES (XS_CLOCK_GROUPS * 4u * 8u)
+int xs_clock_sample(unsigned long long *out, size_t out_bytes, int *wall_khz, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.xs_burst_gap_tiles.restype = ci
         L.xs_mfma_ceiling.argtypes = [ci, ci, ci, vp, sz, vp]
         L.xs_mfma_ceiling.restype = ci
+        L.xs_clock_sample.argtypes = [vp, sz, ip, vp]
+        L.xs_clock_sample.restype = ci
         _lib = L
     return _lib
 

@@ -134,6 +134,21 @@ hipError_t launch_mode(int waves, float* sink, int iters, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// One wave per workgroup: the counters of the compute unit it runs on.  XCC_ID
+// is hardware register 20 (bits 3:0 the XCC), HW_ID register 4.
+__global__ __launch_bounds__(64) void clock_kernel(unsigned long long* out) {
+  if (threadIdx.x != 0) return;
+  const unsigned long long t = __builtin_amdgcn_s_memtime();
+  const unsigned long long r = __builtin_amdgcn_s_memrealtime();
+  const unsigned xcc = __builtin_amdgcn_s_getreg(20 | (3 << 11)) & 0xFu;
+  const unsigned hw = __builtin_amdgcn_s_getreg(4 | (31 << 11));
+  unsigned long long* o = out + 4 * blockIdx.x;
+  o[0] = t;
+  o[1] = r;
+  o[2] = xcc;
+  o[3] = hw;
+}
+
 }  // namespace
 }  // namespace xs
 
@@ -160,4 +175,18 @@ extern "C" int xs_mfma_ceiling(int mode, int waves_per_simd, int iters, float* s
     default: e = launch_mode<XS_CEIL_MIX_DATA>(waves_per_simd, sink, iters, s); break;
   }
   return e == hipSuccess ? 0 : XS_CEIL_ERR_LAUNCH;
+}
+
+extern "C" int xs_clock_sample(unsigned long long* out, size_t out_bytes, int* wall_khz, void* stream) {
+  using namespace xs;
+  if (!out || !wall_khz) return XS_CEIL_ERR_NULL;
+  if (out_bytes < XS_CLOCK_BYTES) return XS_CEIL_ERR_SIZE;
+  if ((uintptr_t)out % 8) return XS_CEIL_ERR_ALIGN;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return XS_CEIL_ERR_LAUNCH;
+  *wall_khz = khz;
+  hipLaunchKernelGGL(clock_kernel, dim3(XS_CLOCK_GROUPS), dim3(64), 0, (hipStream_t)stream, out);
+  return hipGetLastError() == hipSuccess ? 0 : XS_CEIL_ERR_LAUNCH;
 }

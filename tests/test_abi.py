@@ -24,7 +24,7 @@ def test_library_exports_every_declared_function():
                           "xs_attn_fwd_ex", "xs_attn_fwd_fp8_ex", "xs_attn_workspace_size",
                           "xs_attn_split_count", "xs_attn_strerror", "xs_attn_version",
                           "xs_attn_fwd_noalloc", "xs_attn_schedule", "xs_burst_gap",
-                          "xs_burst_gap_tiles", "xs_mfma_ceiling"}
+                          "xs_burst_gap_tiles", "xs_mfma_ceiling", "xs_clock_sample"}
     L = _lib.lib()
     for n in names:
         assert getattr(L, n) is not None
@@ -264,6 +264,16 @@ def test_mfma_ceiling_validates_before_any_launch():
         assert L.xs_mfma_ceiling(mode, waves, iters, S, n, None) == -2
     assert L.xs_mfma_ceiling(0, 2, 16, S, n - 4, None) == -3
     assert L.xs_mfma_ceiling(0, 2, 16, S + 2, n, None) == -4
+
+
+def test_clock_sample_validates_before_any_launch():
+    L = _lib.lib()
+    S, n = 0x60000000, 1024 * 4 * 8
+    khz = ctypes.c_int(0)
+    assert L.xs_clock_sample(None, n, ctypes.byref(khz), None) == -1
+    assert L.xs_clock_sample(S, n, None, None) == -1
+    assert L.xs_clock_sample(S, n - 8, ctypes.byref(khz), None) == -3
+    assert L.xs_clock_sample(S + 4, n, ctypes.byref(khz), None) == -4
 
 
 def test_noalloc_entry_validates_before_any_hip_call():

@@ -70,3 +70,22 @@ def test_amd_smi_text_parsed():
     # socket power and the mean of the GFX clocks only (not the memory clock, not the limits)
     assert bench.smi_parse(SMI_TEXT) == (1331.0, 1766.0)
     assert bench.smi_parse("GPU: 0\n    POWER:\n        SOCKET_POWER: N/A\n") is None
+
+
+def test_live_clock_pairs_samples_by_compute_unit():
+    # constant counter 100 MHz (100000 kHz), 1 ms between the samples.  XCC 0: CUs
+    # 0x01 and 0x02 ran 1.7e6 and 1.9e6 cycles (median 1.8 GHz); XCC 5: CU 0x01 2.0e6;
+    # hw_id bits outside 8-15 do not matter; CU 0x03 of XCC 0 appears in one sample
+    # only and is skipped; later records of a CU already seen are ignored.  The
+    # counters of different CUs are not synchronised.
+    a = [[1000, 500, 0, 0x0107], [9_000_000, 500, 0, 0x0200], [7000, 510, 5, 0x0100],
+         [1, 1, 0, 0x0300], [9, 9, 0, 0x0100]]
+    b = [[1000 + 1_700_000, 500 + 100_000, 0, 0x0155], [9_000_000 + 1_900_000, 500 + 100_000, 0, 0x0200],
+         [7000 + 2_000_000, 510 + 100_000, 5, 0x0100]]
+    ghz = bench.live_clock(a, b, 100000)
+    assert set(ghz) == {0, 5}
+    assert abs(ghz[0] - 1.8) < 1e-9 and abs(ghz[5] - 2.0) < 1e-9
+    rec = bench.run_clock(ghz, 1200.0, 1190.0, 2500.0, None)
+    assert rec["sclk_ghz"] == 1.9
+    assert abs(rec["peak_at_that_clock"] - 2500.0 * 1.9 / 2.4) < 0.1
+    assert bench.run_clock({}, 1.0, 1.0, 2500.0, None)["sclk_ghz"] is None
