@@ -76,7 +76,7 @@ def parse():
                     help="instead of the benchmark, run the matrix-core ceiling probes "
                          "(xs_mfma_ceiling: MFMA rate next to LDS operand reads and softmax "
                          "vector work, one and two waves per SIMD); with --power, the socket "
-                         "power and matrix work per joule of probe modes 0, 5, 7 and 8 instead")
+                         "power and matrix work per joule of probe modes 0, 5, 7, 8, 9 and 10 instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -101,7 +101,9 @@ CEILING_MODES = ["mfma only", "1 KiB ds_read_b128 per MFMA", "0.5 KiB ds_read_b1
                  "softmax work + 1 KiB ds_read_b128 per MFMA (32 query rows per wave)",
                  "softmax work + 0.5 KiB ds_read_b128 per MFMA (64 query rows per wave)",
                  "mfma only, random bf16 operands",
-                 "softmax work + 1 KiB ds_read_b128 per MFMA, random bf16 data"]
+                 "softmax work + 1 KiB ds_read_b128 per MFMA, random bf16 data",
+                 "mfma only, random bf16 operands, as two 16x16x32 MFMAs",
+                 "mode 8 with two 16x16x32 MFMAs sharing the LDS fragment"]
 
 
 def ceilings(iters, reps=5):
@@ -141,7 +143,7 @@ def ceilings(iters, reps=5):
     return res
 
 
-def ceiling_power(seconds, modes=(0, 5, 7, 8), iters=2048):
+def ceiling_power(seconds, modes=(0, 5, 7, 8, 9, 10), iters=2048):
     """Socket power, GFX clock and matrix work per joule of probe modes run back to back
     (two waves per SIMD) for `seconds` each, sampled as in power_run."""
     from sequence_attention_amd import _lib

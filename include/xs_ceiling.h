@@ -40,7 +40,14 @@ extern "C" {
 #define XS_CEIL_MIX_DATA 8   /* XS_CEIL_MIX on such data: the LDS holds those values, the softmax
                                stand-in takes a new argument per MFMA (the A operand's first word
                                read as fp32) and its probabilities, 2^-6 .. 2^2, are the B operand */
-#define XS_CEIL_MODES 9
+#define XS_CEIL_MFMA16_DATA 9 /* XS_CEIL_MFMA_DATA with each 32x32x16 MFMA replaced by two
+                               v_mfma_f32_16x16x32_bf16 (the same multiply-adds; a quarter of
+                               the accumulator registers read and written per instruction) */
+#define XS_CEIL_MIX16_DATA 10 /* XS_CEIL_MIX_DATA with each 32x32x16 MFMA replaced by two
+                               v_mfma_f32_16x16x32_bf16 that share the LDS fragment as A operand
+                               (two 16-query tiles; the second's B operand is the next MFMA's
+                               LDS fragment, random data already in registers) */
+#define XS_CEIL_MODES 11
 
 #define XS_CEIL_SINK_BYTES (1024u * 512u * 4u) /* smallest sink accepted */
 

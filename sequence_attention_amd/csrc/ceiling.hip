@@ -13,6 +13,11 @@ constexpr int kInner = 16;                    // MFMAs per loop trip
 constexpr int kLead = 3;                      // LDS reads issued this many MFMAs ahead
 constexpr int kGroups = 1024;
 
+__device__ __forceinline__ f32x4 mfma16_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
 // A bf16 operand value of the kind the attention kernels multiply: random sign,
 // exponent 2^-3 .. 2^3, random mantissa (never zero, subnormal, Inf or NaN).
 __device__ __forceinline__ uint32_t bf16_sample(uint32_t h) {
@@ -38,17 +43,21 @@ __global__ __launch_bounds__(THREADS, 1) void ceiling_kernel(float* sink, int it
   __shared__ __attribute__((aligned(1024))) uint8_t smem[96 * 1024];
   uint8_t XS_LDS* lds = (uint8_t XS_LDS*)smem;
   const int lane = threadIdx.x & 63;
-  constexpr bool kData = MODE == XS_CEIL_MFMA_DATA || MODE == XS_CEIL_MIX_DATA;
+  constexpr bool kData = MODE == XS_CEIL_MFMA_DATA || MODE == XS_CEIL_MIX_DATA || MODE == XS_CEIL_MFMA16_DATA ||
+                        MODE == XS_CEIL_MIX16_DATA;
+  constexpr bool k16 = MODE == XS_CEIL_MFMA16_DATA || MODE == XS_CEIL_MIX16_DATA;
+  constexpr bool kRegf = MODE == XS_CEIL_MFMA_DATA || MODE == XS_CEIL_MFMA16_DATA;
   for (uint32_t i = threadIdx.x * 4; i < sizeof(smem); i += THREADS * 4)
     *(uint32_t XS_LDS*)(lds + i) = kData ? data_word(i >> 2) : i * 2654435761u;
   __syncthreads();
 
-  constexpr bool kPerMfma =
-      MODE == XS_CEIL_LDS_1K || MODE == XS_CEIL_TR16_1K || MODE == XS_CEIL_MIX || MODE == XS_CEIL_MIX_DATA;
+  constexpr bool kPerMfma = MODE == XS_CEIL_LDS_1K || MODE == XS_CEIL_TR16_1K || MODE == XS_CEIL_MIX ||
+                           MODE == XS_CEIL_MIX_DATA || MODE == XS_CEIL_MIX16_DATA;
   constexpr bool kHalf = MODE == XS_CEIL_LDS_HALF || MODE == XS_CEIL_MIX_HALF;
-  constexpr bool kSoftmax =
-      MODE == XS_CEIL_SOFTMAX || MODE == XS_CEIL_MIX || MODE == XS_CEIL_MIX_HALF || MODE == XS_CEIL_MIX_DATA;
+  constexpr bool kSoftmax = MODE == XS_CEIL_SOFTMAX || MODE == XS_CEIL_MIX || MODE == XS_CEIL_MIX_HALF ||
+                           MODE == XS_CEIL_MIX_DATA || MODE == XS_CEIL_MIX16_DATA;
   f32x16 acc[4] = {};
+  f32x4 acc16[8] = {};
   const u32x4 a = {lane * 3u, lane * 5u, 7u, 9u};
   // softmax stand-in, as in the bf16 kernel: p = 2^(x c - m) of eight independent
   // chains, their row sum, and the pairs rounded to bf16 as the next MFMAs' B operand
@@ -71,7 +80,7 @@ __global__ __launch_bounds__(THREADS, 1) void ceiling_kernel(float* sink, int it
   // MFMAs-only data mode: eight register-held fragments of the LDS data, A and B
   // rotating through them so that every MFMA sees new operand bits
   u32x4 regf[8];
-  if (MODE == XS_CEIL_MFMA_DATA)
+  if (kRegf)
 #pragma unroll
     for (int i = 0; i < 8; ++i) regf[i] = lds_read_b128(lane_base + i * 1024);
   if (kPerMfma || kHalf)
@@ -84,7 +93,7 @@ __global__ __launch_bounds__(THREADS, 1) void ceiling_kernel(float* sink, int it
     for (int k = 0; k < kInner; ++k) {
       u32x4 op = a;
       u32x4 opb = u32x4{pk[0], pk[1], pk[2], pk[3]};
-      if (MODE == XS_CEIL_MFMA_DATA) {
+      if (kRegf) {
         op = regf[k & 7];
         opb = regf[(k + 3) & 7];
       } else if (kPerMfma) {
@@ -94,7 +103,19 @@ __global__ __launch_bounds__(THREADS, 1) void ceiling_kernel(float* sink, int it
         if ((k & 1) == 0) frag[((k >> 1) + kLead) % (kLead + 1)] = read(tb, (k >> 1) + kLead);
         op = frag[(k >> 1) % (kLead + 1)];
       }
-      acc[k & 3] = mfma_bf16(op, opb, acc[k & 3]);
+      if (MODE == XS_CEIL_MFMA16_DATA) {
+        // the same multiply-adds as one 32x32x16 MFMA, as two 16x16x32 ones
+        acc16[(2 * k) & 7] = mfma16_bf16(op, opb, acc16[(2 * k) & 7]);
+        acc16[(2 * k + 1) & 7] = mfma16_bf16(regf[(k + 1) & 7], opb, acc16[(2 * k + 1) & 7]);
+      } else if (MODE == XS_CEIL_MIX16_DATA) {
+        // one LDS fragment as the A operand of two 16x16x32 MFMAs (two 16-query
+        // tiles); the second B operand is the next MFMA's fragment (random data
+        // already in registers)
+        acc16[(2 * k) & 7] = mfma16_bf16(op, opb, acc16[(2 * k) & 7]);
+        acc16[(2 * k + 1) & 7] = mfma16_bf16(op, frag[(k + 1) % (kLead + 1)], acc16[(2 * k + 1) & 7]);
+      } else {
+        acc[k & 3] = mfma_bf16(op, opb, acc[k & 3]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (kSoftmax) {
         // data mode: the exponent's argument is a new value each time (this MFMA's
@@ -118,9 +139,12 @@ __global__ __launch_bounds__(THREADS, 1) void ceiling_kernel(float* sink, int it
   if (kPerMfma || kHalf)
 #pragma unroll
     for (int k = 0; k <= kLead; ++k) s += (float)(frag[k][0] ^ frag[k][3]);
-  if (MODE == XS_CEIL_MFMA_DATA)
+  if (kRegf)
 #pragma unroll
     for (int k = 0; k < 8; ++k) s += (float)(regf[k][1] & 0xFFu);
+  if (k16)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += acc16[k][0] + acc16[k][3];
   sink[blockIdx.x * 512 + threadIdx.x] = s;
 }
 
@@ -172,6 +196,8 @@ extern "C" int xs_mfma_ceiling(int mode, int waves_per_simd, int iters, float* s
     case XS_CEIL_MIX: e = launch_mode<XS_CEIL_MIX>(waves_per_simd, sink, iters, s); break;
     case XS_CEIL_MIX_HALF: e = launch_mode<XS_CEIL_MIX_HALF>(waves_per_simd, sink, iters, s); break;
     case XS_CEIL_MFMA_DATA: e = launch_mode<XS_CEIL_MFMA_DATA>(waves_per_simd, sink, iters, s); break;
+    case XS_CEIL_MFMA16_DATA: e = launch_mode<XS_CEIL_MFMA16_DATA>(waves_per_simd, sink, iters, s); break;
+    case XS_CEIL_MIX16_DATA: e = launch_mode<XS_CEIL_MIX16_DATA>(waves_per_simd, sink, iters, s); break;
     default: e = launch_mode<XS_CEIL_MIX_DATA>(waves_per_simd, sink, iters, s); break;
   }
   return e == hipSuccess ? 0 : XS_CEIL_ERR_LAUNCH;
