@@ -106,6 +106,7 @@ struct Fp8State {
   float m, alpha;
   float l32;         // lane-local fp32 sum of the unquantised p (kept only when C::LSE)
   float lb;          // l32 before the current block's probabilities (C::LSE)
+  float mx0;         // lane max of the next block's key tile 0 (end of step A, without C::LSE)
   bool rescale;
 };
 
@@ -159,6 +160,20 @@ __device__ __forceinline__ void mask_tail8(Scores8<C>& sc, int kv0, int S, int l
       const int key = kv0 + nt * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
       if (key >= S) sc.s[nt][r] = -INFINITY;
     }
+}
+
+// Masks a partial block that step A has just scored.  Without the log-sum-exp,
+// step A already took the lane max of its key tile 0 for step B: take it again
+// without the masked keys.
+template <class C>
+__device__ __forceinline__ void mask_tail_next8(Scores8<C>& sc, Fp8State<C>& st, int kv0, int S, int lane) {
+  mask_tail8<C>(sc, kv0, S, lane);
+  if (!C::LSE) {
+    float mx = sc.s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc.s[0][r]);
+    st.mx0 = mx;
+  }
 }
 
 template <class C>
@@ -391,6 +406,15 @@ __device__ __forceinline__ void step_a8(Scores8<C>& nxt, const Scores8<C>& cur, 
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       if (q * NF / 4 == f) pe[q] = prob4<C>(cur, 1, q, pa, pb, lsum);
+    if (!C::LSE && f == NF - 1) {
+      // the next block's key tile 0 is complete (its last k-step was the MFMA
+      // before this one): half of its row max here, the other half in step B
+      float mx = nxt.s[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, nxt.s[0][r]);
+      pin(mx);
+      st.mx0 = mx;
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -439,62 +463,58 @@ __device__ __forceinline__ void step_b8(Fp8State<C>& st, const Scores8<C>& nxt,
     return __builtin_bit_cast(
         i32x8, (u32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]}));
   };
-  float mx = nxt.s[0][0];
+  float mx = C::LSE ? 0.0f : st.mx0;
   float neg_m = 0.0f, lsum = 0.0f, pa = 0.0f, pb = 0.0f;
   uint32_t w[4];
   f32x4 pe[4];
   i32x8 vf[R];
 #pragma unroll
   for (int f = 0; f < LEAD; ++f) vf[f] = vread(f);
+  if (C::LSE) {
+    neg_m = -st.m;
+    pa = prob_a<C>(c);
+    pb = prob_b<C>(neg_m);
+    lsum = st.l32;
+    st.lb = st.l32;
+  }
+  // the micro-step that computes probability group q (keys 4q..4q+3 of each
+  // half-wave's 32); it is packed one micro-step later.  Without the log-sum-exp
+  // the groups follow the max decision of micro-step 0 (D = 128: groups 0, 1 in
+  // micro-step 1, 2 in 2, 3 in 3); with it, one group per micro-step.
+  auto at = [&](int q) { return C::LSE ? q * NF / 4 : 1 + q * (NF - 1) / 4; };
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     if (f + LEAD < NF) vf[(f + LEAD) % R] = vread(f + LEAD);
     st.o[f] = mfma_fp8(vf[f % R], pf, st.o[f]);
     if (!C::LSE && f == NF - 1) st.lt = mfma_rowsum(ones, pf, st.lt);
-    if (f < HALF) {
-      // Without the log-sum-exp: the next block's row max and the lazy move of
-      // the running max.  With it, the max is not taken here: the fp32 row sums
-      // detect a probability above 2^TAU at the end of the next step A.
-      if (!C::LSE) {
-        constexpr int EPS = 32 / HALF;  // max over the 32 scores of the next block
+    if (!C::LSE && f == 0) {
+      // the rest of the next block's row max and the lazy move of the running
+      // max (the O rescale waits for the next step B)
 #pragma unroll
-        for (int ee = 0; ee < EPS; ++ee) {
-          const int e = f * EPS + ee;
-          mx = fmaxf(mx, nxt.s[e / 16][e % 16]);
-        }
-        pin(mx);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, nxt.s[1][r]);
+      const float mnew = max_halves(mx) * c;
+      const bool need = mnew > st.m + C::TAU;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float a = need ? fast_exp2(st.m - mnew) : 1.0f;
+        st.m = need ? mnew : st.m;
+        st.alpha *= a;
+        st.rescale = true;
       }
-      if (f == HALF - 1) {
-        if (!C::LSE) {
-          // lazy move of the running max (the O rescale waits for the next step B)
-          const float mnew = max_halves(mx) * c;
-          const bool need = mnew > st.m + C::TAU;
-          if (__builtin_amdgcn_ballot_w64(need)) {
-            const float a = need ? fast_exp2(st.m - mnew) : 1.0f;
-            st.m = need ? mnew : st.m;
-            st.alpha *= a;
-            st.rescale = true;
-          }
-        }
-        neg_m = -st.m;
-        pa = prob_a<C>(c);
-        pb = prob_b<C>(neg_m);
-        lsum = st.l32;
-        if (C::LSE) st.lb = st.l32;
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (f > HALF && q * HALF / 4 == f - 1 - HALF) w[q] = packp4<C>(pe[q]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (q * HALF / 4 == f - HALF) pe[q] = prob4<C>(nxt, 0, q, pa, pb, lsum);
+      neg_m = -st.m;
+      pa = prob_a<C>(c);
+      pb = prob_b<C>(neg_m);
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (f >= 1 && at(q) == f - 1) w[q] = packp4<C>(pe[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (at(q) == f) pe[q] = prob4<C>(nxt, 0, q, pa, pb, lsum);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    if (q * HALF / 4 == NF - 1 - HALF) w[q] = packp4<C>(pe[q]);
+    if (at(q) == NF - 1) w[q] = packp4<C>(pe[q]);
   st.l32 = lsum;
   st.p0 = u32x4{w[0], w[1], w[2], w[3]};
   keep(st.p0);
@@ -654,10 +674,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
       ld_v(j + 2, 2);
       ld_v(j + 3, 3);
       step_a8<C, 1>(sb, sa, st, lds, off, c);  // block j
-      if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
+      if (j + 1 >= nfull) mask_tail_next8<C>(sb, st, (j + 1) * BN, S, lane);
       step_b8<C, 0>(st, sb, lds, off, c, ones);
       step_a8<C, 2>(sa, sb, st, lds, off, c);  // block j+1
-      if (j + 2 >= nfull) mask_tail8<C>(sa, (j + 2) * BN, S, lane);
+      if (j + 2 >= nfull) mask_tail_next8<C>(sa, st, (j + 2) * BN, S, lane);
       step_b8<C, 1>(st, sa, lds, off, c, ones);
 
       wait_vmcnt<0>();
@@ -667,10 +687,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
       ld_v(j + 4, 0);
       if (j + 5 < je) ld_v(j + 5, 1);
       step_a8<C, 3>(sb, sa, st, lds, off, c);  // block j+2
-      if (j + 3 >= nfull) mask_tail8<C>(sb, (j + 3) * BN, S, lane);
+      if (j + 3 >= nfull) mask_tail_next8<C>(sb, st, (j + 3) * BN, S, lane);
       step_b8<C, 2>(st, sb, lds, off, c, ones);
       step_a8<C, 0>(sa, sb, st, lds, off, c);  // block j+3
-      if (j + 4 >= nfull) mask_tail8<C>(sa, (j + 4) * BN, S, lane);
+      if (j + 4 >= nfull) mask_tail_next8<C>(sa, st, (j + 4) * BN, S, lane);
       step_b8<C, 3>(st, sa, lds, off, c, ones);
     }
     // the last one to four blocks j .. je-1 (stages 0..3, scores of block j in sa)
@@ -683,19 +703,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
       if (r > 3) ld_v(j + 3, 3);
       if (r > 1) {
         step_a8<C, 1>(sb, sa, st, lds, off, c);  // block j
-        if (j + 1 >= nfull) mask_tail8<C>(sb, (j + 1) * BN, S, lane);
+        if (j + 1 >= nfull) mask_tail_next8<C>(sb, st, (j + 1) * BN, S, lane);
         step_b8<C, 0>(st, sb, lds, off, c, ones);
       }
       if (r > 2) {
         step_a8<C, 2>(sa, sb, st, lds, off, c);  // block j+1
-        if (j + 2 >= nfull) mask_tail8<C>(sa, (j + 2) * BN, S, lane);
+        if (j + 2 >= nfull) mask_tail_next8<C>(sa, st, (j + 2) * BN, S, lane);
         step_b8<C, 1>(st, sa, lds, off, c, ones);
         wait_vmcnt<0>();
         __syncthreads();
       }
       if (r > 3) {
         step_a8<C, 3>(sb, sa, st, lds, off, c);  // block j+2
-        if (j + 3 >= nfull) mask_tail8<C>(sb, (j + 3) * BN, S, lane);
+        if (j + 3 >= nfull) mask_tail_next8<C>(sb, st, (j + 3) * BN, S, lane);
         step_b8<C, 2>(st, sb, lds, off, c, ones);
       }
       // the last block, j + r - 1: scores in sa when r is odd, keys 0..31 done
