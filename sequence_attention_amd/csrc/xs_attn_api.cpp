@@ -20,7 +20,7 @@ static __device__ __align__(256) uint8_t scratch[XS_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // |scale| * log2(e): the kernels compute p = 2^(s*c - m).  A zero scale is

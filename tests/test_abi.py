@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert xs.xs_attn_version() == 10300
+    assert xs.xs_attn_version() == 10400
     for code in (XS_OK, XS_ERR_NULL, XS_ERR_SHAPE, XS_ERR_UNSUPPORTED, XS_ERR_ALIGN, XS_ERR_LAUNCH,
                  XS_ERR_OVERLAP, XS_ERR_WORKSPACE, XS_ERR_SCRATCH, 12345):
         s = xs.xs_attn_strerror(code)
