@@ -76,7 +76,7 @@ def parse():
                     help="instead of the benchmark, run the matrix-core ceiling probes "
                          "(xs_mfma_ceiling: MFMA rate next to LDS operand reads and softmax "
                          "vector work, one and two waves per SIMD); with --power, the socket "
-                         "power and matrix work per joule of probe modes 0, 5, 7, 8, 9 and 10 instead")
+                         "power and matrix work per joule of probe modes 0, 5 and 7-12 instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -100,10 +100,15 @@ CEILING_MODES = ["mfma only", "1 KiB ds_read_b128 per MFMA", "0.5 KiB ds_read_b1
                  "softmax work per MFMA (fma, exp, add, half a bf16 pack)",
                  "softmax work + 1 KiB ds_read_b128 per MFMA (32 query rows per wave)",
                  "softmax work + 0.5 KiB ds_read_b128 per MFMA (64 query rows per wave)",
-                 "mfma only, random bf16 operands",
-                 "softmax work + 1 KiB ds_read_b128 per MFMA, random bf16 data",
-                 "mfma only, random bf16 operands, as two 16x16x32 MFMAs",
-                 "mode 8 with two 16x16x32 MFMAs sharing the LDS fragment"]
+                 "mfma only, N(0, 1) bf16 operands",
+                 "softmax work + 1 KiB ds_read_b128 per MFMA, N(0, 1) bf16 data",
+                 "mfma only, N(0, 1) bf16 operands, as two 16x16x32 MFMAs",
+                 "mode 8 with two 16x16x32 MFMAs sharing the LDS fragment",
+                 "fp8 MFMAs (32x32x64, 64 clocks) only, e4m3 operands like the fp8 share's",
+                 "fp8 kernel's mix: 2 KiB LDS operand + codes (4 FMA, 2 pknorm, perm, 2 max3) per MFMA, e4m3 data"]
+# modes whose MFMA is the fp8 32x32x64 one (four times the multiply-adds of a bf16
+# 32x32x16, in twice the clocks)
+CEILING_FP8_MODES = (11, 12)
 
 
 def ceilings(iters, reps=5):
@@ -143,7 +148,7 @@ def ceilings(iters, reps=5):
     return res
 
 
-def ceiling_power(seconds, modes=(0, 5, 7, 8, 9, 10), iters=2048):
+def ceiling_power(seconds, modes=(0, 5, 7, 8, 9, 10, 11, 12), iters=2048):
     """Socket power, GFX clock and matrix work per joule of probe modes run back to back
     (two waves per SIMD) for `seconds` each, sampled as in power_run."""
     from sequence_attention_amd import _lib
@@ -159,7 +164,8 @@ def ceiling_power(seconds, modes=(0, 5, 7, 8, 9, 10), iters=2048):
                                           sink.numel() * 4, ctypes.c_void_p(stream.cuda_stream)))
         step()
         torch.cuda.synchronize()
-        out.append({"mode": mode, "stream": CEILING_MODES[mode], **power_run(step, seconds, flops)})
+        f = flops * (4 if mode in CEILING_FP8_MODES else 1)
+        out.append({"mode": mode, "stream": CEILING_MODES[mode], **power_run(step, seconds, f)})
         print(f"ceiling power mode {mode} done", file=sys.stderr, flush=True)
     return out
 

@@ -13,7 +13,7 @@
  * each stream alone and under both, so the kernel's own MFMA-busy fraction
  * can be read against them.  Modes 0-6 multiply fixed or arbitrary bit
  * patterns (little switching activity, and NaN once an accumulator overflows);
- * modes 7 and 8 repeat modes 0 and 5 on random finite bf16 data, which draws
+ * modes 7-12 use data distributed like the workloads' inputs, which draws
  * the power that real inputs draw.
  */
 #ifndef XS_CEILING_H
@@ -33,13 +33,13 @@ extern "C" {
                                v_exp_f32, one v_add_f32 and half a v_cvt_pk_bf16_f32, no LDS */
 #define XS_CEIL_MIX 5       /* XS_CEIL_SOFTMAX + XS_CEIL_LDS_1K: the mix of 32 query rows per wave */
 #define XS_CEIL_MIX_HALF 6  /* XS_CEIL_SOFTMAX + XS_CEIL_LDS_HALF: the mix of 64 query rows per wave */
-#define XS_CEIL_MFMA_DATA 7  /* XS_CEIL_MFMA with operands of the kind the kernel multiplies: A and B
-                               rotate through eight register-held fragments of random bf16 values
-                               (random sign and mantissa, magnitudes 2^-3 .. 2^4), so every MFMA
-                               switches operand bits as the attention kernel's do */
+#define XS_CEIL_MFMA_DATA 7  /* XS_CEIL_MFMA with operands like the bf16 workloads' inputs: A and B
+                               rotate through eight register-held fragments of N(0, 1) draws in
+                               bf16, so every MFMA switches operand bits as the attention kernel's do */
 #define XS_CEIL_MIX_DATA 8   /* XS_CEIL_MIX on such data: the LDS holds those values, the softmax
                                stand-in takes a new argument per MFMA (the A operand's first word
-                               read as fp32) and its probabilities, 2^-6 .. 2^2, are the B operand */
+                               read as fp32) and its probabilities, 2^(1.44 x - 5) as the video
+                               share's scores relative to their running max, are the B operand */
 #define XS_CEIL_MFMA16_DATA 9 /* XS_CEIL_MFMA_DATA with each 32x32x16 MFMA replaced by two
                                v_mfma_f32_16x16x32_bf16 (the same multiply-adds; a quarter of
                                the accumulator registers read and written per instruction) */
@@ -47,7 +47,16 @@ extern "C" {
                                v_mfma_f32_16x16x32_bf16 that share the LDS fragment as A operand
                                (two 16-query tiles; the second's B operand is the next MFMA's
                                LDS fragment, random data already in registers) */
-#define XS_CEIL_MODES 11
+#define XS_CEIL_FP8_DATA 11     /* v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3, 64 clocks, four times
+                                   the multiply-adds of one bf16 MFMA) alone on operands like the fp8
+                                   workload's (N(0, 1) draws quantised to e4m3 with amax 5 -> 448),
+                                   rotating through eight register-held fragments */
+#define XS_CEIL_FP8_MIX_DATA 12 /* the fp8 kernel's per-MFMA mix on such data: 2 KiB of LDS operand
+                                   (two ds_read_b128) as A, and as B e4m3 codes made per MFMA by
+                                   four FMAs, two v_cvt_pknorm_u16_f32, one v_perm_b32 and two
+                                   three-input maxima from an earlier accumulator (codes 54 +- 12,
+                                   as the fp8 share's probabilities) */
+#define XS_CEIL_MODES 13
 
 #define XS_CEIL_SINK_BYTES (1024u * 512u * 4u) /* smallest sink accepted */
 

@@ -259,7 +259,7 @@ def test_mfma_ceiling_validates_before_any_launch():
     L = _lib.lib()
     S, n = 0x60000000, 1024 * 512 * 4
     assert L.xs_mfma_ceiling(0, 2, 16, None, n, None) == -1
-    for mode, waves, iters in ((-1, 2, 16), (11, 2, 16), (0, 0, 16), (0, 3, 16), (0, 2, 0),
+    for mode, waves, iters in ((-1, 2, 16), (13, 2, 16), (0, 0, 16), (0, 3, 16), (0, 2, 0),
                                (0, 2, (1 << 20) + 1)):
         assert L.xs_mfma_ceiling(mode, waves, iters, S, n, None) == -2
     assert L.xs_mfma_ceiling(0, 2, 16, S, n - 4, None) == -3
