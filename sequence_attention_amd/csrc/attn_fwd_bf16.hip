@@ -655,9 +655,11 @@ __device__ __forceinline__ void key_pass(Bf16State<C>& st, const AttnArgs& a, Pi
   // blocks i, i+1 (i - jb even) the loads of K_{i+1}, K_{i+2}, V_i, V_{i+1}
   // (issued at the previous barrier) are complete and every wave is done
   // with blocks i-2, i-1, so K_{i+3}, K_{i+4}, V_{i+2}, V_{i+3} go into the
-  // stages those blocks used.  Entering a step for block i: its scores are in
-  // one buffer with their max taken.  Four blocks per trip keep the stages
-  // and score buffers static.
+  // stages those blocks used, one before each of the next four steps (spread
+  // out, not all at the barrier where the eight waves' bursts of LDS writes
+  // would meet their operand reads: 0.7 % faster).  Entering a step for block
+  // i: its scores are in one buffer with their max taken.  Four blocks per
+  // trip keep the stages and score buffers static.
   auto ld_k = [&](int i, int stage) {
     load_tile<C>(kbase, row_stride, i * BN, pa.kcur.at(i), S, kbuf(stage), koff, wave);
   };
@@ -669,27 +671,27 @@ __device__ __forceinline__ void key_pass(Bf16State<C>& st, const AttnArgs& a, Pi
     wait_vmcnt<0>();
     __syncthreads();
     ld_k(j + 3, 3);
-    ld_k(j + 4, 0);
-    ld_v(j + 2, 2);
-    ld_v(j + 3, 3);
     step1<C, 1, CHECK>(sb, sa, st, lds, off, c);  // block j
     if (j + 1 >= nfull) mask_tail<C>(sb, (j + 1) * BN, S, lane);
+    ld_v(j + 2, 2);
     step2<C, 0, CHECK>(st, sa, lds, off, c);
+    ld_k(j + 4, 0);
     step1<C, 2, CHECK>(sa, sb, st, lds, off, c);  // block j+1
     if (j + 2 >= nfull) mask_tail<C>(sa, (j + 2) * BN, S, lane);
+    ld_v(j + 3, 3);
     step2<C, 1, CHECK>(st, sb, lds, off, c);
 
     wait_vmcnt<0>();
     __syncthreads();
     if (j + 5 < je) ld_k(j + 5, 1);
-    if (j + 6 < je) ld_k(j + 6, 2);
-    ld_v(j + 4, 0);
-    if (j + 5 < je) ld_v(j + 5, 1);
     step1<C, 3, CHECK>(sb, sa, st, lds, off, c);  // block j+2
     if (j + 3 >= nfull) mask_tail<C>(sb, (j + 3) * BN, S, lane);
+    ld_v(j + 4, 0);
     step2<C, 2, CHECK>(st, sa, lds, off, c);
+    if (j + 6 < je) ld_k(j + 6, 2);
     step1<C, 0, CHECK>(sa, sb, st, lds, off, c);  // block j+3
     if (j + 4 >= nfull) mask_tail<C>(sa, (j + 4) * BN, S, lane);
+    if (j + 5 < je) ld_v(j + 5, 1);
     step2<C, 3, CHECK>(st, sb, lds, off, c);
   }
   // the last one to four blocks j .. je-1 (stages 0..3, scores of block j in sa)
