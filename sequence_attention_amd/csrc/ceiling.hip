@@ -155,13 +155,14 @@ __global__ __launch_bounds__(THREADS, 1) void ceiling_kernel(float* sink, int it
 
 
 // The fp8 modes: v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, 64 clocks, four
-// times the multiply-adds of a bf16 32x32x16) on e4m3 data like the fp8 workload's.  XS_CEIL_FP8_DATA:
-// A and B rotate through eight register-held 32-byte fragments.  XS_CEIL_FP8_MIX:
-// the fp8 attention kernel's per-MFMA work -- 2 KiB of LDS operand (two
-// ds_read_b128, read three MFMAs ahead) as A, and as B the e4m3 codes of its
-// probabilities: per MFMA four FMAs, two normalised 16-bit conversions, one byte
-// permutation and two three-input maxima on scores from the accumulator two
-// MFMAs back.
+// times the multiply-adds of a bf16 32x32x16) on e4m3 data like the fp8
+// workload's.  XS_CEIL_FP8_DATA: A and B rotate through eight register-held
+// 32-byte fragments.  XS_CEIL_FP8_MIX_DATA: the fp8 attention kernel's per-MFMA
+// work -- 2 KiB of LDS operand (two ds_read_b128, read three MFMAs ahead) as A,
+// and as B the e4m3 codes of its probabilities: per MFMA four FMAs, two
+// normalised 16-bit conversions, one byte permutation (and a mask that keeps the
+// codes below the NaN code, one instruction the kernel does not need) and two
+// three-input maxima on scores from the accumulator two MFMAs back.
 template <int MODE, int THREADS>
 __global__ __launch_bounds__(THREADS, 1) void ceiling_fp8_kernel(float* sink, int iters) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[96 * 1024];
