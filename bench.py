@@ -343,18 +343,30 @@ def cpu_baseline(w, inp, target_s):
 
     threads = oracle.default_threads()
     per_row = 4.0 * w.S * w.D  # algorithmic flops of one query row
-    n = max(threads, 8)
-    rows = workloads.sample_rows(w, n, seed=11)
-    t0 = time.perf_counter()
-    oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, inp["scale"], inp["descales"], threads)
-    dt = time.perf_counter() - t0
-    n = int(min(max(n, n * target_s / max(dt, 1e-6)), w.B * w.S * w.H))
-    n = max(threads, (n // threads) * threads)
+    total = w.B * w.S * w.H
+
+    def probe(n, seed):
+        rows = workloads.sample_rows(w, n, seed=seed)
+        t0 = time.perf_counter()
+        oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, inp["scale"], inp["descales"],
+                              threads)
+        return time.perf_counter() - t0
+
+    # Each oracle call first decodes the whole of q, k and v once, a fixed cost
+    # that a small probe would take for per-row time: two probe sizes separate
+    # the two, and the sample is sized so that the timed call lasts target_s.
+    n1 = min(max(threads, 8), total)
+    n2 = min(4 * n1, total)
+    t1 = probe(n1, 11)
+    t2 = probe(n2, 11)
+    per = (t2 - t1) / (n2 - n1) if n2 > n1 and t2 > t1 else t2 / n2
+    fixed = max(0.0, t2 - per * n2)
+    n = int(min(max(n1, (target_s - fixed) / max(per, 1e-9)), total))
+    n = max(min(threads, total), (n // threads) * threads)
     rows = workloads.sample_rows(w, n, seed=12)
     t0 = time.perf_counter()
     oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, inp["scale"], inp["descales"], threads)
     dt = time.perf_counter() - t0
-    total = w.B * w.S * w.H
     return {
         "value": per_row * len(rows) / dt / 1e12,
         "unit": "TFLOP/s",
