@@ -53,7 +53,8 @@ extern "C" {
 #define XS_ERR_OVERLAP (-6)     /* out_packed, lse or the workspace overlaps another buffer */
 #define XS_ERR_WORKSPACE (-7)   /* workspace smaller than xs_attn_workspace_size() */
 #define XS_ERR_SCRATCH (-8)     /* xs_attn_fwd_noalloc: partials exceed its static scratch */
-/* (XS_ERR_UNSUPPORTED also when B*H_local*ceil(S/256) exceeds 2^31 - 1 query tiles.) */
+/* (XS_ERR_UNSUPPORTED also when B*H_local*ceil(S/128) exceeds 2^31 - 1 half-height query
+   tiles.) */
 
 /* Attention forward over bf16 inputs with the destination-ordered epilogue.
  *   q, k, v     bf16 [B][S][H_local][D], device memory (read only)
@@ -181,13 +182,31 @@ size_t xs_attn_workspace_size(int B, int S, int H_local, int D);
  * on the current device (1 = no tile is cut); 0 for invalid sizes. */
 int xs_attn_split_count(int B, int S, int H_local, int D);
 
-/* The schedule the library runs for this shape on the current device, with
- * (with_workspace != 0) or without a workspace: the number of workgroups, the
- * rounds of whole tiles each takes first, and the most pieces any remainder
- * tile is cut into (1 = none is cut).  Any output pointer may be NULL.  Returns
- * XS_OK or XS_ERR_SHAPE (sizes < 1, D not 64 or 128).  No launch. */
+/* The schedule the library runs for a bf16 call of this shape on the current
+ * device, with (with_workspace != 0) or without a workspace:
+ * xs_attn_schedule_ex(B, S, H_local, D, with_workspace, 0, groups, whole_rounds,
+ * pieces, NULL). */
 int xs_attn_schedule(int B, int S, int H_local, int D, int with_workspace, int *groups,
                      int *whole_rounds, int *pieces);
+
+/* The schedule the library runs for this shape on the current device, for a
+ * bf16 (fp8 = 0) or fp8 (fp8 != 0) call with (with_workspace != 0) or without a
+ * workspace.  Work is split into query tiles of 256 rows (8 wavefronts of 32
+ * rows each) and, inside a tile, pairs of 64-key blocks:
+ *   groups        workgroups of the first launch (0 when it has none);
+ *   whole_rounds  rounds of whole tiles each of them takes first;
+ *   pieces        the most pieces any remaining tile is cut into by their
+ *                 shares of its key blocks (1 = none is cut; cut tiles are
+ *                 merged by a second kernel);
+ *   half_tiles    bf16 calls whose schedule cuts no tile and leaves at most
+ *                 half a round of tiles after the whole rounds: those tiles
+ *                 run as 128-row half tiles (4 wavefronts) in a second launch,
+ *                 one workgroup each, so that the last round fills the chip
+ *                 (0 = none; always 0 for fp8).
+ * Any output pointer may be NULL.  Returns XS_OK or XS_ERR_SHAPE (sizes < 1, D
+ * not 64 or 128).  No launch. */
+int xs_attn_schedule_ex(int B, int S, int H_local, int D, int with_workspace, int fp8,
+                        int *groups, int *whole_rounds, int *pieces, int *half_tiles);
 
 /* Static, never-NULL description of a status code. */
 const char *xs_attn_strerror(int status);

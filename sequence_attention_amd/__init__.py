@@ -171,15 +171,18 @@ def xs_attn_split_count(B, S, H_local, D) -> int:
     return int(lib().xs_attn_split_count(B, S, H_local, D))
 
 
-def xs_attn_schedule(B, S, H_local, D, with_workspace=True) -> dict:
+def xs_attn_schedule(B, S, H_local, D, with_workspace=True, fp8=False) -> dict:
     """The schedule the library runs for this shape on the current device:
-    {"groups", "whole_rounds", "pieces"} (pieces = most pieces a tile is cut into)."""
+    {"groups", "whole_rounds", "pieces", "half_tiles"} (pieces = most pieces a tile is
+    cut into; half_tiles = 128-row tiles of a second launch, bf16 only)."""
     import ctypes
 
-    g, r, p = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    check(lib().xs_attn_schedule(B, S, H_local, D, int(bool(with_workspace)), ctypes.byref(g),
-                                 ctypes.byref(r), ctypes.byref(p)))
-    return {"groups": g.value, "whole_rounds": r.value, "pieces": p.value}
+    g, r, p, h = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    check(lib().xs_attn_schedule_ex(B, S, H_local, D, int(bool(with_workspace)), int(bool(fp8)),
+                                    ctypes.byref(g), ctypes.byref(r), ctypes.byref(p),
+                                    ctypes.byref(h)))
+    return {"groups": g.value, "whole_rounds": r.value, "pieces": p.value,
+            "half_tiles": h.value}
 
 
 workspace_size = xs_attn_workspace_size

@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
         ip = ctypes.POINTER(ci)
         L.xs_attn_schedule.argtypes = [ci, ci, ci, ci, ci, ip, ip, ip]
         L.xs_attn_schedule.restype = ci
+        L.xs_attn_schedule_ex.argtypes = [ci, ci, ci, ci, ci, ci, ip, ip, ip, ip]
+        L.xs_attn_schedule_ex.restype = ci
         L.xs_attn_split_count.argtypes = [ci, ci, ci, ci]
         L.xs_attn_split_count.restype = ci
         L.xs_attn_strerror.argtypes = [ci]

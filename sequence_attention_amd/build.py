@@ -30,10 +30,21 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  The attention kernel's half-height instantiation (4
+# waves per workgroup) can only hold one wave per SIMD, because its LDS ring
+# already fills the compute unit; given that register budget the compiler
+# would switch every MFMA to the accumulation-register form and copy the
+# scores out for the softmax.  The vector-register form keeps it at the
+# 8-wave kernel's layout (250 VGPRs, no AGPRs, no spills); the 8-wave
+# instantiations compile to the same code either way.
+SOURCE_FLAGS = {"attn_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o",
+           obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -71,7 +82,8 @@ def resource_usage() -> str:
     for src in SOURCES:
         if not src.endswith(".hip"):
             continue
-        cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
+        cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-Rpass-analysis=kernel-resource-usage",
+               "-c", os.path.join(CSRC, src),
                "-o", os.devnull]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:

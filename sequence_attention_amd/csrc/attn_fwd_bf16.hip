@@ -848,15 +848,27 @@ __global__ __launch_bounds__(C::THREADS, kGroupsPerCU) void attn_fwd_bf16_kernel
   }
 }
 
-template <int D>
-static hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
-  using C = Bf16Cfg<D, XS_QT, XS_NW, XS_BN>;
-  static_assert(C::BM == kBlockM, "tile geometry");
+template <class C>
+static hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
   if (a.groups < 1) return hipErrorInvalidValue;
   AttnArgs args = a;
   void* kargs[] = {&args};
   return hipLaunchKernel((const void*)attn_fwd_bf16_kernel<C>, dim3((unsigned)a.groups),
                          dim3(C::THREADS), kargs, 0, stream);
+}
+
+// Full-height tiles (8 waves), or half-height ones (4 waves, one per SIMD)
+// for the tiles left over after the whole rounds of a call without a
+// workspace: those run as twice as many half tiles instead of leaving part of
+// the chip idle for a last, partly filled round.  Half tiles are never cut.
+template <int D>
+static hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
+  using C = Bf16Cfg<D, XS_QT, XS_NW, XS_BN>;
+  using CH = Bf16Cfg<D, XS_QT, XS_NW / 2, XS_BN>;
+  static_assert(C::BM == kBlockM && CH::BM == kHalfM, "tile geometry");
+  if (!a.half) return launch_cfg<C>(a, stream);
+  if (a.ws_o != nullptr || a.units != 0) return hipErrorInvalidValue;
+  return launch_cfg<CH>(a, stream);
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream) {

@@ -809,6 +809,7 @@ static hipError_t launch_d8(const AttnArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream) {
+  if (a.half || a.tile0 != 0) return hipErrorInvalidValue;  // full-height tiles only
   switch (a.D) {
     case 64:
       return a.lse ? launch_d8<64, true>(a, stream) : launch_d8<64, false>(a, stream);

@@ -36,6 +36,13 @@ struct AttnArgs {
   int chunk_rows;
   long long jump_rows;
   float* lse;     // NULL or [B][H][S] fp32 log-sum-exp (natural log)
+  // Tile height of this launch: 0 = kBlockM rows (8 waves), 1 = kBlockM / 2
+  // rows (4 waves, bf16 only, whole tiles only).  Tiles are numbered in the
+  // launch's own height, tile = (b*H + h) * ceil(S / height) + m-tile, and the
+  // launch's schedule starts at tile `tile0` (0 unless an earlier launch of the
+  // same call took the tiles before it).
+  int half;
+  int tile0;
 };
 
 // Tile geometry shared by the bf16 and fp8 kernels and the host-side plan.
@@ -49,6 +56,7 @@ constexpr int kBlockM = XS_BM;         // query rows per workgroup
 constexpr int kBlockN = 64;            // keys per K/V block of the schedule
 constexpr int kUnitKeys = 2 * kBlockN; // keys per schedule unit (a pair of blocks)
 constexpr int kGroupsPerCU = XS_WGPC;  // workgroups resident per compute unit
+constexpr int kHalfM = kBlockM / 2;    // query rows per workgroup of a half-height launch
 
 // The work schedule, shared by the kernels, the merge and the host plan.
 // Tiles are numbered tile = (b*H + h) * mtiles + m-tile.  Workgroup share c

@@ -39,14 +39,14 @@ __device__ __forceinline__ PieceAddr next_piece(ShareWalk& w, const Sched& sch, 
   const int npair = sch.npair, mtiles = (a.S + BM - 1) / BM;
   int tile, p0, p1;
   if (w.round < sch.dp) {
-    tile = w.round * sch.groups + w.chunk;
+    tile = a.tile0 + w.round * sch.groups + w.chunk;
     p0 = 0;
     p1 = npair;
     ++w.round;
     slot = -1;
   } else {
     const int rt = (int)(w.u / npair);
-    tile = sch.dp * sch.groups + rt;
+    tile = a.tile0 + sch.dp * sch.groups + rt;
     p0 = (int)(w.u - (long long)rt * npair);
     const long long left = w.uend - w.u;
     p1 = left < npair - p0 ? p0 + (int)left : npair;

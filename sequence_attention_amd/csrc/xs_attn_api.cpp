@@ -20,7 +20,7 @@ static __device__ __align__(256) uint8_t scratch[XS_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // |scale| * log2(e): the kernels compute p = 2^(s*c - m).  A zero scale is
@@ -52,8 +52,9 @@ int validate(const void* q, const void* k, const void* v, void* out, int B, int 
   if (elems * 2.0 > 9.0e18) return XS_ERR_UNSUPPORTED;
   // K/V rows of one (batch, head) are addressed with 32-bit buffer offsets
   if ((double)S * H * D * (double)in_elem_bytes >= 4294967296.0) return XS_ERR_UNSUPPORTED;
-  // query tiles are counted in 32-bit integers
-  if ((double)B * H * ((S + xs::kBlockM - 1) / xs::kBlockM) > 2147483647.0) return XS_ERR_UNSUPPORTED;
+  // query tiles (and the half-height tiles of a second launch) are counted in
+  // 32-bit integers
+  if ((double)B * H * ((S + xs::kHalfM - 1) / xs::kHalfM) > 2147483647.0) return XS_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return XS_ERR_ALIGN;
   const size_t n = (size_t)B * S * H * D;
   const size_t in_bytes = n * in_elem_bytes, out_bytes = n * 2;
@@ -83,6 +84,8 @@ int validate(const void* q, const void* k, const void* v, void* out, int B, int 
   args->chunk_rows = 0;
   args->jump_rows = 0;
   args->lse = nullptr;
+  args->half = 0;
+  args->tile0 = 0;
   return XS_OK;
 }
 
@@ -127,11 +130,19 @@ int device_cus() {
 // cheapest by a run-time model: rounds of resident workgroups x (units per
 // workgroup + 1.5 units of prologue/epilogue per piece) x time per unit, plus,
 // when tiles are cut, the partials' HBM traffic and the merge launch; cutting
-// must gain 3 % over the best uncut schedule.
+// must gain 3 % over the best uncut schedule.  bf16 calls whose best schedule
+// cuts nothing run the tiles left after the whole rounds (at most half a
+// round of them) as half-height tiles in a second launch, one per slot: a
+// round of twice as many half tiles instead of a last round that leaves half
+// of the chip or more idle.
 struct Plan {
   int groups, npair, dp;
   long long units, tiles;  // units of the remainder tiles
   bool cut;
+  // second launch: half tiles [half0, half0 + halves) (none when halves = 0;
+  // groups = 0 when there are no whole rounds before it)
+  long long half0 = 0;
+  int halves = 0;
 };
 
 // Invariant kept for the kernels and the merge: units == 0 or units >= groups
@@ -171,7 +182,24 @@ double plan_cost(const Plan& p, int slots, int D) {
   return t;
 }
 
-Plan plan_for(int B, int S, int H, int D, bool allow_cut) {
+// The half-tile form of an uncut schedule (halves = 0 when it has none): dp
+// whole rounds of full tiles on every slot, then the remaining tiles as half
+// tiles, when those fit one round.
+Plan with_half_tiles(int B, int S, int H, int npair, int slots) {
+  const long long mt = (S + xs::kBlockM - 1) / xs::kBlockM, mh = (S + xs::kHalfM - 1) / xs::kHalfM;
+  const long long tiles = (long long)B * H * mt;
+  const long long dp = tiles / slots, t0 = dp * slots;
+  Plan p = dp > 0 ? make_plan(slots, npair, t0) : Plan{0, npair, 0, 0, 0, false};
+  if (t0 == tiles) return p;
+  const long long bh0 = t0 / mt;
+  p.half0 = bh0 * mh + 2 * (t0 - bh0 * mt);
+  const long long halves = (long long)B * H * mh - p.half0;
+  if (halves > slots) p.halves = 0;
+  else p.halves = (int)halves;
+  return p;
+}
+
+Plan plan_for(int B, int S, int H, int D, bool allow_cut, bool half_ok = false) {
   const long long tiles = (long long)B * H * ((S + xs::kBlockM - 1) / xs::kBlockM);
   const int nblk = (S + xs::kBlockN - 1) / xs::kBlockN;
   const int npair = (nblk + 1) / 2;
@@ -191,6 +219,10 @@ Plan plan_for(int B, int S, int H, int D, bool allow_cut) {
   consider(slots);  // persistent: one workgroup per slot
   for (int k = 2; k <= 16 && k <= npair; ++k)
     if (tiles * k <= slots) consider(tiles * k);  // k equal pieces per tile, one round
+  if (half_ok && !best.cut && tiles % slots != 0) {
+    const Plan h = with_half_tiles(B, S, H, npair, slots);
+    if (h.halves > 0) return h;
+  }
   return best;
 }
 
@@ -202,9 +234,11 @@ size_t workspace_bytes(const Plan& pl, int D) {
 // Attaches the schedule and, when it cuts tiles, the workspace to validated
 // arguments (inputs of in_elem_bytes per element).  Without a workspace the
 // schedule never cuts.
-int attach_workspace(xs::AttnArgs* a, void* ws, size_t ws_bytes, size_t in_elem_bytes) {
+int attach_workspace(xs::AttnArgs* a, void* ws, size_t ws_bytes, size_t in_elem_bytes,
+                     Plan* plan) {
   if (ws != nullptr && ((uintptr_t)ws & 15u) != 0) return XS_ERR_ALIGN;
-  const Plan pl = plan_for(a->B, a->S, a->H, a->D, ws != nullptr);
+  const Plan pl = plan_for(a->B, a->S, a->H, a->D, ws != nullptr, in_elem_bytes == 2);
+  *plan = pl;
   const size_t need = workspace_bytes(pl, a->D);
   if (need > 0 && ws_bytes < need) return XS_ERR_WORKSPACE;
   if (need > 0) {
@@ -248,9 +282,23 @@ int scratch_address(void** out) {
   return XS_OK;
 }
 
-int launch(const xs::AttnArgs& a, bool fp8, hipStream_t stream) {
-  const hipError_t e = fp8 ? xs::launch_attn_fp8(a, stream) : xs::launch_attn_bf16(a, stream);
-  if (e != hipSuccess) return XS_ERR_LAUNCH;
+int launch(const xs::AttnArgs& a, const Plan& pl, bool fp8, hipStream_t stream) {
+  if (a.groups > 0) {
+    const hipError_t e = fp8 ? xs::launch_attn_fp8(a, stream) : xs::launch_attn_bf16(a, stream);
+    if (e != hipSuccess) return XS_ERR_LAUNCH;
+  }
+  if (pl.halves > 0) {
+    if (fp8) return XS_ERR_LAUNCH;  // the plan gives half tiles to bf16 calls only
+    xs::AttnArgs h = a;
+    h.half = 1;
+    h.tile0 = (int)pl.half0;
+    h.groups = pl.halves;
+    h.dp = 1;
+    h.units = 0;
+    h.ws_o = nullptr;
+    h.ws_ml = nullptr;
+    if (xs::launch_attn_bf16(h, stream) != hipSuccess) return XS_ERR_LAUNCH;
+  }
   if (a.ws_o != nullptr && xs::launch_attn_combine(a, stream) != hipSuccess) return XS_ERR_LAUNCH;
   return XS_OK;
 }
@@ -267,9 +315,10 @@ int xs_attn_fwd_ex(const void* q, const void* k, const void* v, int in_layout, v
   if (rc != XS_OK) return rc;
   rc = apply_layout_and_lse(&a, in_layout, lse, 2);
   if (rc != XS_OK) return rc;
-  rc = attach_workspace(&a, workspace, workspace_bytes, 2);
+  Plan pl;
+  rc = attach_workspace(&a, workspace, workspace_bytes, 2, &pl);
   if (rc != XS_OK) return rc;
-  return launch(a, false, (hipStream_t)stream);
+  return launch(a, pl, false, (hipStream_t)stream);
 }
 
 int xs_attn_fwd_ws(const void* q, const void* k, const void* v, void* out_packed, int B, int S,
@@ -303,9 +352,10 @@ int xs_attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v8, int in_la
   a.neg = qk < 0.0f;
   a.c = scores_factor(qk);
   a.o_scale = v_descale;
-  rc = attach_workspace(&a, workspace, workspace_bytes, 1);
+  Plan pl;
+  rc = attach_workspace(&a, workspace, workspace_bytes, 1, &pl);
   if (rc != XS_OK) return rc;
-  return launch(a, true, (hipStream_t)stream);
+  return launch(a, pl, true, (hipStream_t)stream);
 }
 
 int xs_attn_fwd_fp8_ws(const void* q8, const void* k8, const void* v8, float q_descale,
@@ -336,9 +386,10 @@ int xs_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out_p
     rc = scratch_address(&ws);
     if (rc != XS_OK) return rc;
   }
-  rc = attach_workspace(&a, ws, (size_t)XS_NOALLOC_SCRATCH_BYTES, 2);
+  Plan pl;
+  rc = attach_workspace(&a, ws, (size_t)XS_NOALLOC_SCRATCH_BYTES, 2, &pl);
   if (rc != XS_OK) return rc;
-  return launch(a, false, (hipStream_t)stream);
+  return launch(a, pl, false, (hipStream_t)stream);
 }
 
 size_t xs_attn_workspace_size(int B, int S, int H_local, int D) {
@@ -346,12 +397,13 @@ size_t xs_attn_workspace_size(int B, int S, int H_local, int D) {
   return workspace_bytes(plan_for(B, S, H_local, D, true), D);
 }
 
-int xs_attn_schedule(int B, int S, int H_local, int D, int with_workspace, int* groups,
-                     int* whole_rounds, int* pieces) {
+int xs_attn_schedule_ex(int B, int S, int H_local, int D, int with_workspace, int fp8,
+                        int* groups, int* whole_rounds, int* pieces, int* half_tiles) {
   if (B < 1 || S < 1 || H_local < 1 || (D != 64 && D != 128)) return XS_ERR_SHAPE;
-  const Plan p = plan_for(B, S, H_local, D, with_workspace != 0);
+  const Plan p = plan_for(B, S, H_local, D, with_workspace != 0, fp8 == 0);
   if (groups) *groups = p.groups;
   if (whole_rounds) *whole_rounds = p.dp;
+  if (half_tiles) *half_tiles = p.halves;
   if (pieces) {
     int most = 1;
     if (p.cut) {
@@ -364,6 +416,12 @@ int xs_attn_schedule(int B, int S, int H_local, int D, int with_workspace, int* 
     *pieces = most;
   }
   return XS_OK;
+}
+
+int xs_attn_schedule(int B, int S, int H_local, int D, int with_workspace, int* groups,
+                     int* whole_rounds, int* pieces) {
+  return xs_attn_schedule_ex(B, S, H_local, D, with_workspace, 0, groups, whole_rounds, pieces,
+                             nullptr);
 }
 
 int xs_attn_split_count(int B, int S, int H_local, int D) {

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == {"xs_attn_fwd", "xs_attn_fwd_fp8", "xs_attn_fwd_ws", "xs_attn_fwd_fp8_ws",
                           "xs_attn_fwd_ex", "xs_attn_fwd_fp8_ex", "xs_attn_workspace_size",
                           "xs_attn_split_count", "xs_attn_strerror", "xs_attn_version",
-                          "xs_attn_fwd_noalloc", "xs_attn_schedule", "xs_burst_gap",
+                          "xs_attn_fwd_noalloc", "xs_attn_schedule", "xs_attn_schedule_ex", "xs_burst_gap",
                           "xs_burst_gap_tiles", "xs_mfma_ceiling", "xs_clock_sample"}
     L = _lib.lib()
     for n in names:
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert xs.xs_attn_version() == 10400
+    assert xs.xs_attn_version() == 10500
     for code in (XS_OK, XS_ERR_NULL, XS_ERR_SHAPE, XS_ERR_UNSUPPORTED, XS_ERR_ALIGN, XS_ERR_LAUNCH,
                  XS_ERR_OVERLAP, XS_ERR_WORKSPACE, XS_ERR_SCRATCH, 12345):
         s = xs.xs_attn_strerror(code)
@@ -301,6 +301,37 @@ def test_schedule_query_is_consistent_with_split_count():
         s = xs.xs_attn_schedule(*shape)
         assert s["pieces"] == xs.split_count(*shape)
         assert xs.xs_attn_schedule(*shape, with_workspace=False)["pieces"] == 1
-        assert s["groups"] >= 1 and s["whole_rounds"] >= 0
+        assert s["groups"] >= 1 or s["half_tiles"] >= 1
+        assert s["whole_rounds"] >= 0
     with pytest.raises(xs.XsAttnError):
         xs.xs_attn_schedule(1, 64, 1, 96)
+
+
+def test_half_tiles_fill_the_last_round():
+    # without a device the plan assumes 256 compute units
+    tiles = lambda B, S, H: B * H * -(-S // 256)
+    # video share without a workspace: 640 tiles = 2 whole rounds + 128 tiles,
+    # which run as 256 half tiles; with a workspace they are cut by keys instead
+    s = xs.xs_attn_schedule(1, 32768, 5, 128, with_workspace=False)
+    assert (s["groups"], s["whole_rounds"], s["pieces"], s["half_tiles"]) == (256, 2, 1, 256)
+    s = xs.xs_attn_schedule(1, 32768, 5, 128, with_workspace=True)
+    assert (s["groups"], s["whole_rounds"], s["pieces"], s["half_tiles"]) == (256, 2, 2, 0)
+    # fp8 calls never run half tiles: the uncut plan keeps a partial last round
+    s = xs.xs_attn_schedule(1, 32768, 5, 128, with_workspace=False, fp8=True)
+    assert s["half_tiles"] == 0 and s["pieces"] == 1
+    assert s["groups"] * max(s["whole_rounds"], 1) >= tiles(1, 32768, 5)
+    # image share without a workspace: 54 tiles, no whole round, 108 half tiles
+    s = xs.xs_attn_schedule(1, 4608, 3, 128, with_workspace=False)
+    assert (s["groups"], s["whole_rounds"], s["half_tiles"]) == (0, 0, 108)
+    # a head whose last tile holds at most 128 rows has one half tile fewer:
+    # S = 7000 -> 28 tiles, 55 half tiles per head; 280 tiles = 1 round + 24
+    # tiles, the first of them tile 4 of head 9 (of 10)
+    s = xs.xs_attn_schedule(2, 7000, 5, 128, with_workspace=False)
+    assert (s["groups"], s["whole_rounds"], s["half_tiles"]) == (256, 1, 55 - 8)
+    # long share: 6 exact rounds, nothing left over
+    s = xs.xs_attn_schedule(1, 131072, 3, 128, with_workspace=False)
+    assert (s["groups"], s["whole_rounds"], s["half_tiles"]) == (256, 6, 0)
+    # more than half a round left over: twice as many half tiles would not fit
+    # one round, so the plan keeps full tiles (200 tiles, one round)
+    s = xs.xs_attn_schedule(1, 200 * 256, 1, 128, with_workspace=False)
+    assert s["half_tiles"] == 0 and s["groups"] == 200

@@ -4,8 +4,9 @@
 * video and fp8 shares: every element of out_packed, both through the product
   path (the split schedule with a caller workspace, what the benchmark times)
   and through xs_attn_fwd / xs_attn_fwd_fp8 themselves (no workspace: the uncut
-  persistent schedule), each output prefilled with NaN so an unwritten element
-  cannot pass;
+  schedule; for bf16 video two rounds of whole tiles, then the remaining 128
+  tiles as 256 half-height tiles), each output prefilled with NaN so an
+  unwritten element cannot pass;
 * long share: NaN prefill, every element finite, and three rows of every
   256-row query tile (its first, its last and one drawn at random) against the
   oracle -- every tile of the schedule is checked, not only a sample of rows;
@@ -13,7 +14,8 @@
   cuts the remainder tiles between workgroups (the path of the three large
   shares), on every element;
 * xs_attn_fwd and xs_attn_fwd_fp8 called by name through ctypes on the image
-  share, where the default plan would cut tiles, on every element.
+  share, where the default plan would cut tiles, on every element (bf16: all
+  of it in half-height tiles).
 
 Bar: max-abs 1e-2 (bf16 inputs) / 5e-2 (fp8) and relative L2 1e-2 / 8e-2 on every
 compared element, the stated tolerance on the workloads' own inputs.
