@@ -581,7 +581,7 @@ def main():
     # start on a GPU whose clock has already settled (about 0.6 % on a run with 5
     # warm-up steps); its own result is compared with the product path's below.
     out_ns = torch.empty_like(out)
-    sched_ns = xs.xs_attn_schedule(w.B, w.S, w.H, w.D, with_workspace=False)
+    sched_ns = xs.xs_attn_schedule(w.B, w.S, w.H, w.D, with_workspace=False, fp8=w.dtype == "fp8")
 
     def step_ns():
         if w.dtype == "fp8":
@@ -715,7 +715,8 @@ def main():
                    "causal": False,
                    "entry": ("xs_attn_fwd_fp8_ex" if w.dtype == "fp8" else "xs_attn_fwd_ex")
                             + (" with a caller workspace" if ws_bytes else " (no workspace)"),
-                   "schedule": xs.xs_attn_schedule(w.B, w.S, w.H, w.D, with_workspace=True),
+                   "schedule": xs.xs_attn_schedule(w.B, w.S, w.H, w.D, with_workspace=True,
+                                                   fp8=w.dtype == "fp8"),
                    "key_splits": nsplit, "workspace_bytes": ws_bytes,
                    "caches": "evicted before every call (--cold)" if args.cold else "warm",
                    "launch": "hip graph replay" if args.graph else "direct",
