@@ -140,6 +140,11 @@ int xs_attn_fwd_noalloc(const void *q, const void *k, const void *v, void *out_p
                                (T = S/P) of every batch -- the layout the Ulysses
                                pre-attention All-to-All delivers, the same chunk layout as
                                out_packed.  Byte-identical to BSHD when B = 1 or P = 1. */
+/* Flag OR-ed into in_layout: run the whole call in one attention launch, as a call
+ * whose out_packed lies behind a link does (no half-height tiles in a second launch,
+ * xs_attn_schedule_ex); the rows are the same bit for bit.  For comparing an output
+ * in device memory with one behind a link under the same schedule. */
+#define XS_ONE_LAUNCH 0x100
 
 /* The split-key entry points with two additions (both optional):
  *   in_layout  XS_LAYOUT_BSHD or XS_LAYOUT_CHUNKED: q, k, v may be consumed directly
@@ -202,7 +207,12 @@ int xs_attn_schedule(int B, int S, int H_local, int D, int with_workspace, int *
  *                 half a round of tiles after the whole rounds: those tiles
  *                 run as 128-row half tiles (4 wavefronts) in a second launch,
  *                 one workgroup each, so that the last round fills the chip
- *                 (0 = none; always 0 for fp8).
+ *                 (0 = none; always 0 for fp8).  Only when out_packed is
+ *                 device memory of the current device: behind a link (host or
+ *                 peer memory) the first launch would have to drain its whole
+ *                 last round before the second starts, so such calls keep a
+ *                 last round of full tiles in the same launch (the schedule
+ *                 with half_tiles = 0 and groups covering every tile).
  * Any output pointer may be NULL.  Returns XS_OK or XS_ERR_SHAPE (sizes < 1, D
  * not 64 or 128).  No launch. */
 int xs_attn_schedule_ex(int B, int S, int H_local, int D, int with_workspace, int fp8,

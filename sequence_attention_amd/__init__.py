@@ -35,9 +35,10 @@ __all__ = ["fwd", "fwd_fp8", "unpack", "chunk", "workspace_size", "split_count",
            "xs_attn_fwd_fp8_ex", "xs_attn_workspace_size", "xs_attn_split_count",
            "xs_attn_schedule", "xs_attn_fwd_noalloc",
            "xs_attn_strerror", "xs_attn_version", "XsAttnError", "default_scale",
-           "LAYOUT_BSHD", "LAYOUT_CHUNKED"]
+           "LAYOUT_BSHD", "LAYOUT_CHUNKED", "ONE_LAUNCH"]
 
 LAYOUT_BSHD, LAYOUT_CHUNKED = 0, 1  # include/xs_attn.h XS_LAYOUT_*
+ONE_LAUNCH = 0x100  # include/xs_attn.h XS_ONE_LAUNCH, OR-ed into the layout code
 
 
 def default_scale(D: int) -> float:

@@ -500,7 +500,7 @@ def attention_overhead(w, inp, p: Params, torch_device, reps: int = 21, p_tiles:
     """The attention call with out_packed in fine-grained host memory (the
     stand-in remote link) against out_packed in HBM, for a workload `w` (sizes
     B, S, H, D, P, name) with inputs `inp` (q, k, v, scale on the CPU), with the
-    uncut schedule (no workspace).  Every tile owner's O
+    uncut schedule in one launch (no workspace, XS_ONE_LAUNCH).  Every tile owner's O
     tile (256 rows x D bf16) is one producer's burst; a round of resident
     workgroups is K = min(tiles, CUs) producers issuing V = K tile bytes, and the
     next round's key loop is their gap.  The model predicts the extra time as
@@ -518,9 +518,11 @@ def attention_overhead(w, inp, p: Params, torch_device, reps: int = 21, p_tiles:
     host = HostBuffer(nbytes)
     stream = torch.cuda.current_stream(torch_device)
 
+    # both outputs under the same schedule: an output behind a link never takes the
+    # second, half-tile launch, so the device-memory run is held to one launch too
     def call(ptr):
-        rc = xs.xs_attn_fwd_ex(q, k, v, 0, ptr, None, w.B, w.S, w.H, w.D, w.P, inp["scale"], None, 0,
-                               stream.cuda_stream)
+        rc = xs.xs_attn_fwd_ex(q, k, v, xs.LAYOUT_BSHD | xs.ONE_LAUNCH, ptr, None, w.B, w.S, w.H,
+                               w.D, w.P, inp["scale"], None, 0, stream.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"xs_attn_fwd_ex failed with {rc}")
 

@@ -199,6 +199,21 @@ Plan with_half_tiles(int B, int S, int H, int npair, int slots) {
   return p;
 }
 
+// True when `p` is device memory of the current device.  A kernel completes
+// only when its stores are visible where they went, so with out_packed behind
+// a link (host memory, a peer GPU) a second launch would first wait for the
+// whole last round of the first to drain instead of overlapping that drain with
+// the next tiles' computation; half tiles are used only for local outputs.
+bool local_device_memory(const void* p) {
+  int dev = -1;
+  hipPointerAttribute_t at;
+  if (hipGetDevice(&dev) != hipSuccess || hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // an unknown pointer leaves no error behind
+    return false;
+  }
+  return at.type == hipMemoryTypeDevice && at.device == dev;
+}
+
 Plan plan_for(int B, int S, int H, int D, bool allow_cut, bool half_ok = false) {
   const long long tiles = (long long)B * H * ((S + xs::kBlockM - 1) / xs::kBlockM);
   const int nblk = (S + xs::kBlockN - 1) / xs::kBlockN;
@@ -235,9 +250,11 @@ size_t workspace_bytes(const Plan& pl, int D) {
 // arguments (inputs of in_elem_bytes per element).  Without a workspace the
 // schedule never cuts.
 int attach_workspace(xs::AttnArgs* a, void* ws, size_t ws_bytes, size_t in_elem_bytes,
-                     Plan* plan) {
+                     Plan* plan, bool one_launch = false) {
   if (ws != nullptr && ((uintptr_t)ws & 15u) != 0) return XS_ERR_ALIGN;
-  const Plan pl = plan_for(a->B, a->S, a->H, a->D, ws != nullptr, in_elem_bytes == 2);
+  Plan pl = plan_for(a->B, a->S, a->H, a->D, ws != nullptr, in_elem_bytes == 2 && !one_launch);
+  if (pl.halves > 0 && !local_device_memory(a->out))
+    pl = plan_for(a->B, a->S, a->H, a->D, ws != nullptr, false);
   *plan = pl;
   const size_t need = workspace_bytes(pl, a->D);
   if (need > 0 && ws_bytes < need) return XS_ERR_WORKSPACE;
@@ -313,10 +330,11 @@ int xs_attn_fwd_ex(const void* q, const void* k, const void* v, int in_layout, v
   xs::AttnArgs a;
   int rc = validate(q, k, v, out_packed, B, S, H_local, D, P, scale, 2, &a);
   if (rc != XS_OK) return rc;
-  rc = apply_layout_and_lse(&a, in_layout, lse, 2);
+  const bool one_launch = (in_layout & XS_ONE_LAUNCH) != 0;
+  rc = apply_layout_and_lse(&a, in_layout & ~XS_ONE_LAUNCH, lse, 2);
   if (rc != XS_OK) return rc;
   Plan pl;
-  rc = attach_workspace(&a, workspace, workspace_bytes, 2, &pl);
+  rc = attach_workspace(&a, workspace, workspace_bytes, 2, &pl, one_launch);
   if (rc != XS_OK) return rc;
   return launch(a, pl, false, (hipStream_t)stream);
 }
@@ -341,7 +359,7 @@ int xs_attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v8, int in_la
   xs::AttnArgs a;
   int rc = validate(q8, k8, v8, out_packed, B, S, H_local, D, P, scale, 1, &a);
   if (rc != XS_OK) return rc;
-  rc = apply_layout_and_lse(&a, in_layout, lse, 1);
+  rc = apply_layout_and_lse(&a, in_layout & ~XS_ONE_LAUNCH, lse, 1);  // fp8: always one launch
   if (rc != XS_OK) return rc;
   if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale))
     return XS_ERR_UNSUPPORTED;

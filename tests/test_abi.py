@@ -190,8 +190,22 @@ def _fwd8_ex(**kw):
 
 @pytest.mark.parametrize("call", [_fwd_ex, _fwd8_ex])
 def test_ex_rejects_unknown_layouts(call):
-    for layout in (-1, 2, 7):
+    for layout in (-1, 2, 7, 0x102, 0x200, 0x300):
         assert call(layout=layout) == XS_ERR_UNSUPPORTED
+
+
+def test_one_launch_flag_is_accepted_with_either_layout():
+    # the flag is stripped before the layout is checked: a call that then fails on
+    # its misaligned workspace (checked after the layout) reports XS_ERR_ALIGN
+    need = xs.workspace_size(1, 4608, 3, 128)
+    W = 0x50000000 + 8
+    for layout in (0, 1, xs.ONE_LAUNCH, xs.ONE_LAUNCH | xs.LAYOUT_CHUNKED):
+        assert xs.xs_attn_fwd_ex(Q, K, V, layout, O, None, 1, 4608, 3, 128, 8, 0.125, W, need,
+                                 None) == XS_ERR_ALIGN, layout
+        assert xs.xs_attn_fwd_fp8_ex(Q, K, V, layout, 0.01, 0.01, 0.01, O, None, 1, 4608, 3, 128,
+                                     8, 0.125, W, need, None) == XS_ERR_ALIGN, layout
+    assert xs.xs_attn_fwd_ex(Q, K, V, 0x200, O, None, 1, 4608, 3, 128, 8, 0.125, W, need,
+                             None) == XS_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("call", [_fwd_ex, _fwd8_ex])

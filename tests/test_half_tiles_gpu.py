@@ -12,7 +12,10 @@ launch, one workgroup each.
 * the 4-wave and the 8-wave kernel give bit-identical rows: each row's
   arithmetic (its key order, its fast pass and lazy rescale) does not depend on
   how many waves share the tile, so the same heads computed in whole tiles
-  (a shape of exactly one round) and in half tiles must agree bit for bit.
+  (a shape of exactly one round) and in half tiles must agree bit for bit;
+* out_packed in host memory (behind a link) keeps the single-launch schedule of
+  full tiles and gives the same bytes, as does that schedule asked for with
+  XS_ONE_LAUNCH.
 
 Bar: max-abs 1e-2 and relative L2 1e-2 (bf16) on every element; the LSE within
 the 5e-3 bar derived for the log-sum-exp output.
@@ -124,3 +127,40 @@ def test_half_and_whole_tiles_bit_identical(gpu, S, D):
     assert torch.isfinite(b.float()).all()
     assert torch.equal(a.contiguous().view(torch.int16), b.contiguous().view(torch.int16))
     assert torch.equal(lse_full[:, :H_few], lse_few)
+
+
+def test_output_behind_a_link_keeps_full_tiles(gpu):
+    # out_packed in fine-grained host memory (the stand-in for a remote
+    # destination): the call keeps the single-launch schedule of full tiles,
+    # whose rows are bit-identical to the half-tile schedule's in device memory
+    from sequence_attention_amd.burst_gap import HostBuffer
+
+    w = workloads.WORKLOADS["image"].with_(index=8500)
+    s = xs.xs_attn_schedule(w.B, w.S, w.H, w.D, with_workspace=False)
+    _say(f"host-memory output, image share, device-output schedule {s}")
+    assert s["half_tiles"] > 0
+    inp = workloads.make_inputs(w)
+    q, k, v = (inp[n].to(gpu) for n in "qkv")
+    out = torch.full((w.P, w.B, w.S // w.P, w.H, w.D), float("nan"), dtype=torch.bfloat16,
+                     device=gpu)
+    stream = torch.cuda.current_stream(gpu).cuda_stream
+    host = HostBuffer(out.numel() * 2)
+    try:
+        host.view(np.uint8)[:] = 0xFF  # NaN in bf16: an unwritten row cannot pass
+        for ptr in (out.data_ptr(), host.ptr):
+            rc = xs.xs_attn_fwd(q, k, v, ptr, w.B, w.S, w.H, w.D, w.P, inp["scale"], stream)
+            assert rc == 0, xs.xs_attn_strerror(rc)
+        torch.cuda.synchronize()
+        got = host.view(np.uint16).copy()
+    finally:
+        host.free()
+    assert np.array_equal(got, out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1))
+    # the same one-launch schedule asked for explicitly, output in device memory
+    one = torch.full_like(out, float("nan"))
+    rc = xs.xs_attn_fwd_ex(q, k, v, xs.LAYOUT_BSHD | xs.ONE_LAUNCH, one, None, w.B, w.S, w.H, w.D,
+                           w.P, inp["scale"], None, 0, stream)
+    assert rc == 0, xs.xs_attn_strerror(rc)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), out.view(torch.int16))
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], w.P, inp["scale"])
+    _gate(_f64(out), ref, "device-memory output (half tiles)")
