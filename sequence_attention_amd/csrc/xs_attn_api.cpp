@@ -206,9 +206,13 @@ Plan with_half_tiles(int B, int S, int H, int npair, int slots) {
 // the next tiles' computation; half tiles are used only for local outputs.
 bool local_device_memory(const void* p) {
   int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const hipError_t before = hipPeekAtLastError();
   hipPointerAttribute_t at;
-  if (hipGetDevice(&dev) != hipSuccess || hipPointerGetAttributes(&at, p) != hipSuccess) {
-    (void)hipGetLastError();  // an unknown pointer leaves no error behind
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    // a pointer the runtime does not know: take the one-launch schedule and
+    // leave no error of this query behind (an earlier one stays reported)
+    if (before == hipSuccess) (void)hipGetLastError();
     return false;
   }
   return at.type == hipMemoryTypeDevice && at.device == dev;
