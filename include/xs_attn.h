@@ -187,7 +187,7 @@ size_t xs_attn_workspace_size(int B, int S, int H_local, int D);
  * on the current device (1 = no tile is cut); 0 for invalid sizes. */
 int xs_attn_split_count(int B, int S, int H_local, int D);
 
-/* The schedule the library runs for a bf16 call of this shape on the current
+/* The schedule the library runs for a call of this shape on the current
  * device, with (with_workspace != 0) or without a workspace:
  * xs_attn_schedule_ex(B, S, H_local, D, with_workspace, 0, groups, whole_rounds,
  * pieces, NULL). */
@@ -195,19 +195,19 @@ int xs_attn_schedule(int B, int S, int H_local, int D, int with_workspace, int *
                      int *whole_rounds, int *pieces);
 
 /* The schedule the library runs for this shape on the current device, for a
- * bf16 (fp8 = 0) or fp8 (fp8 != 0) call with (with_workspace != 0) or without a
- * workspace.  Work is split into query tiles of 256 rows (8 wavefronts of 32
+ * bf16 (fp8 = 0) or fp8 (fp8 != 0) call -- the two are scheduled alike -- with
+ * (with_workspace != 0) or without a workspace.  Work is split into query tiles of 256 rows (8 wavefronts of 32
  * rows each) and, inside a tile, pairs of 64-key blocks:
  *   groups        workgroups of the first launch (0 when it has none);
  *   whole_rounds  rounds of whole tiles each of them takes first;
  *   pieces        the most pieces any remaining tile is cut into by their
  *                 shares of its key blocks (1 = none is cut; cut tiles are
  *                 merged by a second kernel);
- *   half_tiles    bf16 calls whose schedule cuts no tile and leaves at most
- *                 half a round of tiles after the whole rounds: those tiles
- *                 run as 128-row half tiles (4 wavefronts) in a second launch,
- *                 one workgroup each, so that the last round fills the chip
- *                 (0 = none; always 0 for fp8).  Only when out_packed is
+ *   half_tiles    calls whose schedule cuts no tile and leaves at most half
+ *                 a round of tiles after the whole rounds: those tiles run as
+ *                 128-row half tiles (4 wavefronts) in a second launch, one
+ *                 workgroup each, so that the last round fills the chip
+ *                 (0 = none).  Only when out_packed is
  *                 device memory of the current device: behind a link (host or
  *                 peer memory) the first launch would have to drain its whole
  *                 last round before the second starts, so such calls keep a

@@ -30,14 +30,15 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags.  The attention kernel's half-height instantiation (4
-# waves per workgroup) can only hold one wave per SIMD, because its LDS ring
-# already fills the compute unit; given that register budget the compiler
-# would switch every MFMA to the accumulation-register form and copy the
-# scores out for the softmax.  The vector-register form keeps it at the
-# 8-wave kernel's layout (250 VGPRs, no AGPRs, no spills); the 8-wave
-# instantiations compile to the same code either way.
-SOURCE_FLAGS = {"attn_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.  The attention kernels' half-height instantiations
+# (4 waves per workgroup) can hold only one wave per SIMD at D = 128, because
+# the LDS ring already fills the compute unit; given that register budget the
+# compiler would switch every MFMA to the accumulation-register form and copy
+# the scores out for the softmax.  The vector-register form keeps them at the
+# 8-wave kernels' layout (no AGPRs, no spills); the 8-wave instantiations
+# compile to the same code either way.
+SOURCE_FLAGS = {"attn_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "attn_fwd_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

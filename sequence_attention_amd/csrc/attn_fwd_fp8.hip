@@ -38,11 +38,11 @@
 
 namespace xs {
 
-template <int D_, bool LSE_>
+template <int D_, bool LSE_, int NW_ = 8>
 struct Fp8Cfg {
   static constexpr int D = D_;
   static constexpr bool LSE = LSE_;       // also keep fp32 row sums for the log-sum-exp output
-  static constexpr int NW = 8;            // waves per workgroup, 32 query rows each
+  static constexpr int NW = NW_;          // waves per workgroup, 32 query rows each
   static constexpr int BN = 64;           // keys per K/V block
   static constexpr int QW = 32;
   static constexpr int BM = QW * NW;
@@ -64,7 +64,10 @@ struct Fp8Cfg {
   // is code 126 (448), one below the NaN code.
   static constexpr float SHIFT = 4.75f;
   static constexpr float CODE_BIAS = 8.0f * (SHIFT + 7.0f);
-  static_assert(LOADS <= NW, "one direct load per wave at most");
+  // 1 KiB direct loads per wave and tile: one (the first LOADS waves), or
+  // LOADS / NW when there are fewer waves than loads
+  static constexpr int LPW = LOADS > NW ? LOADS / NW : 1;
+  static_assert(LOADS <= NW || LOADS % NW == 0, "tile loads must split evenly over waves");
   static_assert(NT == 2, "the P^T operand layout assumes 64-key blocks");
 };
 
@@ -83,11 +86,19 @@ __device__ __forceinline__ int vswz(int R) { return 2 * ((R / C::RPB) & (C::CH /
 template <class C>
 __device__ __forceinline__ void load_tile8(const uint8_t* head_base, uint32_t row_stride, int kv0,
                                            size_t extra, int S, const uint8_t XS_LDS* dst,
-                                           uint32_t voff, int wave) {
-  if (wave < C::LOADS) {
+                                           const uint32_t (&voff)[C::LPW], int wave) {
+  if constexpr (C::LPW == 1) {
+    if (wave < C::LOADS) {
+      const u32x4 rsrc = make_rsrc(head_base + (size_t)kv0 * row_stride + extra,
+                                   (uint32_t)(S - kv0 - 1) * row_stride + (uint32_t)C::ROWB);
+      load_lds_b128(rsrc, voff[0], lds_addr(dst) + (uint32_t)wave * 1024u);
+    }
+  } else {
     const u32x4 rsrc = make_rsrc(head_base + (size_t)kv0 * row_stride + extra,
                                  (uint32_t)(S - kv0 - 1) * row_stride + (uint32_t)C::ROWB);
-    load_lds_b128(rsrc, voff, lds_addr(dst) + (uint32_t)wave * 1024u);
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i)
+      load_lds_b128(rsrc, voff[i], lds_addr(dst) + (uint32_t)(wave * C::LPW + i) * 1024u);
   }
 }
 
@@ -550,8 +561,10 @@ __device__ __forceinline__ void pv_only8(Fp8State<C>& st, const uint8_t XS_LDS* 
 template <class C>
 __device__ __forceinline__ PieceAddr begin_piece8(ShareWalk& walk, const Sched& sch,
                                                   const AttnArgs& a, int nblk, uint32_t row_stride,
-                                                  uint8_t XS_LDS* lds, uint32_t koff,
-                                                  uint32_t voff, int wave, int& slot) {
+                                                  uint8_t XS_LDS* lds,
+                                                  const uint32_t (&koff)[C::LPW],
+                                                  const uint32_t (&voff)[C::LPW], int wave,
+                                                  int& slot) {
   PieceAddr pa = next_piece<C::BM, C::ROWB, C::BN>(walk, sch, a, nblk, row_stride, slot);
   const uint8_t* kbase = (const uint8_t*)a.k + pa.head_off;
   const uint8_t* vbase = (const uint8_t*)a.v + pa.head_off;
@@ -602,13 +615,21 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const uint32_t row_stride = (uint32_t)H * C::ROWB;
-  // this lane's 16-byte chunk of the wave's 1 KiB direct load, for K and V
-  uint32_t koff, voff;
-  {
+  // this lane's 16-byte chunk of each of the wave's 1 KiB direct loads, for K and V
+  uint32_t koff[C::LPW], voff[C::LPW];
+  if constexpr (C::LPW == 1) {
     const int pos = wave * 64 + lane;
     const int R = pos / C::CH, cp = pos % C::CH;
-    koff = (uint32_t)R * row_stride + (uint32_t)((cp ^ kswz<C>(R)) * 16);
-    voff = (uint32_t)vrow_key(R) * row_stride + (uint32_t)((cp ^ vswz<C>(R)) * 16);
+    koff[0] = (uint32_t)R * row_stride + (uint32_t)((cp ^ kswz<C>(R)) * 16);
+    voff[0] = (uint32_t)vrow_key(R) * row_stride + (uint32_t)((cp ^ vswz<C>(R)) * 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      const int pos = (wave * C::LPW + i) * 64 + lane;
+      const int R = pos / C::CH, cp = pos % C::CH;
+      koff[i] = (uint32_t)R * row_stride + (uint32_t)((cp ^ kswz<C>(R)) * 16);
+      voff[i] = (uint32_t)vrow_key(R) * row_stride + (uint32_t)((cp ^ vswz<C>(R)) * 16);
+    }
   }
   const int nblk = (S + BN - 1) / BN;
   const int nfull = S / BN;
@@ -797,10 +818,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void attn_fwd_fp8_kernel(AttnArgs a)
   }
 }
 
-template <int D, bool LSE>
-static hipError_t launch_d8(const AttnArgs& a, hipStream_t stream) {
-  using C = Fp8Cfg<D, LSE>;
-  static_assert(C::BM == kBlockM && C::BN == kBlockN, "tile geometry");
+template <class C>
+static hipError_t launch_cfg8(const AttnArgs& a, hipStream_t stream) {
   if (a.groups < 1) return hipErrorInvalidValue;
   AttnArgs args = a;
   void* kargs[] = {&args};
@@ -808,8 +827,20 @@ static hipError_t launch_d8(const AttnArgs& a, hipStream_t stream) {
                          dim3(C::THREADS), kargs, 0, stream);
 }
 
+// Full-height tiles (8 waves), or half-height ones (4 waves) for the tiles a
+// call without cut tiles leaves after its whole rounds; half tiles are never cut.
+template <int D, bool LSE>
+static hipError_t launch_d8(const AttnArgs& a, hipStream_t stream) {
+  using C = Fp8Cfg<D, LSE>;
+  using CH = Fp8Cfg<D, LSE, 4>;
+  static_assert(C::BM == kBlockM && C::BN == kBlockN, "tile geometry");
+  static_assert(CH::BM == kHalfM && CH::BN == kBlockN, "tile geometry");
+  if (!a.half) return launch_cfg8<C>(a, stream);
+  if (a.ws_o != nullptr || a.units != 0) return hipErrorInvalidValue;
+  return launch_cfg8<CH>(a, stream);
+}
+
 hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream) {
-  if (a.half || a.tile0 != 0) return hipErrorInvalidValue;  // full-height tiles only
   switch (a.D) {
     case 64:
       return a.lse ? launch_d8<64, true>(a, stream) : launch_d8<64, false>(a, stream);

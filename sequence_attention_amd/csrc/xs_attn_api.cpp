@@ -130,11 +130,11 @@ int device_cus() {
 // cheapest by a run-time model: rounds of resident workgroups x (units per
 // workgroup + 1.5 units of prologue/epilogue per piece) x time per unit, plus,
 // when tiles are cut, the partials' HBM traffic and the merge launch; cutting
-// must gain 3 % over the best uncut schedule.  bf16 calls whose best schedule
-// cuts nothing run the tiles left after the whole rounds (at most half a
-// round of them) as half-height tiles in a second launch, one per slot: a
-// round of twice as many half tiles instead of a last round that leaves half
-// of the chip or more idle.
+// must gain 3 % over the best uncut schedule.  Calls whose best schedule cuts
+// nothing run the tiles left after the whole rounds (at most half a round of
+// them) as half-height tiles in a second launch, one per slot: a round of
+// twice as many half tiles instead of a last round that leaves half of the
+// chip or more idle.
 struct Plan {
   int groups, npair, dp;
   long long units, tiles;  // units of the remainder tiles
@@ -256,7 +256,7 @@ size_t workspace_bytes(const Plan& pl, int D) {
 int attach_workspace(xs::AttnArgs* a, void* ws, size_t ws_bytes, size_t in_elem_bytes,
                      Plan* plan, bool one_launch = false) {
   if (ws != nullptr && ((uintptr_t)ws & 15u) != 0) return XS_ERR_ALIGN;
-  Plan pl = plan_for(a->B, a->S, a->H, a->D, ws != nullptr, in_elem_bytes == 2 && !one_launch);
+  Plan pl = plan_for(a->B, a->S, a->H, a->D, ws != nullptr, !one_launch);
   if (pl.halves > 0 && !local_device_memory(a->out))
     pl = plan_for(a->B, a->S, a->H, a->D, ws != nullptr, false);
   *plan = pl;
@@ -309,7 +309,6 @@ int launch(const xs::AttnArgs& a, const Plan& pl, bool fp8, hipStream_t stream) 
     if (e != hipSuccess) return XS_ERR_LAUNCH;
   }
   if (pl.halves > 0) {
-    if (fp8) return XS_ERR_LAUNCH;  // the plan gives half tiles to bf16 calls only
     xs::AttnArgs h = a;
     h.half = 1;
     h.tile0 = (int)pl.half0;
@@ -318,7 +317,8 @@ int launch(const xs::AttnArgs& a, const Plan& pl, bool fp8, hipStream_t stream) 
     h.units = 0;
     h.ws_o = nullptr;
     h.ws_ml = nullptr;
-    if (xs::launch_attn_bf16(h, stream) != hipSuccess) return XS_ERR_LAUNCH;
+    const hipError_t e = fp8 ? xs::launch_attn_fp8(h, stream) : xs::launch_attn_bf16(h, stream);
+    if (e != hipSuccess) return XS_ERR_LAUNCH;
   }
   if (a.ws_o != nullptr && xs::launch_attn_combine(a, stream) != hipSuccess) return XS_ERR_LAUNCH;
   return XS_OK;
@@ -363,7 +363,8 @@ int xs_attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v8, int in_la
   xs::AttnArgs a;
   int rc = validate(q8, k8, v8, out_packed, B, S, H_local, D, P, scale, 1, &a);
   if (rc != XS_OK) return rc;
-  rc = apply_layout_and_lse(&a, in_layout & ~XS_ONE_LAUNCH, lse, 1);  // fp8: always one launch
+  const bool one_launch = (in_layout & XS_ONE_LAUNCH) != 0;
+  rc = apply_layout_and_lse(&a, in_layout & ~XS_ONE_LAUNCH, lse, 1);
   if (rc != XS_OK) return rc;
   if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale))
     return XS_ERR_UNSUPPORTED;
@@ -375,7 +376,7 @@ int xs_attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v8, int in_la
   a.c = scores_factor(qk);
   a.o_scale = v_descale;
   Plan pl;
-  rc = attach_workspace(&a, workspace, workspace_bytes, 1, &pl);
+  rc = attach_workspace(&a, workspace, workspace_bytes, 1, &pl, one_launch);
   if (rc != XS_OK) return rc;
   return launch(a, pl, true, (hipStream_t)stream);
 }
@@ -422,7 +423,8 @@ size_t xs_attn_workspace_size(int B, int S, int H_local, int D) {
 int xs_attn_schedule_ex(int B, int S, int H_local, int D, int with_workspace, int fp8,
                         int* groups, int* whole_rounds, int* pieces, int* half_tiles) {
   if (B < 1 || S < 1 || H_local < 1 || (D != 64 && D != 128)) return XS_ERR_SHAPE;
-  const Plan p = plan_for(B, S, H_local, D, with_workspace != 0, fp8 == 0);
+  (void)fp8;  // bf16 and fp8 calls run the same schedule
+  const Plan p = plan_for(B, S, H_local, D, with_workspace != 0, true);
   if (groups) *groups = p.groups;
   if (whole_rounds) *whole_rounds = p.dp;
   if (half_tiles) *half_tiles = p.halves;

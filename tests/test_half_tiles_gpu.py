@@ -1,7 +1,7 @@
-"""GPU parity of the half-height tiles: a bf16 call whose schedule cuts no tile
-runs the tiles left after its whole rounds (at most half a round of them) as
-128-row tiles of the same kernel with 4 wavefronts instead of 8, in a second
-launch, one workgroup each.
+"""GPU parity of the half-height tiles: a call whose schedule cuts no tile runs
+the tiles left after its whole rounds (at most half a round of them) as 128-row
+tiles of the same kernel with 4 wavefronts instead of 8, in a second launch,
+one workgroup each (bf16 and fp8).
 
 * shapes whose last round runs as half tiles, on every element of out_packed
   against the fp64 oracle (NaN-prefilled, through xs_attn_fwd by name): a
@@ -17,8 +17,8 @@ launch, one workgroup each.
   full tiles and gives the same bytes, as does that schedule asked for with
   XS_ONE_LAUNCH.
 
-Bar: max-abs 1e-2 and relative L2 1e-2 (bf16) on every element; the LSE within
-the 5e-3 bar derived for the log-sum-exp output.
+Bar: max-abs 1e-2 / 5e-2 and relative L2 1e-2 / 8e-2 (bf16 / fp8) on every
+element; the LSE within the 5e-3 bar derived for the log-sum-exp output.
 """
 import numpy as np
 import pytest
@@ -30,7 +30,7 @@ from oracle import oracle
 
 pytestmark = pytest.mark.gpu
 
-TOL = (1e-2, 1e-2)  # max-abs, rel-L2 (bf16 inputs)
+TOL = {"bf16": (1e-2, 1e-2), "fp8": (5e-2, 8e-2)}  # max-abs, rel-L2
 LSE_BAR = 5e-3
 
 
@@ -42,35 +42,41 @@ def _f64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def _gate(got, ref, what):
+def _gate(got, ref, what, tol=TOL["bf16"]):
     err = np.abs(got - ref)
     rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
     print(f"  {what}: max_abs={err.max():.3e} rel_l2={rel:.3e} ({got.size} elements)", flush=True)
     assert np.isfinite(got).all(), f"{what}: non-finite output (unwritten?)"
-    assert err.max() <= TOL[0] and rel <= TOL[1], f"{what}: max_abs={err.max():.3e} rel={rel:.3e}"
+    assert err.max() <= tol[0] and rel <= tol[1], f"{what}: max_abs={err.max():.3e} rel={rel:.3e}"
 
 
 def _cus(dev):
     return torch.cuda.get_device_properties(dev).multi_processor_count
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("B,S,H,D,P", [(2, 7000, 5, 128, 8), (1, 4000, 20, 64, 4)])
-def test_half_tile_round_every_element(gpu, B, S, H, D, P):
-    w = workloads.custom(B, S, H, D, P, index=8300 + D)
-    s = xs.xs_attn_schedule(B, S, H, D, with_workspace=False)
+def test_half_tile_round_every_element(gpu, dtype, B, S, H, D, P):
+    w = workloads.custom(B, S, H, D, P, dtype=dtype, index=8300 + D + (dtype == "fp8"))
+    s = xs.xs_attn_schedule(B, S, H, D, with_workspace=False, fp8=dtype == "fp8")
     tiles = B * H * -(-S // 256)
     cus = _cus(gpu)
-    _say(f"half tiles B={B} S={S} H={H} D={D} P={P}: {tiles} tiles on {cus} CUs, schedule {s}")
+    _say(f"half tiles {dtype} B={B} S={S} H={H} D={D} P={P}: {tiles} tiles on {cus} CUs, "
+         f"schedule {s}")
     assert s["half_tiles"] > 0 and s["whole_rounds"] >= 1, "the shape must end in half tiles"
     inp = workloads.make_inputs(w)
     q, k, v = (inp[n].to(gpu) for n in "qkv")
     out = torch.full((P, B, S // P, H, D), float("nan"), dtype=torch.bfloat16, device=gpu)
-    rc = xs.xs_attn_fwd(q, k, v, out, B, S, H, D, P, inp["scale"],
-                        torch.cuda.current_stream(gpu).cuda_stream)
+    stream = torch.cuda.current_stream(gpu).cuda_stream
+    if dtype == "fp8":
+        dq, dk, dv = inp["descales"]
+        rc = xs.xs_attn_fwd_fp8(q, k, v, dq, dk, dv, out, B, S, H, D, P, inp["scale"], stream)
+    else:
+        rc = xs.xs_attn_fwd(q, k, v, out, B, S, H, D, P, inp["scale"], stream)
     assert rc == 0, xs.xs_attn_strerror(rc)
     torch.cuda.synchronize()
-    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, inp["scale"])
-    _gate(_f64(out), ref, f"xs_attn_fwd B={B} S={S} H={H} D={D}")
+    ref = oracle.attention_packed(inp["q"], inp["k"], inp["v"], P, inp["scale"], inp["descales"])
+    _gate(_f64(out), ref, f"{dtype} B={B} S={S} H={H} D={D}", TOL[dtype])
 
 
 def test_half_tiles_with_lse_and_chunked_inputs(gpu):
@@ -98,8 +104,9 @@ def test_half_tiles_with_lse_and_chunked_inputs(gpu):
     assert torch.equal(lse, lse_c), "chunked inputs: lse differs"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("S,D", [(1000, 64), (1000, 128), (4096, 128)])
-def test_half_and_whole_tiles_bit_identical(gpu, S, D):
+def test_half_and_whole_tiles_bit_identical(gpu, S, D, dtype):
     # H_full heads make exactly one round of whole tiles on this device (no
     # half tiles); the first few of the same heads alone leave the chip mostly
     # idle and run as half tiles.  Heads are independent, so the rows of those
@@ -110,17 +117,30 @@ def test_half_and_whole_tiles_bit_identical(gpu, S, D):
         pytest.skip(f"{cus} CUs is not a multiple of {mt} tiles per head")
     H_full, P, B = cus // mt, 8, 1
     H_few = max(1, H_full // 8)
-    w = workloads.custom(B, S, H_full, D, P, index=8400 + D + S)
+    w = workloads.custom(B, S, H_full, D, P, dtype=dtype, index=8400 + D + S + (dtype == "fp8"))
     sf = xs.xs_attn_schedule(B, S, H_full, D, with_workspace=False)
     sh = xs.xs_attn_schedule(B, S, H_few, D, with_workspace=False)
-    _say(f"bit identity S={S} D={D}: {H_full} heads {sf} against {H_few} heads {sh}")
+    _say(f"bit identity {dtype} S={S} D={D}: {H_full} heads {sf} against {H_few} heads {sh}")
     assert sf["half_tiles"] == 0 and sf["whole_rounds"] == 1 and sf["groups"] == cus
     assert sh["half_tiles"] > 0 and sh["groups"] == 0
     inp = workloads.make_inputs(w)
     q, k, v = (inp[n].to(gpu) for n in "qkv")
-    full, lse_full = xs.fwd(q, k, v, P, inp["scale"], workspace=None, lse=True)
     few_in = [t[:, :, :H_few].contiguous() for t in (q, k, v)]
-    few, lse_few = xs.fwd(*few_in, P, inp["scale"], workspace=None, lse=True)
+    if dtype == "fp8":
+        # the call without the log-sum-exp (the fp8 share's) and the one with it
+        # run different kernel instantiations; check both
+        full = xs.fwd_fp8(q, k, v, inp["descales"], P, inp["scale"], workspace=None)
+        few = xs.fwd_fp8(*few_in, inp["descales"], P, inp["scale"], workspace=None)
+        torch.cuda.synchronize()
+        assert torch.equal(xs.unpack(full, S)[:, :, :H_few].contiguous().view(torch.int16),
+                           xs.unpack(few, S).contiguous().view(torch.int16))
+        full, lse_full = xs.fwd_fp8(q, k, v, inp["descales"], P, inp["scale"], workspace=None,
+                                    lse=True)
+        few, lse_few = xs.fwd_fp8(*few_in, inp["descales"], P, inp["scale"], workspace=None,
+                                  lse=True)
+    else:
+        full, lse_full = xs.fwd(q, k, v, P, inp["scale"], workspace=None, lse=True)
+        few, lse_few = xs.fwd(*few_in, P, inp["scale"], workspace=None, lse=True)
     torch.cuda.synchronize()
     a = xs.unpack(full, S)[:, :, :H_few]
     b = xs.unpack(few, S)
