@@ -175,7 +175,7 @@ def xs_attn_split_count(B, S, H_local, D) -> int:
 def xs_attn_schedule(B, S, H_local, D, with_workspace=True, fp8=False) -> dict:
     """The schedule the library runs for this shape on the current device:
     {"groups", "whole_rounds", "pieces", "half_tiles"} (pieces = most pieces a tile is
-    cut into; half_tiles = 128-row tiles of a second launch, bf16 only)."""
+    cut into; half_tiles = 128-row tiles of a second launch; fp8 calls are scheduled alike)."""
     import ctypes
 
     g, r, p, h = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()

@@ -857,10 +857,11 @@ static hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
                          dim3(C::THREADS), kargs, 0, stream);
 }
 
-// Full-height tiles (8 waves), or half-height ones (4 waves, one per SIMD)
-// for the tiles left over after the whole rounds of a call without a
-// workspace: those run as twice as many half tiles instead of leaving part of
-// the chip idle for a last, partly filled round.  Half tiles are never cut.
+// Full-height tiles (8 waves), or half-height ones (4 waves, one per SIMD at
+// D = 128) for the tiles left over after the whole rounds of a call whose
+// schedule cuts no tile: those run as twice as many half tiles instead of
+// leaving part of the chip idle for a last, partly filled round.  Half tiles
+// are never cut.
 template <int D>
 static hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   using C = Bf16Cfg<D, XS_QT, XS_NW, XS_BN>;

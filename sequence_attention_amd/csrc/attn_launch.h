@@ -37,7 +37,7 @@ struct AttnArgs {
   long long jump_rows;
   float* lse;     // NULL or [B][H][S] fp32 log-sum-exp (natural log)
   // Tile height of this launch: 0 = kBlockM rows (8 waves), 1 = kBlockM / 2
-  // rows (4 waves, bf16 only, whole tiles only).  Tiles are numbered in the
+  // rows (4 waves, whole tiles only).  Tiles are numbered in the
   // launch's own height, tile = (b*H + h) * ceil(S / height) + m-tile, and the
   // launch's schedule starts at tile `tile0` (0 unless an earlier launch of the
   // same call took the tiles before it).
