@@ -4,6 +4,7 @@ import ctypes
 import math
 import subprocess
 
+import numpy as np
 import pytest
 
 import sequence_attention_amd as xs
@@ -349,3 +350,28 @@ def test_half_tiles_fill_the_last_round():
     # one round, so the plan keeps full tiles (200 tiles, one round)
     s = xs.xs_attn_schedule(1, 200 * 256, 1, 128, with_workspace=False)
     assert s["half_tiles"] == 0 and s["groups"] == 200
+
+
+def test_half_tiles_cover_exactly_the_tiles_after_the_whole_rounds():
+    # without a device the plan assumes 256 compute units; rows of the tiles
+    # [whole_rounds * 256, tiles) must be exactly the rows of the half tiles, a
+    # tile of more than 128 rows giving two and one of at most 128 rows one
+    rng = np.random.default_rng(7)
+    seen = 0
+    for _ in range(400):
+        B, H = int(rng.integers(1, 5)), int(rng.integers(1, 41))
+        S = int(rng.integers(1, 20000))
+        D = int(rng.choice([64, 128]))
+        s = xs.xs_attn_schedule(B, S, H, D, with_workspace=False)
+        mt = -(-S // 256)
+        tiles = B * H * mt
+        if s["half_tiles"] == 0:
+            continue
+        seen += 1
+        t0 = s["whole_rounds"] * 256
+        assert s["groups"] == (256 if s["whole_rounds"] else 0)
+        assert 0 < tiles - t0 <= 128 and t0 <= tiles
+        rows = lambda m: min(256, S - 256 * m)  # noqa: E731
+        expect = sum(2 if rows(t % mt) > 128 else 1 for t in range(t0, tiles))
+        assert s["half_tiles"] == expect <= 256, (B, S, H, D, s)
+    assert seen > 50
